@@ -1,0 +1,273 @@
+// Matrix products of the layer template on the gfx950 matrix cores.
+//
+// One kernel template covers the three products of a Linear layer:
+//   NT  C = A[M,K] . B[N,K]^T   forward          (A, B contiguous along K)
+//   NN  C = A[M,K] . B[K,N]     input gradient   (B contiguous along N)
+//   TN  C = A[K,M]^T . B[K,N]   weight gradient  (A, B contiguous along M / N)
+// in fp32 (v_mfma_f32_32x32x2_f32) or bf16 with fp32 accumulation
+// (v_mfma_f32_32x32x16_bf16), with an optional residual R added in the
+// epilogue (C = R + A.B, R may alias C).
+//
+// Tiling: 128x128 output tile per 256-thread workgroup (4 wave64, 2x2, each
+// 64x64 = 2x2 MFMA 32x32 tiles); the K loop moves 64 bytes per row per step
+// (32 bf16 / 16 fp32) through two LDS stages. Global loads are 16-byte vectors
+// along each operand's contiguous dimension; operands contiguous along M/N are
+// transposed into the K-contiguous LDS layout as pairs of k rows. Inside a
+// k-step, lane group g = lane/32 reads 32 contiguous bytes of its row; matrix
+// core instruction s consumes slot s of those, so A and B agree on which k
+// each slot holds. Workgroups are remapped so that consecutive tile ids land
+// on the same XCD (each of the 8 XCDs has its own L2) and walk the output in
+// groups of 8 tile rows.
+#include "dev_common.h"
+#include "kernels.h"
+
+namespace mt {
+namespace {
+
+constexpr int BM = 128, BN = 128;
+constexpr int ROW_BYTES = 64;                 // k-extent of a stage per row
+constexpr int PITCH = ROW_BYTES + 16;         // LDS row pitch (bytes)
+constexpr int STAGE_BYTES = (BM + BN) * PITCH;
+
+template <typename T>
+struct Tile {
+  static constexpr int VE = 16 / sizeof(T);   // elements per 16-byte vector
+  static constexpr int BK = ROW_BYTES / sizeof(T);
+};
+
+// Load one operand tile (rows = the M or N index, ROWS = 128) for k-range
+// [k0, k0 + BK) into registers.
+//  KCONTIG: element (r, k) at base[(r0 + r) * ld + k]; each thread loads two
+//           16-byte chunks c = tid + 256 j: row c/4, column chunk c%4.
+//  otherwise: element (r, k) at base[k * ld + r0 + r]; each thread loads rows
+//           k0 + 2p and k0 + 2p + 1 at 16 bytes of consecutive r.
+template <typename T, bool KCONTIG>
+struct Loader {
+  static constexpr int VE = Tile<T>::VE;
+  static constexpr int BK = Tile<T>::BK;
+  Vec16 v[2];
+
+  __device__ __forceinline__ void load(const T* __restrict__ base, int64_t ld, int r0, int rows,
+                                       int k0, int K, bool vec, int tid) {
+    if (KCONTIG) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = tid + 256 * j;
+        const int r = c >> 2, kk = k0 + (c & 3) * VE;
+        const int gr = r0 + r;
+        const T* p = base + (int64_t)gr * ld + kk;
+        if (vec && gr < rows && kk + VE <= K) {
+          v[j] = *reinterpret_cast<const Vec16*>(p);
+        } else {
+          T tmp[VE];
+#pragma unroll
+          for (int e = 0; e < VE; ++e) tmp[e] = (gr < rows && kk + e < K) ? p[e] : T(0);
+          __builtin_memcpy(&v[j], tmp, 16);
+        }
+      }
+    } else {
+      constexpr int CHUNKS = 128 / VE;       // 16-byte chunks along r
+      const int p2 = tid / CHUNKS, rc = (tid % CHUNKS) * VE;
+      const int gr = r0 + rc;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int kk = k0 + 2 * p2 + j;
+        const T* p = base + (int64_t)kk * ld + gr;
+        if (vec && kk < K && gr + VE <= rows) {
+          v[j] = *reinterpret_cast<const Vec16*>(p);
+        } else {
+          T tmp[VE];
+#pragma unroll
+          for (int e = 0; e < VE; ++e) tmp[e] = (kk < K && gr + e < rows) ? p[e] : T(0);
+          __builtin_memcpy(&v[j], tmp, 16);
+        }
+      }
+    }
+  }
+
+  // Write the registers into the K-contiguous LDS tile (row pitch PITCH bytes).
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+    if (KCONTIG) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = tid + 256 * j;
+        *reinterpret_cast<Vec16*>(lds + (c >> 2) * PITCH + (c & 3) * 16) = v[j];
+      }
+    } else {
+      constexpr int CHUNKS = 128 / VE;
+      const int p2 = tid / CHUNKS, rc = (tid % CHUNKS) * VE;
+      const T* a = reinterpret_cast<const T*>(&v[0]);
+      const T* b = reinterpret_cast<const T*>(&v[1]);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        T pair[2] = {a[e], b[e]};
+        char* dst = lds + (rc + e) * PITCH + (2 * p2) * (int)sizeof(T);
+        if (sizeof(T) == 2) {
+          uint32_t u;
+          __builtin_memcpy(&u, pair, 4);
+          *reinterpret_cast<uint32_t*>(dst) = u;
+        } else {
+          uint2 u;
+          __builtin_memcpy(&u, pair, 8);
+          *reinterpret_cast<uint2*>(dst) = u;
+        }
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ int remap_tile(int bid, int nwg) {
+  // Hardware places workgroup bid on XCD bid % 8; give each XCD a contiguous
+  // range of tile ids so neighbouring tiles share an L2.
+  if ((nwg & 7) != 0) return bid;
+  return (bid & 7) * (nwg >> 3) + (bid >> 3);
+}
+
+template <typename T, int LAYOUT>
+__global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int64_t lda,
+                                                   const T* __restrict__ B, int64_t ldb,
+                                                   float* C, int64_t ldc, const float* R,
+                                                   int64_t ldr, int M, int N, int K,
+                                                   int tiles_m, int tiles_n, int vec_a,
+                                                   int vec_b) {
+  constexpr bool A_KC = (LAYOUT != MT_GEMM_TN);
+  constexpr bool B_KC = (LAYOUT == MT_GEMM_NT);
+  constexpr int BK = Tile<T>::BK;
+  typedef Mfma32<T> MF;
+  constexpr int KPL = BK / 2;                 // k values each lane reads per row per stage
+  constexpr int NMMA = KPL / MF::KL;          // instructions per (i, j) per stage
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 5, l32 = lane & 31;
+
+  // tile coordinates: XCD-local ids, grouped by 8 tile rows
+  const int nwg = tiles_m * tiles_n;
+  const int pid = remap_tile(blockIdx.x, nwg);
+  const int group = 8 * tiles_n;
+  const int first_m = (pid / group) * 8;
+  const int gsize = min(tiles_m - first_m, 8);
+  const int tm = first_m + (pid % group) % gsize;
+  const int tn = (pid % group) / gsize;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  Loader<T, A_KC> la;
+  Loader<T, B_KC> lb;
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
+
+  const int nk = (K + BK - 1) / BK;
+  if (nk > 0) {
+    la.load(A, lda, m0, M, 0, K, vec_a, tid);
+    lb.load(B, ldb, n0, N, 0, K, vec_b, tid);
+    la.store(smem, tid);
+    lb.store(smem + BM * PITCH, tid);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    char* cur = smem + (kt & 1) * STAGE_BYTES;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      la.load(A, lda, m0, M, (kt + 1) * BK, K, vec_a, tid);
+      lb.load(B, ldb, n0, N, (kt + 1) * BK, K, vec_b, tid);
+    }
+    typename MF::frag af[2][NMMA], bfg[2][NMMA];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const char* pa = cur + (wm * 64 + i * 32 + l32) * PITCH + g * 32;
+      const char* pb = cur + BM * PITCH + (wn * 64 + i * 32 + l32) * PITCH + g * 32;
+      const Vec16 a0 = *reinterpret_cast<const Vec16*>(pa), a1 = *reinterpret_cast<const Vec16*>(pa + 16);
+      const Vec16 b0 = *reinterpret_cast<const Vec16*>(pb), b1 = *reinterpret_cast<const Vec16*>(pb + 16);
+      Vec16 av[2] = {a0, a1}, bv[2] = {b0, b1};
+      __builtin_memcpy(&af[i][0], av, 32);
+      __builtin_memcpy(&bfg[i][0], bv, 32);
+    }
+#pragma unroll
+    for (int s = 0; s < NMMA; ++s)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = MF::mma(af[i][s], bfg[j][s], acc[i][j]);
+    if (more) {
+      char* nxt = smem + ((kt + 1) & 1) * STAGE_BYTES;
+      la.store(nxt, tid);
+      lb.store(nxt + BM * PITCH, tid);
+    }
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows (r/4)*8 + g*4 + r%4 of each 32x32 tile, column l32
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn * 64 + j * 32 + l32;
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+        if (row < M) {
+          float val = acc[i][j][r];
+          if (R) val += R[(int64_t)row * ldr + col];
+          C[(int64_t)row * ldc + col] = val;
+        }
+      }
+    }
+}
+
+// C = R (or 0) for K = 0
+__global__ void fill_kernel(float* C, int64_t ldc, const float* R, int64_t ldr, int M, int N) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)M * N) return;
+  const int r = (int)(i / N), c = (int)(i % N);
+  C[(int64_t)r * ldc + c] = R ? R[(int64_t)r * ldr + c] : 0.f;
+}
+
+template <typename T, int LAYOUT>
+hipError_t launch(const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc,
+                  const float* R, int64_t ldr, int M, int N, int K, hipStream_t s) {
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  auto aligned = [](const void* p, int64_t ld) {
+    return ((uintptr_t)p % 16 == 0) && ((ld * (int64_t)sizeof(T)) % 16 == 0);
+  };
+  hipLaunchKernelGGL((gemm_kernel<T, LAYOUT>), dim3(tm * tn), dim3(256), 0, s,
+                     (const T*)A, lda, (const T*)B, ldb, C, ldc, R, ldr, M, N, K, tm, tn,
+                     (int)aligned(A, lda), (int)aligned(B, ldb));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t gemm(int dtype, int layout, const void* A, int64_t lda, const void* B, int64_t ldb,
+                float* C, int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N,
+                int64_t K, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (K == 0) {
+    const int64_t n = M * N;
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, C, ldc, R,
+                       ldr, (int)M, (int)N);
+    return hipGetLastError();
+  }
+  const int m = (int)M, n = (int)N, k = (int)K;
+  if (dtype == 1) {
+    switch (layout) {
+      case MT_GEMM_NT: return launch<bf16, MT_GEMM_NT>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
+      case MT_GEMM_NN: return launch<bf16, MT_GEMM_NN>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
+      default: return launch<bf16, MT_GEMM_TN>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
+    }
+  }
+  switch (layout) {
+    case MT_GEMM_NT: return launch<float, MT_GEMM_NT>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
+    case MT_GEMM_NN: return launch<float, MT_GEMM_NN>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
+    default: return launch<float, MT_GEMM_TN>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
+  }
+}
+
+}  // namespace mt

@@ -1,0 +1,39 @@
+// Host-side launchers of the gfx950 kernels (defined in the .hip files).
+// Plain types only, so host translation units compiled with g++ can call them.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "mt_ops.h"
+
+namespace mt {
+
+// dtype: 0 = fp32, 1 = bf16 (same values as MT_FP32 / MT_BF16)
+hipError_t gemm(int dtype, int layout, const void* A, int64_t lda, const void* B, int64_t ldb,
+                float* C, int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N,
+                int64_t K, hipStream_t s);
+
+bool attn_supported(int dtype, int hd);
+int64_t attn_ws_d_bytes(int B, int T, int H);
+hipError_t attn_fwd(int dtype, const void* qkv, float* o, void* o_cast, float* lse, int B, int T,
+                    int H, int Hkv, int hd, hipStream_t s);
+hipError_t attn_bwd(int dtype, const void* qkv, const float* o, const float* dout, const float* lse,
+                    float* dqkv, void* ws, int B, int T, int H, int Hkv, int hd, hipStream_t s);
+
+int rmsnorm_bwd_partials(int64_t rows);
+hipError_t rmsnorm_fwd(int out_dtype, const float* x, const float* w, void* y, float* rstd,
+                       int64_t rows, int d, float eps, hipStream_t s);
+hipError_t rmsnorm_bwd(const float* x, const float* w, const float* rstd, const float* dy,
+                       float* dx, int accumulate, float* dw, float* ws, int64_t rows, int d,
+                       hipStream_t s);
+hipError_t rope(int out_dtype, int backward, const float* in, void* out, const float* cos,
+                const float* sin, int B, int T, int H, int Hkv, int hd, hipStream_t s);
+hipError_t swiglu_fwd(int out_dtype, const float* gu, void* act, int64_t M, int F, hipStream_t s);
+hipError_t swiglu_bwd(int out_dtype, const float* gu, const float* dact, void* dgu, int64_t M,
+                      int F, hipStream_t s);
+hipError_t xent(int out_dtype, const float* logits, const int32_t* targets, float* loss,
+                void* dlogits, int64_t rows, int V, float scale, hipStream_t s);
+hipError_t cast(int out_dtype, const float* x, void* y, int64_t n, hipStream_t s);
+
+}  // namespace mt

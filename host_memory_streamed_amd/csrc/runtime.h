@@ -1,0 +1,231 @@
+// Internal structures of the streamed training-step library: unit layouts,
+// the host store, device workspace, the thread pool and the context.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <chrono>
+#include <condition_variable>
+#include <cstdint>
+#include <deque>
+#include <functional>
+#include <mutex>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "mt.h"
+
+namespace mt {
+
+// ----------------------------------------------------------- thread pool ---
+
+class Pool {
+ public:
+  explicit Pool(int n);
+  ~Pool();
+  int size() const { return (int)workers_.size(); }
+  // Run fn(i) for i in [0, n) on the workers; when all have finished, call
+  // done() (on the worker that finished last). Returns immediately.
+  void submit(int64_t n, std::function<void(int64_t)> fn, std::function<void()> done = nullptr);
+  // Run fn(i) for i in [0, n) and wait for all of them.
+  void run(int64_t n, const std::function<void(int64_t)>& fn);
+
+ private:
+  struct Job {
+    std::function<void(int64_t)> fn;
+    std::function<void()> done;
+    int64_t n;
+    std::atomic<int64_t> next{0};
+    std::atomic<int64_t> finished{0};
+  };
+  void loop();
+  std::vector<std::thread> workers_;
+  std::mutex mu_;
+  std::condition_variable cv_;
+  std::deque<std::shared_ptr<Job>> jobs_;
+  bool stop_ = false;
+};
+
+// ------------------------------------------------------------- layouts ---
+
+constexpr int64_t kAlign = 64;   // elements
+inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// A unit (embedding, one layer, or the head) is one contiguous slab of fp32
+// master values. Norm gains come first ([0, mat_base)), matrices after, each
+// matrix group starting on a 64-element boundary. The device image of a unit
+// keeps the gains in fp32 and stores the matrices in the compute dtype.
+struct UnitLayout {
+  int64_t n = 0;          // slab elements, padding included
+  int64_t mat_base = 0;   // first matrix element
+  // layer: 0 attn_norm, 1 mlp_norm, 2 wqkv, 3 wo, 4 wgu, 5 wdown
+  // head : 0 final_norm, 1 lm_head
+  std::vector<int64_t> off;
+  size_t image_bytes(int dtype) const {
+    return (size_t)mat_base * 4 + (size_t)(n - mat_base) * (dtype ? 2 : 4);
+  }
+  size_t image_offset(int64_t elem, int dtype) const {
+    return elem < mat_base ? (size_t)elem * 4
+                           : (size_t)mat_base * 4 + (size_t)(elem - mat_base) * (dtype ? 2 : 4);
+  }
+};
+
+struct Dims {
+  int L, d, H, Hkv, hd, F, V;
+  int qd, kvd, qkvd;
+};
+
+struct TensorRef {
+  int unit;        // -1 embedding, 0..L-1 layers, L head
+  int64_t off, numel;
+  int64_t rows, cols;
+  std::string name;
+};
+
+struct Unit {
+  UnitLayout lay;
+  float* p = nullptr;       // fp32 master (pinned when it is the fp32 device image)
+  float* m = nullptr;
+  float* v = nullptr;
+  float* g = nullptr;       // gradients (MT_KEEP_GRADS, and always for the embedding)
+  void* shadow = nullptr;   // bf16-mode device image (pinned)
+  bool p_pinned = false;
+  const void* image() const { return shadow ? shadow : (const void*)p; }
+};
+
+// --------------------------------------------------------- kernel timing ---
+
+enum KClass {
+  K_GEMM_NT, K_GEMM_NN, K_GEMM_TN, K_ATTN_FWD, K_ATTN_BWD, K_RMS_FWD, K_RMS_BWD,
+  K_ROPE, K_SWIGLU, K_XENT, K_CAST, K_OTHER, K_COUNT
+};
+
+struct KTiming {
+  bool on = false;
+  std::vector<hipEvent_t> ev;   // pairs
+  size_t used = 0;
+  struct Rec { int cls; double flops, bytes; size_t e; };
+  std::vector<Rec> recs;
+};
+
+// ----------------------------------------------------- device workspace ---
+
+struct Workspace {
+  // per-layer activations (M = max_batch * max_seq rows)
+  void* h = nullptr;        // RMSNorm out (S)
+  float* rstd1 = nullptr;
+  float* rstd2 = nullptr;
+  float* qkv_f = nullptr;   // projection out
+  void* qkv_s = nullptr;    // rotated, cast
+  float* o_f = nullptr;
+  void* o_s = nullptr;      // bf16 mode: cast of o (fp32 mode: o_f)
+  float* lse = nullptr;
+  float* x1 = nullptr;
+  void* h2 = nullptr;
+  float* gu_f = nullptr;
+  void* act = nullptr;
+  // backward
+  float* g_f = nullptr;     // running residual gradient
+  void* g_s = nullptr;      // its cast (fp32 mode: g_f)
+  float* dact_f = nullptr;
+  void* dgu_s = nullptr;
+  float* dh_f = nullptr;
+  float* do_f = nullptr;
+  float* dqkv_f = nullptr;
+  void* dqkv_s = nullptr;
+  void* attn_ws = nullptr;
+  float* rms_ws = nullptr;
+  // head
+  void* hf = nullptr;
+  float* rstdf = nullptr;
+  float* logits = nullptr;  // [head_chunk, V]
+  void* dz_s = nullptr;     // bf16 mode cast of dlogits (fp32 mode: logits)
+  float* tok_loss = nullptr;
+  int32_t* targets = nullptr;
+  float* rope_cos = nullptr;
+  float* rope_sin = nullptr;
+  int64_t head_chunk = 0;
+};
+
+// ------------------------------------------------------------- context ---
+
+struct Ctx {
+  mt_model_cfg cfg;
+  Dims D;
+  int dtype;                 // 0 fp32, 1 bf16
+  int nbuf;
+  bool resident;
+  int64_t M_max;
+  std::string err;
+
+  std::vector<Unit> units;   // [0, L) layers, L head, L+1 embedding
+  Unit& layer(int l) { return units[l]; }
+  Unit& head() { return units[D.L]; }
+  Unit& emb() { return units[D.L + 1]; }
+  std::vector<TensorRef> tensors;
+
+  // grad staging ring (MT_KEEP_GRADS off)
+  int ring = 0;
+  std::vector<float*> ring_slot;
+  // pinned staging
+  float* x0_host = nullptr;      // [M_max, d]
+  float* dx0_host = nullptr;     // [M_max, d]
+  int32_t* tgt_host = nullptr;   // [M_max]
+  float* loss_host = nullptr;    // [M_max]
+  std::vector<float> token_loss; // last step
+  std::vector<int32_t> prev_rows;  // embedding rows touched by the previous step
+
+  // device
+  std::vector<void*> buf;        // layer buffers
+  float* gbuf[2] = {nullptr, nullptr};
+  float* ckpt = nullptr;         // (L+1) * M_max * d
+  Workspace ws;
+  std::vector<void*> dev_allocs;
+  int64_t dev_bytes = 0;
+
+  hipStream_t s_in = nullptr, s_comp = nullptr, s_out = nullptr;
+  bool own_streams[3] = {false, false, false};
+
+  Pool* pool = nullptr;
+  int64_t step = 0;
+  mt_step_stats stats{};
+  KTiming kt;
+  std::vector<mt_kernel_stat> kstats;
+  std::vector<mt_sched_entry> sched;
+};
+
+// ----------------------------------------------------------- helpers ---
+
+int set_error(Ctx* c, int code, const std::string& msg);
+void* host_alloc_plain(size_t bytes);
+void host_free_plain(void* p, size_t bytes);
+
+struct AdamConst {
+  float decay, b1, omb1, b2, omb2, step_size, inv_sqrt_bc2, eps;
+};
+AdamConst adam_const(const mt_model_cfg& c, int64_t t);
+// p, m, v, g over [0, n); optional outputs: bf16 image and/or fp32 copy of p.
+void adamw_range(float* p, float* m, float* v, const float* g, int64_t n, const AdamConst& k,
+                 uint16_t* bf16_out, float* f32_out);
+void to_bf16_range(const float* x, uint16_t* y, int64_t n);
+
+// Layer template (layer.cpp)
+struct LayerPtrs {
+  const float* attn_norm;
+  const float* mlp_norm;
+  const void* wqkv;
+  const void* wo;
+  const void* wgu;
+  const void* wdown;
+};
+LayerPtrs bind_layer(const Ctx& c, const void* image);
+int layer_forward(Ctx& c, const LayerPtrs& W, int l, int B, int T, bool recompute);
+int layer_backward(Ctx& c, const LayerPtrs& W, int l, int B, int T, float* grad_unit);
+int head_forward_backward(Ctx& c, const void* image, int B, int T, float* grad_unit);
+
+// kernel-timing wrapper: run fn on the compute stream, bracketed by events
+int timed(Ctx& c, int cls, double flops, double bytes, const std::function<hipError_t()>& fn);
+
+}  // namespace mt

@@ -1,0 +1,577 @@
+// One training step: the double-buffered streaming schedule.
+//
+// "MegaTrain: Full Precision Training of 100B+ Parameter LLMs on a Single
+// GPU", abstract: per layer, parameters stream in and gradients stream out; a
+// pipelined double-buffered engine overlaps parameter prefetch, computation and
+// gradient offload across several streams. "MegaTrain fits 120B LLM training on
+// one GPU using CPU RAM", section "Pipelined double buffering": while layer n
+// computes, layer n+1 prefetches. "Technical Brief: MegaTrain's Single-GPU
+// 120B-Parameter Training Breakthrough", section "Quantifying Host Memory
+// Requirements...": gradients are pushed back to the host right after a
+// layer's compute.
+//
+// Three HIP streams: copy-in (unit images host -> layer buffer), compute (the
+// layer template's kernels), copy-out (gradients and per-token losses device
+// -> host). Compute order: forward of layers 0..L-1, the head (final norm, LM
+// head, loss and its backward), then recompute + backward of layers L-1..0.
+// Layer l always lives in buffer l % 2 (the head in L % 2), so layer L-1 is
+// still resident when the backward starts and is not fetched again. A load
+// into a buffer waits for the compute that last used it; a gradient item
+// waits for the copy-out of the item two before it (two gradient buffers).
+// A host dispatcher loop submits copies only once the compute they depend on
+// has completed, enqueues compute with device-side waits on the copies, and
+// hands each unit's AdamW to the worker pool as its gradients land; the step
+// returns when every update has landed.
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstring>
+
+#include "kernels.h"
+#include "runtime.h"
+
+namespace mt {
+
+namespace {
+
+enum { PH_FWD = MT_PH_FWD, PH_HEAD = MT_PH_HEAD, PH_BWD = MT_PH_BWD };
+
+struct Item {
+  int phase;
+  int unit;       // layer index, or L for the head
+  int buf;
+  bool load;
+  int prev_user;  // index of the last earlier item using the same buffer, or -1
+  int grad_k;     // -1, or the index among gradient-producing items
+};
+
+std::vector<Item> build_items(const Ctx& c) {
+  const int L = c.D.L;
+  std::vector<Item> it;
+  auto bufof = [&](int unit) { return c.resident ? unit : unit % 2; };
+  for (int l = 0; l < L; ++l) it.push_back({PH_FWD, l, bufof(l), true, -1, -1});
+  it.push_back({PH_HEAD, L, bufof(L), true, -1, 0});
+  for (int l = L - 1; l >= 0; --l)
+    it.push_back({PH_BWD, l, bufof(l), !c.resident && l != L - 1, -1, L - l});
+  for (size_t i = 0; i < it.size(); ++i)
+    for (int j = (int)i - 1; j >= 0; --j)
+      if (it[j].buf == it[i].buf) { it[i].prev_user = j; break; }
+  return it;
+}
+
+double ms_since(std::chrono::steady_clock::time_point t0) {
+  return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+}
+
+}  // namespace
+
+struct StepEvents {
+  std::vector<hipEvent_t> loaded, freed, drained;
+  hipEvent_t x0 = nullptr, loss = nullptr, dx0 = nullptr, start = nullptr;
+  std::vector<hipEvent_t> trace;   // timing events: per item 6 (load, compute, copy-out)
+};
+
+int create_step_events(Ctx& c, StepEvents*& out);
+void destroy_step_events(StepEvents* e);
+
+int create_step_events(Ctx& c, StepEvents*& out) {
+  auto* e = new StepEvents();
+  const int n = 2 * c.D.L + 1;
+  auto mk = [&](hipEvent_t& ev, unsigned flags) {
+    return hipEventCreateWithFlags(&ev, flags) == hipSuccess;
+  };
+  bool ok = true;
+  const unsigned sync = hipEventDisableTiming;
+  const unsigned host = hipEventDisableTiming;
+  e->loaded.resize(n);
+  e->freed.resize(n);
+  e->drained.resize(c.D.L + 1);
+  for (auto& ev : e->loaded) ok &= mk(ev, sync);
+  for (auto& ev : e->freed) ok &= mk(ev, sync);
+  for (auto& ev : e->drained) ok &= mk(ev, host);
+  ok &= mk(e->x0, sync);
+  ok &= mk(e->loss, host);
+  ok &= mk(e->dx0, host);
+  ok &= mk(e->start, hipEventBlockingSync);
+  if (c.cfg.flags & MT_TRACE) {
+    e->trace.resize((size_t)n * 6 + 4);
+    for (auto& ev : e->trace) ok &= mk(ev, hipEventDefault);
+  }
+  out = e;
+  if (!ok) return set_error(&c, MT_EHIP, "hipEventCreate failed");
+  return MT_OK;
+}
+
+void destroy_step_events(StepEvents* e) {
+  if (!e) return;
+  for (auto* v : {&e->loaded, &e->freed, &e->drained, &e->trace})
+    for (auto ev : *v)
+      if (ev) hipEventDestroy(ev);
+  for (auto ev : {e->x0, e->loss, e->dx0, e->start})
+    if (ev) hipEventDestroy(ev);
+  delete e;
+}
+
+#define HIPCK(call)                                                                        \
+  do {                                                                                     \
+    hipError_t e_ = (call);                                                                \
+    if (e_ != hipSuccess) return set_error(&c, MT_EHIP, std::string(#call ": ") + hipGetErrorString(e_)); \
+  } while (0)
+
+// AdamW over element ranges of one unit as a single pool job of chunks of at
+// most 1M elements; writes p, m, v and the unit's device image (bf16 mode:
+// fp32 gains + bf16 matrices).
+static void submit_adamw(Ctx& c, Unit& u, const float* g, std::vector<std::pair<int64_t, int64_t>> ranges,
+                         const AdamConst& k, std::function<void()> done, std::atomic<int64_t>* adam_ns) {
+  constexpr int64_t CH = 1 << 20;
+  auto chunks = std::make_shared<std::vector<std::pair<int64_t, int64_t>>>();
+  for (auto& r : ranges)
+    for (int64_t a = r.first; a < r.second; a += CH) chunks->push_back({a, std::min(r.second, a + CH)});
+  const int dt = c.dtype;
+  c.pool->submit(
+      (int64_t)chunks->size(),
+      [&u, g, chunks, k, dt, adam_ns](int64_t i) {
+        const auto t0 = std::chrono::steady_clock::now();
+        const int64_t a = (*chunks)[i].first, b = (*chunks)[i].second;
+        const int64_t mb = u.lay.mat_base;
+        if (a < mb) {   // gains region: fp32 in the image
+          const int64_t e = std::min(b, mb);
+          float* f32 = (dt && u.shadow) ? static_cast<float*>(u.shadow) + a : nullptr;
+          adamw_range(u.p + a, u.m + a, u.v + a, g + a, e - a, k, nullptr, f32);
+        }
+        if (b > mb) {   // matrices: bf16 in the image (bf16 mode)
+          const int64_t s = std::max(a, mb);
+          uint16_t* bo = (dt && u.shadow)
+                             ? reinterpret_cast<uint16_t*>(static_cast<char*>(u.shadow) + mb * 4) + (s - mb)
+                             : nullptr;
+          adamw_range(u.p + s, u.m + s, u.v + s, g + s, b - s, k, bo, nullptr);
+        }
+        adam_ns->fetch_add((int64_t)(std::chrono::duration<double, std::nano>(
+                                          std::chrono::steady_clock::now() - t0).count()));
+      },
+      std::move(done));
+}
+
+int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t* targets, int B,
+                    int T, float* loss_out) {
+  const Dims& D = c.D;
+  const int L = D.L;
+  const int64_t M = (int64_t)B * T;
+  const int64_t d = D.d;
+  const auto t_begin = std::chrono::steady_clock::now();
+  const bool trace = (c.cfg.flags & MT_TRACE) != 0;
+  const bool keep = (c.cfg.flags & MT_KEEP_GRADS) != 0;
+  c.kt.on = (c.cfg.flags & MT_KERNEL_TIMING) != 0;
+  c.kt.used = 0;
+  c.kt.recs.clear();
+  c.sched.clear();
+
+  HIPCK(hipEventRecord(E.start, c.s_comp));
+  HIPCK(hipEventSynchronize(E.start));
+  const auto t_dev0 = std::chrono::steady_clock::now();
+
+  // ---- inputs: targets and the embedding gather x0 = E[tokens] (host) ----
+  std::memcpy(c.tgt_host, targets, (size_t)M * 4);
+  Unit& emb = c.emb();
+  c.pool->run((M + 255) / 256, [&](int64_t i) {
+    const int64_t a = i * 256, b = std::min(M, a + 256);
+    for (int64_t r = a; r < b; ++r)
+      std::memcpy(c.x0_host + r * d, emb.p + (int64_t)tokens[r] * d, (size_t)d * 4);
+  });
+  HIPCK(hipMemcpyAsync(c.ws.targets, c.tgt_host, (size_t)M * 4, hipMemcpyHostToDevice, c.s_in));
+  HIPCK(hipMemcpyAsync(c.ckpt, c.x0_host, (size_t)M * d * 4, hipMemcpyHostToDevice, c.s_in));
+  HIPCK(hipEventRecord(E.x0, c.s_in));
+  double h2d_bytes = (double)M * 4 + (double)M * d * 4, d2h_bytes = 0;
+
+  // rows of the embedding this step touches, with their token positions in
+  // (b, t) order (counting sort; deterministic scatter below)
+  std::vector<int32_t> cnt(D.V + 1, 0);
+  for (int64_t r = 0; r < M; ++r) cnt[tokens[r] + 1]++;
+  for (int v = 0; v < D.V; ++v) cnt[v + 1] += cnt[v];
+  std::vector<int32_t> pos(M), fill(cnt.begin(), cnt.end() - 1);
+  for (int64_t r = 0; r < M; ++r) pos[fill[tokens[r]]++] = (int32_t)r;
+  std::vector<int32_t> rows;
+  for (int v = 0; v < D.V; ++v)
+    if (cnt[v + 1] > cnt[v]) rows.push_back(v);
+  // the embedding gradient holds zeros outside the rows written last step
+  for (int32_t v : c.prev_rows) std::memset(emb.g + (int64_t)v * d, 0, (size_t)d * 4);
+  c.prev_rows = rows;
+
+  const std::vector<Item> items = build_items(c);
+  const int n_items = (int)items.size();
+  const AdamConst k = adam_const(c.cfg, c.step + 1);
+
+  std::atomic<int64_t> adam_ns{0};
+  std::vector<double> adam_end_ms(L + 2, 0.0), adam_start_ms(L + 2, 0.0);
+  bool abort = false;
+  double loss_sum = 0.0, forward_ms = 0.0, last_land_ms = 0.0;
+
+  auto grad_unit = [&](int kk) -> Unit& { return kk == 0 ? c.head() : c.layer(L - kk); };
+  auto grad_dest = [&](int kk) -> float* { return keep ? grad_unit(kk).g : c.ring_slot[kk % c.ring]; };
+  auto unit_id = [&](const Item& it) { return it.phase == PH_HEAD ? MT_UNIT_HEAD : it.unit; };
+
+  // AdamW tasks in flight and their completion (set from pool threads)
+  std::mutex amu;
+  std::condition_variable acv;
+  int pending = 0;
+  std::vector<char> adam_done(L + 1, 0);
+  auto job_done = [&](int kk) {
+    {
+      std::lock_guard<std::mutex> g(amu);
+      if (kk >= 0) {
+        adam_done[kk] = 1;
+        adam_end_ms[kk] = ms_since(t_begin);
+      }
+      pending--;
+    }
+    acv.notify_all();
+  };
+  auto adam_is_done = [&](int kk) {
+    std::lock_guard<std::mutex> g(amu);
+    return adam_done[kk] != 0;
+  };
+  auto add_pending = [&] {
+    std::lock_guard<std::mutex> g(amu);
+    pending++;
+  };
+
+  // ---- host dispatcher ----
+  // Copies are submitted only once the compute they depend on has completed
+  // (observed by polling its event), so no copy ever waits on the device; the
+  // compute stream waits on copy events on the device. Compute therefore runs
+  // at most two items ahead of the GPU, which is ample: submitting one layer
+  // takes a small fraction of its compute time.
+  int rc = MT_OK;
+  auto trace_ev = [&](int i, int slot) -> hipEvent_t { return E.trace[(size_t)i * 6 + slot]; };
+  struct HostSpan { int phase, unit; double t0, t1; };
+  std::vector<HostSpan> host_spans;
+  auto span = [&](int phase, int unit, std::chrono::steady_clock::time_point a) {
+    if (trace)
+      host_spans.push_back({phase, unit, std::chrono::duration<double, std::milli>(a - t_begin).count(),
+                            ms_since(t_begin)});
+  };
+  std::vector<char> computed(n_items, 0), done_seen(n_items, 0), load_issued(n_items, 0);
+  std::vector<int> loads, grad_item(L + 1, -1);
+  for (int i = 0; i < n_items; ++i) {
+    if (items[i].load) loads.push_back(i);
+    if (items[i].grad_k >= 0) grad_item[items[i].grad_k] = i;
+  }
+  const int head_item = L;
+  auto item_done = [&](int i) -> int {   // 1 done, 0 not yet, <0 error
+    if (!computed[i]) return 0;
+    if (done_seen[i]) return 1;
+    const hipError_t r = hipEventQuery(E.freed[i]);
+    if (r == hipSuccess) { done_seen[i] = 1; return 1; }
+    if (r == hipErrorNotReady) return 0;
+    return set_error(&c, MT_EHIP, std::string("hipEventQuery: ") + hipGetErrorString(r));
+  };
+  auto event_done = [&](hipEvent_t e) -> int {
+    const hipError_t r = hipEventQuery(e);
+    if (r == hipSuccess) return 1;
+    if (r == hipErrorNotReady) return 0;
+    return set_error(&c, MT_EHIP, std::string("hipEventQuery: ") + hipGetErrorString(r));
+  };
+  std::vector<char> grad_issued(L + 1, 0);
+  size_t next_l = 0;
+  int next_c = 0, next_g = 0, next_a = 0;
+  bool loss_issued = false, loss_checked = false, dx0_issued = false, dx0_done = false;
+
+  auto issue_load = [&](int j) -> int {
+    const Item& it = items[j];
+    const Unit& u = it.phase == PH_HEAD ? c.head() : c.layer(it.unit);
+    const size_t bytes = u.lay.image_bytes(c.dtype);
+    if (trace) HIPCK(hipEventRecord(trace_ev(j, 0), c.s_in));
+    const auto hq = std::chrono::steady_clock::now();
+    HIPCK(hipMemcpyAsync(c.buf[it.buf], u.image(), bytes, hipMemcpyHostToDevice, c.s_in));
+    span(MT_PH_LOAD, unit_id(it), hq);
+    if (trace) HIPCK(hipEventRecord(trace_ev(j, 1), c.s_in));
+    HIPCK(hipEventRecord(E.loaded[j], c.s_in));
+    load_issued[j] = 1;
+    h2d_bytes += (double)bytes;
+    return MT_OK;
+  };
+  auto issue_compute = [&](int i) -> int {
+    const Item& it = items[i];
+    if (it.load) HIPCK(hipStreamWaitEvent(c.s_comp, E.loaded[i], 0));
+    if (i == 0) HIPCK(hipStreamWaitEvent(c.s_comp, E.x0, 0));
+    if (it.grad_k >= 2) HIPCK(hipStreamWaitEvent(c.s_comp, E.drained[it.grad_k - 2], 0));
+    if (trace) HIPCK(hipEventRecord(trace_ev(i, 2), c.s_comp));
+    float* gdev = it.grad_k >= 0 ? c.gbuf[it.grad_k % 2] : nullptr;
+    const auto hc = std::chrono::steady_clock::now();
+    int r;
+    if (it.phase == PH_FWD)
+      r = layer_forward(c, bind_layer(c, c.buf[it.buf]), it.unit, B, T, false);
+    else if (it.phase == PH_HEAD)
+      r = head_forward_backward(c, c.buf[it.buf], B, T, gdev);
+    else
+      r = layer_backward(c, bind_layer(c, c.buf[it.buf]), it.unit, B, T, gdev);
+    if (r) return r;
+    span(it.phase, unit_id(it), hc);
+    if (trace) HIPCK(hipEventRecord(trace_ev(i, 3), c.s_comp));
+    HIPCK(hipEventRecord(E.freed[i], c.s_comp));
+    computed[i] = 1;
+    return MT_OK;
+  };
+  auto issue_grad = [&](int kk) -> int {
+    const int i = grad_item[kk];
+    const Unit& u = grad_unit(kk);
+    if (trace) HIPCK(hipEventRecord(trace_ev(i, 4), c.s_out));
+    const auto hg = std::chrono::steady_clock::now();
+    HIPCK(hipMemcpyAsync(grad_dest(kk), c.gbuf[kk % 2], (size_t)u.lay.n * 4, hipMemcpyDeviceToHost, c.s_out));
+    span(MT_PH_GRAD, unit_id(items[i]), hg);
+    if (trace) HIPCK(hipEventRecord(trace_ev(i, 5), c.s_out));
+    HIPCK(hipEventRecord(E.drained[kk], c.s_out));
+    grad_issued[kk] = 1;
+    d2h_bytes += (double)u.lay.n * 4;
+    return MT_OK;
+  };
+  auto issue_loss = [&]() -> int {
+    HIPCK(hipMemcpyAsync(c.loss_host, c.ws.tok_loss, (size_t)M * 4, hipMemcpyDeviceToHost, c.s_out));
+    HIPCK(hipEventRecord(E.loss, c.s_out));
+    d2h_bytes += (double)M * 4;
+    return MT_OK;
+  };
+  auto issue_dx0 = [&]() -> int {
+    HIPCK(hipMemcpyAsync(c.dx0_host, c.ws.g_f, (size_t)M * d * 4, hipMemcpyDeviceToHost, c.s_out));
+    HIPCK(hipEventRecord(E.dx0, c.s_out));
+    d2h_bytes += (double)M * d * 4;
+    return MT_OK;
+  };
+  auto start_emb_untouched = [&] {
+    // embedding rows this step does not touch have a zero gradient: their
+    // update can run now, overlapping the backward
+    int64_t prev = 0;
+    std::vector<std::pair<int64_t, int64_t>> runs;
+    for (int32_t v : rows) {
+      if (v > prev) runs.push_back({prev, v});
+      prev = v + 1;
+    }
+    if (prev < D.V) runs.push_back({prev, D.V});
+    for (auto& rr : runs) rr = {rr.first * d, rr.second * d};
+    add_pending();
+    submit_adamw(c, emb, emb.g, std::move(runs), k, [&] { job_done(-1); }, &adam_ns);
+  };
+
+  for (;;) {
+    bool progress = false;
+    // loads, in order, once the buffer's previous user has finished
+    while (next_l < loads.size()) {
+      const int j = loads[next_l];
+      const int p = items[j].prev_user;
+      if (p >= 0) {
+        const int st = item_done(p);
+        if (st < 0) { rc = st; break; }
+        if (!st) break;
+      }
+      if ((rc = issue_load(j))) break;
+      ++next_l;
+      progress = true;
+    }
+    if (rc) break;
+    // next compute item, once its weights and its gradient buffer are on their way
+    if (next_c < n_items) {
+      const Item& it = items[next_c];
+      const bool ready = (!it.load || load_issued[next_c]) && (it.grad_k < 2 || grad_issued[it.grad_k - 2]);
+      if (ready) {
+        if ((rc = issue_compute(next_c))) break;
+        ++next_c;
+        progress = true;
+      }
+    }
+    // per-token losses once the head has run
+    if (!loss_issued) {
+      const int st = item_done(head_item);
+      if (st < 0) { rc = st; break; }
+      if (st) {
+        if ((rc = issue_loss())) break;
+        loss_issued = progress = true;
+      }
+    }
+    if (loss_issued && !loss_checked) {
+      const int st = event_done(E.loss);
+      if (st < 0) { rc = st; break; }
+      if (st) {
+        for (int64_t r = 0; r < M; ++r) loss_sum += (double)c.loss_host[r];
+        forward_ms = ms_since(t_begin);
+        abort = !std::isfinite(loss_sum);
+        if (!abort) start_emb_untouched();
+        loss_checked = progress = true;
+      }
+    }
+    // gradient copies, in order, once their compute has finished (and, with
+    // the staging ring, once the AdamW that used the slot has finished)
+    while (loss_issued && next_g <= L) {
+      const int st = item_done(grad_item[next_g]);
+      if (st < 0) { rc = st; break; }
+      if (!st) break;
+      if (!keep && next_g >= c.ring && !abort && !adam_is_done(next_g - c.ring)) break;
+      if ((rc = issue_grad(next_g))) break;
+      ++next_g;
+      progress = true;
+    }
+    if (rc) break;
+    // AdamW of each unit as its gradients land (after the loss is known finite)
+    while (loss_checked && next_a < next_g) {
+      const int st = event_done(E.drained[next_a]);
+      if (st < 0) { rc = st; break; }
+      if (!st) break;
+      last_land_ms = ms_since(t_begin);
+      if (!abort) {
+        Unit& u = grad_unit(next_a);
+        add_pending();
+        adam_start_ms[next_a] = last_land_ms;
+        const int kk = next_a;
+        submit_adamw(c, u, grad_dest(kk), {{0, u.lay.n}}, k, [&, kk] { job_done(kk); }, &adam_ns);
+      } else {
+        std::lock_guard<std::mutex> g(amu);
+        adam_done[next_a] = 1;
+      }
+      ++next_a;
+      progress = true;
+    }
+    if (rc) break;
+    // the input gradient of layer 0 goes to the host for the embedding scatter
+    if (!dx0_issued && next_g > L) {
+      if ((rc = issue_dx0())) break;
+      dx0_issued = progress = true;
+    }
+    if (dx0_issued && !dx0_done) {
+      const int st = event_done(E.dx0);
+      if (st < 0) { rc = st; break; }
+      if (st) dx0_done = progress = true;
+    }
+    if (dx0_done && next_a > L) break;
+    if (!progress) std::this_thread::sleep_for(std::chrono::microseconds(10));
+  }
+  if (rc) {
+    // drain what was submitted before reporting the error
+    hipStreamSynchronize(c.s_in);
+    hipStreamSynchronize(c.s_comp);
+    hipStreamSynchronize(c.s_out);
+    std::unique_lock<std::mutex> lk(amu);
+    acv.wait(lk, [&] { return pending == 0; });
+    return rc;
+  }
+
+  // ---- embedding: dE[v] += dx0[r] over positions r of token v, in increasing r ----
+  last_land_ms = ms_since(t_begin);
+  if (!abort) {
+    const int64_t nr = (int64_t)rows.size();
+    const int64_t per = 64;
+    adam_start_ms[L + 1] = ms_since(t_begin);
+    c.pool->run((nr + per - 1) / per, [&](int64_t i) {
+      for (int64_t j = i * per; j < std::min(nr, (i + 1) * per); ++j) {
+        const int32_t v = rows[j];
+        float* dst = emb.g + (int64_t)v * d;
+        for (int32_t q = cnt[v]; q < cnt[v + 1]; ++q) {
+          const float* src = c.dx0_host + (int64_t)pos[q] * d;
+          for (int64_t e = 0; e < d; ++e) dst[e] += src[e];
+        }
+      }
+    });
+    // AdamW of the touched rows, in runs of consecutive rows
+    std::vector<std::pair<int64_t, int64_t>> runs;
+    size_t a = 0;
+    while (a < rows.size()) {
+      size_t b = a + 1;
+      while (b < rows.size() && rows[b] == rows[b - 1] + 1) ++b;
+      runs.push_back({(int64_t)rows[a] * d, (int64_t)(rows[b - 1] + 1) * d});
+      a = b;
+    }
+    add_pending();
+    submit_adamw(c, emb, emb.g, std::move(runs), k, [&] { job_done(-1); }, &adam_ns);
+  }
+  {
+    std::unique_lock<std::mutex> lk(amu);
+    acv.wait(lk, [&] { return pending == 0; });
+  }
+  adam_end_ms[L + 1] = ms_since(t_begin);
+  const hipError_t s1 = hipStreamSynchronize(c.s_in), s2 = hipStreamSynchronize(c.s_comp),
+                   s3 = hipStreamSynchronize(c.s_out);
+  if (s1 != hipSuccess || s2 != hipSuccess || s3 != hipSuccess)
+    return set_error(&c, MT_EHIP, std::string("stream synchronize: ") +
+                                      hipGetErrorString(s1 != hipSuccess ? s1 : s2 != hipSuccess ? s2 : s3));
+
+  const double step_ms = ms_since(t_begin);
+  const double loss = loss_sum / (double)M;
+  c.token_loss.assign(c.loss_host, c.loss_host + M);
+
+  // ---- statistics ----
+  mt_step_stats& st = c.stats;
+  st = mt_step_stats{};
+  st.step_ms = step_ms;
+  st.forward_ms = forward_ms;
+  st.h2d_bytes = h2d_bytes;
+  st.d2h_bytes = d2h_bytes;
+  st.adamw_ms = (double)adam_ns.load() * 1e-6;
+  int64_t n_all = 0;
+  for (auto& u : c.units) n_all += u.lay.n;
+  st.adamw_bytes = (double)n_all * (16.0 + 12.0 + (c.dtype ? 2.0 : 0.0));
+  st.tail_ms = step_ms - last_land_ms;
+  st.tokens = M;
+  {
+    const double Nl = (double)D.qkvd * d + (double)d * D.qd + 3.0 * d * D.F;
+    const double Nh = (double)D.V * d;
+    const double Af = 2.0 * B * (double)T * T * D.H * D.hd;
+    st.model_flops = 6.0 * (Nl * L + Nh) * (double)M + 3.0 * L * Af;
+    st.hw_flops = st.model_flops + L * (2.0 * (Nl - (double)d * D.F) * (double)M + Af);
+  }
+  if (trace) {
+    float t;
+    auto rel = [&](hipEvent_t e) {
+      return hipEventElapsedTime(&t, E.start, e) == hipSuccess ? (double)t : -1.0;
+    };
+    for (int i = 0; i < n_items; ++i) {
+      const Item& it = items[i];
+      const int unit = it.phase == PH_HEAD ? MT_UNIT_HEAD : it.unit;
+      if (it.load) {
+        const double a = rel(trace_ev(i, 0)), b = rel(trace_ev(i, 1));
+        c.sched.push_back({MT_PH_LOAD, unit, it.buf, 0, a, b});
+        st.h2d_busy_ms += b - a;
+      }
+      const double a = rel(trace_ev(i, 2)), b = rel(trace_ev(i, 3));
+      c.sched.push_back({it.phase, unit, it.buf, 1, a, b});
+      st.compute_busy_ms += b - a;
+      if (it.grad_k >= 0) {
+        const double a2 = rel(trace_ev(i, 4)), b2 = rel(trace_ev(i, 5));
+        c.sched.push_back({MT_PH_GRAD, unit, it.grad_k % 2, 2, a2, b2});
+        st.d2h_busy_ms += b2 - a2;
+      }
+    }
+    // host AdamW entries on the same clock (device times are relative to the
+    // start event, host times to the moment it completed)
+    const double off = std::chrono::duration<double, std::milli>(t_dev0 - t_begin).count();
+    for (int kk = 0; kk <= L; ++kk) {
+      const int unit = kk == 0 ? MT_UNIT_HEAD : L - kk;
+      c.sched.push_back({MT_PH_ADAMW, unit, -1, 3, adam_start_ms[kk] - off, adam_end_ms[kk] - off});
+    }
+    c.sched.push_back({MT_PH_ADAMW, MT_UNIT_EMB, -1, 3, adam_start_ms[L + 1] - off, adam_end_ms[L + 1] - off});
+    for (auto& h : host_spans) c.sched.push_back({h.phase, h.unit, -1, 4, h.t0 - off, h.t1 - off});
+  }
+  if (c.kt.on) {
+    c.kstats.assign(K_COUNT * 2, mt_kernel_stat{});
+    static const char* names[K_COUNT] = {"gemm_nt", "gemm_nn", "gemm_tn", "attn_fwd", "attn_bwd",
+                                         "rmsnorm_fwd", "rmsnorm_bwd", "rope", "swiglu", "xent",
+                                         "cast", "other"};
+    for (int i = 0; i < K_COUNT; ++i)
+      snprintf(c.kstats[i].name, sizeof(c.kstats[i].name), "%s_%s", names[i], c.dtype ? "bf16" : "fp32");
+    for (auto& r : c.kt.recs) {
+      float t = 0.f;
+      hipEventElapsedTime(&t, c.kt.ev[r.e], c.kt.ev[r.e + 1]);
+      mt_kernel_stat& s = c.kstats[r.cls];
+      s.launches++;
+      s.ms += t;
+      s.flops += r.flops;
+      s.bytes += r.bytes;
+    }
+    c.kstats.resize(K_COUNT);
+  }
+
+  if (abort) return set_error(&c, MT_ENONFINITE, "loss is not finite; no update applied");
+  c.step++;
+  st.step = c.step;
+  if (loss_out) *loss_out = (float)loss;
+  return MT_OK;
+}
+
+}  // namespace mt

@@ -1,0 +1,203 @@
+/*
+ * mt.h - C ABI of the layer-streamed transformer training step.
+ *
+ * Method ("MegaTrain: Full Precision Training of 100B+ Parameter LLMs on a
+ * Single GPU", abstract): parameters and optimizer state live in host memory
+ * and the GPU is a transient compute engine; per layer, parameters stream in
+ * and gradients stream out; a double-buffered pipeline overlaps prefetch,
+ * compute and gradient offload on several streams; stateless layer templates
+ * are bound to whichever weights are resident. Activations are recomputed in
+ * backward and the optimizer step runs on the CPU over fp32 master weights and
+ * moments ("Technical Brief: MegaTrain's Single-GPU 120B-Parameter Training
+ * Breakthrough", section "Checkpointing, Manual Gradients, and CPU-Side
+ * Optimizer Steps").
+ *
+ * The model is a Llama-style decoder: RMSNorm, half-split rotary embeddings,
+ * causal grouped-query attention, SwiGLU MLP, final RMSNorm, untied LM head,
+ * mean next-token cross-entropy, AdamW with decoupled weight decay.
+ *
+ * Conventions for every entry point:
+ *  - Return 0 (MT_OK) on success, a negative MT_E* code on failure; no C++
+ *    exception crosses the ABI. After an error, mt_last_error() describes it
+ *    and the context can still be destroyed.
+ *  - Pointers are plain host pointers unless stated otherwise.
+ *  - Calls on one context are not thread-safe: the caller serialises them.
+ *
+ * Canonical tensor order (ids used by mt_set_param / mt_params / mt_grads /
+ * mt_opt_state), all fp32, row-major, Linear weights [out, in] (y = x W^T):
+ *   0                 tok_emb   [vocab, d]
+ *   1 + 9*l + 0..8    layer l:  attn_norm [d], wq [H*hd, d], wk [Hkv*hd, d],
+ *                               wv [Hkv*hd, d], wo [d, H*hd], mlp_norm [d],
+ *                               w_gate [F, d], w_up [F, d], w_down [d, F]
+ *   1 + 9*L           final_norm [d]
+ *   2 + 9*L           lm_head   [vocab, d]
+ */
+#ifndef MT_H
+#define MT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- error codes ---- */
+#define MT_OK 0
+#define MT_EINVAL -1      /* bad config, id, shape, pointer, or token id outside [0, vocab) */
+#define MT_EHOSTOOM -2    /* host (pinned or pageable) allocation failed */
+#define MT_EDEVOOM -3     /* device allocation failed */
+#define MT_EHIP -4        /* a HIP runtime call failed; mt_last_error() has its text */
+#define MT_ENONFINITE -5  /* the step's loss was not finite: no update was applied */
+#define MT_ETIMEOUT -6    /* a host-side wait exceeded its limit */
+#define MT_ENOGRADS -7    /* gradients were not kept (MT_KEEP_GRADS off) */
+#define MT_ESTATE -8      /* call not valid in the context's current state */
+
+/* ---- compute dtypes ---- */
+#define MT_FP32 0   /* fp32 weights streamed, fp32 matrix-core products */
+#define MT_BF16 1   /* bf16 shadow streamed, bf16 operands, fp32 accumulation */
+
+/* ---- flags ---- */
+#define MT_KEEP_GRADS 1u     /* keep every tensor's gradient in host memory (mt_grads) */
+#define MT_KERNEL_TIMING 2u  /* time every kernel launch with HIP events (mt_kernel_stats) */
+#define MT_TRACE 4u          /* record the per-unit schedule log (mt_schedule, mt_trace_dump) */
+
+typedef struct mt_model_cfg {
+  int32_t n_layers;
+  int32_t d_model;
+  int32_t n_heads;
+  int32_t n_kv_heads;   /* must divide n_heads; query head h reads kv head h / (H/Hkv) */
+  int32_t head_dim;     /* fp32: 16, 32, 64 or 128; bf16: 64 or 128 */
+  int32_t ffn_dim;
+  int32_t vocab;
+  int32_t max_batch;    /* largest B accepted by mt_train_step */
+  int32_t max_seq;      /* largest T accepted by mt_train_step */
+  int32_t compute_dtype;     /* MT_FP32 or MT_BF16 */
+  int32_t n_layer_buffers;   /* 2 = streamed; >= n_layers + 1 = every layer resident */
+  int32_t host_threads;      /* AdamW / gather pool size; 0 = online CPUs (at most 64) */
+  uint32_t flags;            /* MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE */
+  float rms_eps;
+  float rope_base;
+  double lr, beta1, beta2, adam_eps, weight_decay;   /* AdamW hyperparameters */
+} mt_model_cfg;
+
+/* Optional streams for the three pipeline stages (hipStream_t values passed as
+ * void*). NULL env, or a NULL member, makes the library create its own. */
+typedef struct mt_device_env {
+  void* copy_in;
+  void* compute;
+  void* copy_out;
+} mt_device_env;
+
+typedef struct mt_ctx mt_ctx;
+
+/* Number of tensors in the canonical order: 9 * n_layers + 3. */
+int32_t mt_tensor_count(const mt_model_cfg* cfg);
+
+/* Name (NUL-terminated, truncated to name_cap) and shape of tensor id.
+ * ndim is 1 or 2; shape[1] is 1 for vectors. */
+int mt_tensor_info(const mt_model_cfg* cfg, int32_t id, char* name, int32_t name_cap,
+                   int64_t shape[2], int32_t* ndim);
+
+/* Create a context: validates cfg, allocates the host store (fp32 master p,
+ * AdamW m and v zeroed, step count 0, the bf16 device-format shadow in bf16
+ * mode, gradient buffers), the device layer buffers, gradient buffers,
+ * checkpoints and activation workspace, the three streams and the events.
+ * host_param_ptrs: NULL (parameters start at zero; fill them with mt_set_param)
+ * or an array of mt_tensor_count(cfg) caller-owned fp32 tensors in canonical
+ * order, copied during the call. On failure *out is NULL and
+ * mt_last_error(NULL) describes the error. */
+int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs,
+              const mt_device_env* env, mt_ctx** out);
+
+/* Copy one tensor's fp32 values into the master store and refresh its
+ * device-format shadow. Valid between steps. */
+int mt_set_param(mt_ctx* ctx, int32_t id, const float* src);
+
+/* One training step on tokens / targets, each [B, T] int32 row-major
+ * (read during the call; every id must lie in [0, vocab)). Synchronous: it
+ * returns after every AdamW update has landed in host memory. *loss_out is
+ * the mean cross-entropy over the B*T positions. On MT_ENONFINITE the state is
+ * unchanged and the step count is not advanced. */
+int mt_train_step(mt_ctx* ctx, const int32_t* tokens, const int32_t* targets, int32_t B,
+                  int32_t T, float* loss_out);
+
+/* Per-token losses of the last step in (b, t) order: *n = B*T. Library-owned,
+ * valid until the next mt_train_step or mt_destroy. */
+int mt_token_losses(mt_ctx* ctx, const float** ptr, int64_t* n);
+
+/* Read-only, library-owned views of the fp32 master parameters, the raw
+ * gradients dL/dp of the last step (MT_ENOGRADS unless MT_KEEP_GRADS), and
+ * the AdamW moments with the step count. Valid until the next
+ * mt_train_step / mt_set_param / mt_destroy. */
+int mt_params(mt_ctx* ctx, int32_t id, const float** ptr, int64_t* numel);
+int mt_grads(mt_ctx* ctx, int32_t id, const float** ptr, int64_t* numel);
+int mt_opt_state(mt_ctx* ctx, int32_t id, const float** m, const float** v, int64_t* t);
+
+typedef struct mt_step_stats {
+  double step_ms;          /* wall time of the last mt_train_step */
+  double forward_ms;       /* start of step to the loss being known on the host */
+  double h2d_bytes, d2h_bytes;      /* bytes moved over the host link by the step */
+  double h2d_busy_ms, d2h_busy_ms;  /* summed copy durations (MT_TRACE only, else 0) */
+  double compute_busy_ms;           /* summed unit compute durations (MT_TRACE only, else 0) */
+  double adamw_ms;         /* summed wall time of the host AdamW tasks */
+  double adamw_bytes;      /* host DRAM bytes the AdamW pass reads and writes */
+  double tail_ms;          /* from the last gradient landing to the step's return */
+  double model_flops;      /* 6 * matmul params * tokens + causal attention (fwd + bwd) */
+  double hw_flops;         /* model FLOPs plus the recompute */
+  int64_t tokens;
+  int64_t step;            /* AdamW step count after the step */
+} mt_step_stats;
+
+int mt_stats(mt_ctx* ctx, mt_step_stats* out);
+
+/* Per-kernel-class totals of the last step (needs MT_KERNEL_TIMING), measured
+ * with HIP events on the compute stream around each launch. */
+#define MT_KCLASS_COUNT 12
+typedef struct mt_kernel_stat {
+  char name[32];           /* e.g. "gemm_nt_bf16" */
+  int64_t launches;
+  double ms;               /* summed launch durations */
+  double flops;            /* summed algorithmic FLOPs (2*M*N*K for products) */
+  double bytes;            /* summed algorithmic HBM bytes */
+} mt_kernel_stat;
+
+int mt_kernel_stats(mt_ctx* ctx, mt_kernel_stat* out, int32_t cap, int32_t* n);
+
+/* Schedule log of the last step (needs MT_TRACE): one entry per unit stage. */
+#define MT_PH_LOAD 0      /* H2D of a unit image into a layer buffer (stream 0) */
+#define MT_PH_FWD 1       /* forward of a layer (stream 1) */
+#define MT_PH_HEAD 2      /* head forward + backward (stream 1) */
+#define MT_PH_BWD 3       /* recompute + backward of a layer (stream 1) */
+#define MT_PH_GRAD 4      /* D2H of a unit's gradients (stream 2) */
+#define MT_PH_ADAMW 5     /* host AdamW of a unit (stream 3 = host) */
+#define MT_UNIT_EMB -1
+#define MT_UNIT_HEAD -2
+typedef struct mt_sched_entry {
+  int32_t phase;
+  int32_t unit;            /* layer index, MT_UNIT_HEAD or MT_UNIT_EMB */
+  int32_t buffer;          /* layer buffer (LOAD/FWD/HEAD/BWD) or gradient buffer (GRAD) */
+  int32_t stream;          /* 0 copy-in, 1 compute, 2 copy-out, 3 host AdamW,
+                              4 host time spent submitting the stage's work */
+  double t0_ms, t1_ms;     /* relative to the start of the step */
+} mt_sched_entry;
+
+int mt_schedule(mt_ctx* ctx, mt_sched_entry* out, int32_t cap, int32_t* n);
+
+/* Write the schedule log as Chrome trace-event JSON. */
+int mt_trace_dump(mt_ctx* ctx, const char* path);
+
+/* Device bytes the context holds (buffers, checkpoints, workspace). */
+int mt_device_bytes(mt_ctx* ctx, int64_t* bytes);
+
+/* Text of the last error on ctx (or of the last failed mt_create on this
+ * thread when ctx is NULL). Never NULL. */
+const char* mt_last_error(const mt_ctx* ctx);
+
+void mt_destroy(mt_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MT_H */

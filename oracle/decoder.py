@@ -48,6 +48,14 @@ the same points and accumulates in float64:
   loss, ``D = rowsum(dO * O)``, the weight gradients, AdamW) stays full
   precision.
 
+Where P is rounded has two readings. The plain one (``mode="bf16"``) rounds
+the normalised probabilities P = softmax(S). A flash-style kernel never holds
+the normalised P before the product with V: it rounds exp(S - m) against the
+running row maximum m over successive key blocks, rescales the partial sums
+when m grows, and divides by the row sum at the end. ``mode="bf16-flash64"``
+follows that reading with 64-key blocks (the rest is identical; the backward
+rounds the normalised P recomputed from the logsumexp in both readings).
+
 The exact rounding outcomes in bf16 mode are parity unpinned: they are checked
 to a tolerance only.
 
@@ -118,13 +126,14 @@ def fp32(x) -> np.ndarray:
 
 class _Prec:
     def __init__(self, mode: str):
-        if mode not in ("fp32", "bf16"):
+        if mode not in ("fp32", "bf16", "bf16-flash64"):
             raise ValueError(mode)
         self.mode = mode
+        self.p_block = 64 if mode == "bf16-flash64" else None
 
     def op(self, x):
         """Operand of a matrix product."""
-        return bf16(x) if self.mode == "bf16" else x
+        return bf16(x) if self.mode != "fp32" else x
 
 
 # ----------------------------------------------------------------------------
@@ -188,12 +197,28 @@ def attention_fwd(q, k, v, prec: _Prec):
             kv = h // grp
             S = (q[b, :, h, :] @ k[b, :, kv, :].T) * scale
             S[mask] = -np.inf
-            m = S.max(axis=1, keepdims=True)
-            e = np.exp(S - m)
-            l = e.sum(axis=1, keepdims=True)
-            P = e / l
-            lse[b, h] = (m + np.log(l))[:, 0]
-            o[b, :, h, :] = prec.op(P) @ v[b, :, kv, :]
+            if prec.p_block is None:
+                m = S.max(axis=1, keepdims=True)
+                e = np.exp(S - m)
+                l = e.sum(axis=1, keepdims=True)
+                P = e / l
+                lse[b, h] = (m + np.log(l))[:, 0]
+                o[b, :, h, :] = prec.op(P) @ v[b, :, kv, :]
+            else:
+                # running maximum over key blocks; unnormalised probabilities rounded
+                m = np.full(T, -np.inf)
+                l = np.zeros(T)
+                acc = np.zeros((T, hd))
+                for k0 in range(0, T, prec.p_block):
+                    s = S[:, k0:k0 + prec.p_block]
+                    mn = np.maximum(m, s.max(axis=1))
+                    a = np.exp(m - mn)
+                    e = np.exp(s - mn[:, None])
+                    l = l * a + e.sum(axis=1)
+                    acc = acc * a[:, None] + prec.op(e) @ v[b, k0:k0 + prec.p_block, kv, :]
+                    m = mn
+                o[b, :, h, :] = acc / l[:, None]
+                lse[b, h] = m + np.log(l)
     return o, lse
 
 

@@ -1,0 +1,116 @@
+"""CPU checks of the C-ABI library: it loads, exports every declared entry
+point, reports the canonical tensor table, rejects bad configurations before
+touching a device, and its host-side AdamW and RoPE table agree with the
+oracle."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from oracle.configs import SHAPES
+from host_memory_streamed_amd import mt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    if not os.path.exists(mt.LIB_PATH):
+        from host_memory_streamed_amd import build
+        build.build_mt()
+
+
+def _declared():
+    names = set()
+    for h in ("mt.h", "mt_ops.h"):
+        txt = open(os.path.join(ROOT, "include", h)).read()
+        txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+        names |= set(re.findall(r"\b(mt_\w+)\s*\(", txt))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(mt.LIB_PATH)
+    declared = _declared()
+    assert len(declared) >= 30
+    for name in sorted(declared):
+        assert hasattr(L, name), name
+    assert declared == set(mt.exported_names())
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_tensor_table_matches_oracle(name):
+    cfg, B, T = SHAPES[name]
+    c = mt.make_config(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn_dim,
+                       cfg.vocab, B, T, dtype=mt.MT_BF16)
+    lib_table = mt.tensor_table(c)
+    orc = O.tensor_table(cfg)
+    assert [n for n, _ in lib_table] == [n for n, _, _ in orc]
+    assert [tuple(s) for _, s in lib_table] == [tuple(s) for _, s, _ in orc]
+
+
+@pytest.mark.parametrize("field,value", [("n_layers", 0), ("n_kv_heads", 3), ("head_dim", 48),
+                                         ("compute_dtype", 7), ("n_layer_buffers", 1), ("d_model", 66),
+                                         ("max_seq", 0), ("flags", 1 << 10)])
+def test_create_rejects_bad_config(field, value):
+    c = mt.make_config(2, 64, 4, 4, 16, 172, 256, 2, 32)
+    setattr(c, field, value)
+    h = ctypes.c_void_p()
+    rc = mt.lib().mt_create(ctypes.byref(c), None, None, ctypes.byref(h))
+    assert rc == mt.MT_EINVAL and not h.value
+    assert mt.lib().mt_last_error(None)
+
+
+def test_bf16_head_dim_restriction():
+    c = mt.make_config(2, 64, 4, 4, 16, 172, 256, 2, 32, dtype=mt.MT_BF16)
+    h = ctypes.c_void_p()
+    assert mt.lib().mt_create(ctypes.byref(c), None, None, ctypes.byref(h)) == mt.MT_EINVAL
+
+
+def test_host_adamw_matches_oracle_over_steps():
+    # Each step starts both sides from the same fp32 state; the fp32 error of
+    # each update is bounded by a few ulps of the terms it sums.
+    cfg = O.Config(1, 8, 1, 1, 8, 8, 8)
+    rng = np.random.default_rng(5)
+    n = 100_003   # ragged against the vector width and the chunking
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    bf = np.empty(n, np.uint16)
+    u = 2.0 ** -23
+    for t in range(1, 5):
+        g = (rng.standard_normal(n) * 10.0 ** rng.integers(-9, -1, n)).astype(np.float32)
+        p0, m0, v0 = (a.astype(np.float64) for a in (p, m, v))
+        g64 = g.astype(np.float64)
+        mt.adamw_host(p, m, v, g, t, cfg.lr, cfg.beta1, cfg.beta2, cfg.adam_eps, cfg.weight_decay, bf16_out=bf,
+                      threads=4)
+        P, Mo, Vo = O.adamw(p0, g64, m0, v0, t, cfg)
+        assert np.all(np.abs(m - Mo) <= 4 * u * (0.9 * np.abs(m0) + 0.1 * np.abs(g64)) + 1e-45)
+        assert np.all(np.abs(v - Vo) <= 4 * u * (0.999 * v0 + 0.001 * g64 * g64) + 1e-45)
+        step = cfg.lr * (Mo / (1 - 0.9 ** t)) / (np.sqrt(Vo / (1 - 0.999 ** t)) + cfg.adam_eps)
+        assert np.all(np.abs(p - P) <= 8 * u * (np.abs(p0) + np.abs(step)) + 1e-45)
+        # the bf16 image is exactly the rounding of the updated fp32 value
+        img = (bf.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        np.testing.assert_array_equal(img, O.bf16(p))
+
+
+def test_host_adamw_rejects_bad_arguments():
+    a = np.zeros(4, np.float32)
+    with pytest.raises(mt.MTError):
+        mt.adamw_host(a, a.copy(), a.copy(), a.copy(), 0, 1e-3, 0.9, 0.999, 1e-8, 0.01)
+
+
+def test_rope_table_matches_oracle():
+    for T, hd in ((33, 16), (4096, 128)):
+        c, s = mt.rope_table(T, hd, 10000.0)
+        oc, os_ = O.rope_tables(T, hd, 10000.0)
+        np.testing.assert_allclose(c, oc, rtol=0, atol=6e-8)
+        np.testing.assert_allclose(s, os_, rtol=0, atol=6e-8)
+    # far positions: the table is built in double, so the angle stays exact
+    c, s = mt.rope_table(524288, 2, 10000.0)
+    t = 524287
+    assert abs(c[t, 0] - math.cos(t)) < 1e-7 and abs(s[t, 0] - math.sin(t)) < 1e-7

@@ -1,0 +1,301 @@
+"""Each kernel of the step, called through the C-ABI (mt_op_*), against the
+oracle's operation on the same seeded inputs.
+
+Small shapes span several tiles and a ragged tail; the full 14B per-layer
+shapes are checked on sampled outputs that the oracle computes one by one.
+Tolerances: fp32 results within a few fp32 ulps of the sum of absolute terms;
+bf16-mode results within 2e-2 * (|ref| + rms(ref)) of the bf16-emulating
+oracle (exact bf16 rounding outcomes are not pinned)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from host_memory_streamed_amd import mt  # noqa: E402
+
+DEV = "cuda"
+RNG = np.random.default_rng(42)
+
+
+def dev(a, dtype=torch.float32):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(dtype)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def bf16_close(gpu, ref, tol=2e-2, floor=0.0):
+    scale = np.abs(ref) + np.sqrt(np.mean(ref ** 2)) + floor + 1e-30
+    bad = np.abs(gpu - ref) > tol * scale
+    assert not bad.any(), f"{bad.sum()} of {bad.size} outside bf16 tolerance; max {np.max(np.abs(gpu - ref) / scale)}"
+
+
+def fp32_close(gpu, ref, absterm, ulps=64):
+    bound = ulps * 2.0 ** -24 * absterm + 1e-30
+    bad = np.abs(gpu - ref) > bound
+    assert not bad.any(), f"{bad.sum()} of {bad.size} outside fp32 bound; worst ratio {np.max(np.abs(gpu - ref) / bound)}"
+
+
+# -------------------------------------------------------------------- GEMM ---
+
+def _gemm_case(dtype, layout, M, N, K, residual=False, sample=None):
+    # logical operands: X [M, K], Y [K, N]; stored per layout
+    X = RNG.standard_normal((M, K)).astype(np.float32)
+    Y = RNG.standard_normal((K, N)).astype(np.float32)
+    if dtype == mt.MT_BF16:
+        X, Y = O.bf16(X).astype(np.float32), O.bf16(Y).astype(np.float32)
+    tdt = torch.bfloat16 if dtype == mt.MT_BF16 else torch.float32
+    if layout == mt.MT_GEMM_NT:
+        A, B, lda, ldb = dev(X, tdt), dev(Y.T, tdt), K, K
+    elif layout == mt.MT_GEMM_NN:
+        A, B, lda, ldb = dev(X, tdt), dev(Y, tdt), K, N
+    else:
+        A, B, lda, ldb = dev(X.T, tdt), dev(Y, tdt), M, N
+    R = RNG.standard_normal((M, N)).astype(np.float32) if residual else None
+    C = torch.full((M, N), float("nan"), device=DEV)
+    Rd = dev(R) if residual else None
+    mt.gemm(dtype, layout, A, lda, B, ldb, C, N, M, N, K, R=Rd, ldr=N)
+    got = host(C)
+    X64, Y64 = X.astype(np.float64), Y.astype(np.float64)
+    if sample is None:
+        ref = X64 @ Y64 + (R if residual else 0)
+        absterm = np.abs(X64) @ np.abs(Y64) + (np.abs(R) if residual else 0)
+        fp32_close(got, ref, absterm)
+    else:
+        ii = RNG.integers(0, M, sample)
+        jj = RNG.integers(0, N, sample)
+        ref = np.einsum("sk,ks->s", X64[ii], Y64[:, jj])
+        absterm = np.einsum("sk,ks->s", np.abs(X64[ii]), np.abs(Y64[:, jj]))
+        fp32_close(got[ii, jj], ref, absterm)
+
+
+@pytest.mark.parametrize("dtype", [mt.MT_FP32, mt.MT_BF16])
+@pytest.mark.parametrize("layout", [mt.MT_GEMM_NT, mt.MT_GEMM_NN, mt.MT_GEMM_TN])
+@pytest.mark.parametrize("M,N,K", [(128, 128, 64), (256, 384, 96), (200, 72, 40), (1, 3, 5), (300, 172, 64),
+                                   (64, 172, 300)])
+def test_gemm_small_and_ragged(dtype, layout, M, N, K):
+    _gemm_case(dtype, layout, M, N, K, residual=(M % 2 == 0))
+
+
+@pytest.mark.parametrize("layout,M,N,K", [(mt.MT_GEMM_NT, 4096, 7168, 5120), (mt.MT_GEMM_NN, 4096, 5120, 13824),
+                                          (mt.MT_GEMM_TN, 27648, 5120, 4096)])
+def test_gemm_full_14b_shapes_sampled(layout, M, N, K):
+    _gemm_case(mt.MT_BF16, layout, M, N, K, sample=512)
+
+
+def test_gemm_k_zero_gives_residual():
+    R = dev(RNG.standard_normal((5, 7)))
+    C = torch.zeros(5, 7, device=DEV)
+    A = torch.zeros(1, device=DEV)
+    mt.gemm(mt.MT_FP32, mt.MT_GEMM_NT, A, 1, A, 1, C, 7, 5, 7, 0, R=R, ldr=7)
+    np.testing.assert_array_equal(host(C), host(R))
+
+
+def test_gemm_rejects_bad_leading_dimension():
+    A = torch.zeros(64, device=DEV)
+    with pytest.raises(mt.MTError):
+        mt.gemm(mt.MT_FP32, mt.MT_GEMM_NT, A, 4, A, 8, A, 8, 8, 8, 8)
+
+
+# ----------------------------------------------------------------- RMSNorm ---
+
+@pytest.mark.parametrize("dtype", [mt.MT_FP32, mt.MT_BF16])
+@pytest.mark.parametrize("rows,d", [(37, 64), (300, 2048), (5, 5120)])
+def test_rmsnorm(dtype, rows, d):
+    x = RNG.standard_normal((rows, d)).astype(np.float32) * 3
+    w = RNG.standard_normal(d).astype(np.float32)
+    dy = RNG.standard_normal((rows, d)).astype(np.float32)
+    acc0 = RNG.standard_normal((rows, d)).astype(np.float32)
+    tdt = torch.bfloat16 if dtype else torch.float32
+    xd, wd = dev(x), dev(w)
+    y = torch.empty(rows, d, device=DEV, dtype=tdt)
+    rstd = torch.empty(rows, device=DEV)
+    mt.rmsnorm_fwd(dtype, xd, wd, y, rstd, rows, d, 1e-5)
+    yref, rref = O.rmsnorm_fwd(x.astype(np.float64), w.astype(np.float64), 1e-5)
+    np.testing.assert_allclose(host(rstd), rref, rtol=2e-6)
+    if dtype:
+        assert np.all(np.abs(host(y) - yref) <= 2.0 ** -8 * np.abs(yref) + 1e-30)
+    else:
+        fp32_close(host(y), yref, np.abs(yref), ulps=8)
+    # backward (accumulating into an existing gradient)
+    dx = dev(acc0)
+    dw = torch.empty(d, device=DEV)
+    ws = torch.empty(mt.rmsnorm_bwd_ws_floats(rows, d), device=DEV)
+    mt.rmsnorm_bwd(xd, wd, rstd, dev(dy), dx, 1, dw, ws, rows, d)
+    dxr, dwr = O.rmsnorm_bwd(x.astype(np.float64), w.astype(np.float64), host(rstd), dy.astype(np.float64))
+    gw = np.abs(dy * w)
+    np.testing.assert_allclose(host(dx), dxr + acc0, rtol=1e-4, atol=1e-5 * np.sqrt(np.mean(dxr ** 2)))
+    fp32_close(host(dw), dwr, np.sum(np.abs(dy * x) * host(rstd)[:, None], axis=0), ulps=512)
+    del gw
+
+
+# -------------------------------------------------------------------- RoPE ---
+
+@pytest.mark.parametrize("dtype", [mt.MT_FP32, mt.MT_BF16])
+@pytest.mark.parametrize("B,T,H,Hkv,hd", [(2, 33, 4, 2, 16), (1, 300, 8, 2, 128)])
+def test_rope(dtype, B, T, H, Hkv, hd):
+    W = (H + 2 * Hkv) * hd
+    x = RNG.standard_normal((B * T, W)).astype(np.float32)
+    c, s = mt.rope_table(T, hd, 10000.0)
+    tdt = torch.bfloat16 if dtype else torch.float32
+    out = torch.empty(B * T, W, device=DEV, dtype=tdt)
+    cos, sin = O.rope_tables(T, hd, 10000.0)
+    for bwd in (0, 1):
+        mt.rope(dtype, bwd, dev(x), out, dev(c), dev(s), B, T, H, Hkv, hd)
+        xr = x.astype(np.float64).reshape(B, T, H + 2 * Hkv, hd)
+        f = O.rope_bwd if bwd else O.rope_fwd
+        ref = np.concatenate([f(xr[:, :, :H + Hkv], cos, sin), xr[:, :, H + Hkv:]], axis=2).reshape(B * T, W)
+        got = host(out)
+        if dtype:
+            assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+        else:
+            np.testing.assert_allclose(got, ref, rtol=0, atol=3e-6 * np.max(np.abs(ref)))
+
+
+# --------------------------------------------------------------- attention ---
+
+def _attn_inputs(B, T, H, Hkv, hd, dtype, scale=1.0):
+    qkv = (RNG.standard_normal((B * T, (H + 2 * Hkv) * hd)) * scale).astype(np.float32)
+    if dtype:
+        qkv = O.bf16(qkv).astype(np.float32)
+    return qkv
+
+
+def _split(qkv, B, T, H, Hkv, hd):
+    a = qkv.astype(np.float64).reshape(B, T, H + 2 * Hkv, hd)
+    return a[:, :, :H], a[:, :, H:H + Hkv], a[:, :, H + Hkv:]
+
+
+@pytest.mark.parametrize("dtype,hd", [(mt.MT_FP32, 16), (mt.MT_FP32, 32), (mt.MT_FP32, 64), (mt.MT_FP32, 128),
+                                      (mt.MT_BF16, 64), (mt.MT_BF16, 128)])
+@pytest.mark.parametrize("B,T,H,Hkv", [(2, 100, 4, 2), (1, 130, 4, 4), (1, 1, 2, 1), (1, 257, 8, 1)])
+def test_attention_fwd_bwd(dtype, hd, B, T, H, Hkv):
+    tdt = torch.bfloat16 if dtype else torch.float32
+    qkv = _attn_inputs(B, T, H, Hkv, hd, dtype)
+    q, k, v = _split(qkv, B, T, H, Hkv, hd)
+    # bf16: the kernel rounds P against a running maximum over 64-key blocks
+    prec = O.decoder._Prec("bf16-flash64" if dtype else "fp32")
+    oref, lref = O.attention_fwd(q, k, v, prec)
+    if dtype:
+        oplain, _ = O.attention_fwd(q, k, v, O.decoder._Prec("bf16"))
+    M = B * T
+    qd = dev(qkv, tdt)
+    o = torch.full((M, H * hd), float("nan"), device=DEV)
+    oc = torch.empty(M, H * hd, device=DEV, dtype=tdt) if dtype else None
+    lse = torch.empty(B, H, T, device=DEV)
+    mt.attn_fwd(dtype, qd, o, oc, lse, B, T, H, Hkv, hd)
+    got = host(o).reshape(B, T, H, hd)
+    np.testing.assert_allclose(host(lse), lref, rtol=1e-5, atol=1e-5)
+    if dtype:
+        bf16_close(got, oref, tol=2e-3)
+        assert np.linalg.norm(got - oplain) <= 2e-2 * np.linalg.norm(oplain)
+        assert np.all(np.abs(host(oc).reshape(got.shape) - got) <= 2.0 ** -8 * np.abs(got) + 1e-30)
+    else:
+        np.testing.assert_allclose(got, oref, rtol=1e-4, atol=1e-5)
+    # backward, both sides from the same forward output o and lse
+    do = RNG.standard_normal((B, T, H, hd))
+    dqr, dkr, dvr = O.attention_bwd(q, k, v, got, host(lse), do, prec)
+    dqkv = torch.full((M, (H + 2 * Hkv) * hd), float("nan"), device=DEV)
+    ws = torch.empty(mt.attn_bwd_ws_bytes(dtype, B, T, H, hd), device=DEV, dtype=torch.uint8)
+    mt.attn_bwd(dtype, qd, o, dev(do.reshape(M, H * hd)), lse, dqkv, ws, B, T, H, Hkv, hd)
+    dq, dk, dv = _split(host(dqkv).astype(np.float32), B, T, H, Hkv, hd)
+    # magnitude of the terms each gradient sums (dS = P (dP - D) cancels exactly at T = 1)
+    rms = lambda a: np.sqrt(np.mean(np.square(a)))
+    term_qk = rms(do) * rms(v) * rms(k) * math.sqrt(hd)
+    for g, r, term in ((dq, dqr, term_qk), (dk, dkr, term_qk), (dv, dvr, rms(do))):
+        if dtype:
+            bf16_close(g, r, floor=1e-2 * term)
+        else:
+            np.testing.assert_allclose(g, r, rtol=1e-4, atol=1e-4 * rms(r) + 1e-5 * term)
+
+
+@pytest.mark.parametrize("B,T,H,Hkv", [(1, 4096, 40, 8)])
+def test_attention_full_14b_shape_sampled_rows(B, T, H, Hkv):
+    hd, dtype = 128, mt.MT_BF16
+    qkv = _attn_inputs(B, T, H, Hkv, hd, dtype)
+    q, k, v = _split(qkv, B, T, H, Hkv, hd)
+    M = B * T
+    qd = dev(qkv, torch.bfloat16)
+    o = torch.empty(M, H * hd, device=DEV)
+    lse = torch.empty(B, H, T, device=DEV)
+    mt.attn_fwd(dtype, qd, o, None, lse, B, T, H, Hkv, hd)
+    got, gl = host(o).reshape(B, T, H, hd), host(lse)
+    for _ in range(48):
+        h, t = int(RNG.integers(H)), int(RNG.integers(T))
+        s = q[0, t, h] @ k[0, :t + 1, h // (H // Hkv)].T / math.sqrt(hd)
+        mx = s.max()
+        p = np.exp(s - mx)
+        ref = (O.bf16(p / p.sum()) @ v[0, :t + 1, h // (H // Hkv)])
+        assert abs(gl[0, h, t] - (mx + math.log(p.sum()))) < 1e-4
+        bf16_close(got[0, t, h], ref)
+
+
+# ------------------------------------------------------- SwiGLU / CE / cast ---
+
+@pytest.mark.parametrize("dtype", [mt.MT_FP32, mt.MT_BF16])
+def test_swiglu(dtype):
+    M, F = 77, 172
+    gu = (RNG.standard_normal((M, 2 * F)) * 4).astype(np.float32)
+    da = RNG.standard_normal((M, F)).astype(np.float32)
+    tdt = torch.bfloat16 if dtype else torch.float32
+    act = torch.empty(M, F, device=DEV, dtype=tdt)
+    dgu = torch.empty(M, 2 * F, device=DEV, dtype=tdt)
+    mt.swiglu_fwd(dtype, dev(gu), act, M, F)
+    mt.swiglu_bwd(dtype, dev(gu), dev(da), dgu, M, F)
+    g, u = gu[:, :F].astype(np.float64), gu[:, F:].astype(np.float64)
+    aref = O.swiglu_fwd(g, u)
+    dg, du = O.swiglu_bwd(g, u, da.astype(np.float64))
+    dref = np.concatenate([dg, du], axis=1)
+    rt = 2.0 ** -8 if dtype else 2e-6
+    assert np.all(np.abs(host(act) - aref) <= rt * np.abs(aref) + 1e-6)
+    assert np.all(np.abs(host(dgu) - dref) <= rt * np.abs(dref) + 1e-6)
+
+
+@pytest.mark.parametrize("dtype", [mt.MT_FP32, mt.MT_BF16])
+@pytest.mark.parametrize("rows,V", [(9, 256), (3, 152064), (5, 32000)])
+def test_cross_entropy(dtype, rows, V):
+    z = (RNG.standard_normal((rows, V)) * 3).astype(np.float32)
+    tgt = RNG.integers(0, V, rows).astype(np.int32)
+    tdt = torch.bfloat16 if dtype else torch.float32
+    zd = dev(z)
+    loss = torch.empty(rows, device=DEV)
+    dz = zd if not dtype else torch.empty(rows, V, device=DEV, dtype=tdt)   # fp32 in place
+    mt.xent(dtype, zd, torch.from_numpy(tgt).to(DEV), loss, dz, rows, V, 1.0 / 1000)
+    lref, dref = O.cross_entropy(z.astype(np.float64), tgt)
+    np.testing.assert_allclose(host(loss), lref, rtol=1e-5, atol=1e-5)
+    dref = dref * rows / 1000
+    rt = 2.0 ** -8 if dtype else 1e-5
+    assert np.all(np.abs(host(dz) - dref) <= rt * np.abs(dref) + 1e-12)
+
+
+def test_cross_entropy_in_place_repeated():
+    # dlogits overwrite the logits: every row's loss must still see its target logit
+    rows, V = 64, 256
+    for rep in range(20):
+        z = (RNG.standard_normal((rows, V)) * 3).astype(np.float32)
+        tgt = RNG.integers(0, V, rows).astype(np.int32)
+        zd = dev(z)
+        loss = torch.empty(rows, device=DEV)
+        mt.xent(mt.MT_FP32, zd, torch.from_numpy(tgt).to(DEV), loss, zd, rows, V, 1.0)
+        lref, dref = O.cross_entropy(z.astype(np.float64), tgt)
+        np.testing.assert_allclose(host(loss), lref, rtol=1e-5, atol=1e-5)
+        np.testing.assert_allclose(host(zd), dref * rows, rtol=1e-5, atol=1e-7)
+
+
+def test_cast_is_round_to_nearest_even():
+    x = np.concatenate([RNG.standard_normal(10000).astype(np.float32),
+                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8)], np.float32)])
+    y = torch.empty(x.size, device=DEV, dtype=torch.bfloat16)
+    mt.cast(mt.MT_BF16, dev(x), y, x.size)
+    np.testing.assert_array_equal(host(y), O.bf16(x))
