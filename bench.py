@@ -1,0 +1,248 @@
+"""Throughput of the layer-streamed training step on one MI355X.
+
+Workload (default): the 14B-shaped decoder -- 48 layers, d_model 5120, 40
+query / 8 kv heads (head_dim 128), SwiGLU FFN 13824, vocab 152064 -- batch
+1 x 4096 uniform-random token ids with next-token targets, weights N(0, 0.02)
+(norm gains 1) from seed 0, bf16 matrix-core compute with fp32 master weights
+and AdamW state in host memory, streamed through two device layer buffers.
+
+A step is one full mt_train_step: forward, head, recompute + backward, every
+gradient copied to the host and every AdamW update applied. Inputs (token ids)
+are generated before the timed region; the timed region is K steps bracketed
+by device synchronisation. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15        # dense bf16 matrix-core FLOP/s (MI355X)
+PEAK_FP32 = 157.3e12      # dense fp32 matrix-core FLOP/s
+PEAK_HBM = 8.0e12         # bytes/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_context(w, dtype, seed, flags, host_threads=0):
+    from host_memory_streamed_amd import mt, synth
+    cfg = mt.make_config(w.n_layers, w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn_dim, w.vocab,
+                         w.batch, w.seq, dtype=dtype, n_layer_buffers=2, host_threads=host_threads,
+                         flags=flags)
+    t0 = time.perf_counter()
+    ctx = mt.Context(cfg)
+    log(f"context created in {time.perf_counter() - t0:.1f}s; device bytes {ctx.device_bytes() / 1e9:.2f} GB")
+    t0 = time.perf_counter()
+    biggest = max(int(np.prod(s)) for _, s in ctx.table)
+    buf = np.empty(biggest, dtype=np.float32)
+    for i, (name, shape) in enumerate(ctx.table):
+        n = int(np.prod(shape))
+        view = buf[:n]
+        synth.init_tensor(seed, i, (n,), name.endswith("norm"), out=view)
+        ctx.set_param(i, view)
+    log(f"parameters drawn and loaded in {time.perf_counter() - t0:.1f}s")
+    return ctx
+
+
+def cpu_baseline(w, budget_tokens=512):
+    """The CPU oracle (plain float64 NumPy) timed on a bounded sample of the
+    same workload: one decoder layer of the real shape and the real head on
+    1 x budget_tokens tokens, and AdamW on a 16M-element sample; composed into
+    a full-depth step time and reported as tokens/s of that sample."""
+    import oracle as O
+    from oracle.decoder import _Prec
+    from host_memory_streamed_amd import synth
+
+    cfg = O.Config(1, w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn_dim, w.vocab)
+    table = O.tensor_table(cfg)
+    params = [synth.init_tensor(0, i, s, g) for i, (_, s, g) in enumerate(table)]
+    P = [p.astype(np.float64) for p in params]
+    B, T = 1, budget_tokens
+    tokens, targets = synth.token_batch(0, B, T, w.vocab)
+    prec = _Prec("bf16")
+    rope = O.rope_tables(T, cfg.head_dim, cfg.rope_base)
+    W = {n: P[1 + i] for i, n in enumerate(O.LAYER_TENSORS)}
+    x = P[0][tokens.reshape(-1)]
+    t0 = time.perf_counter()
+    y, cache = O.layer_fwd(x, W, cfg, prec, rope, B, T)
+    t_fwd = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    _, g, _, _ = O.head_fwd_bwd(y, P[-2], P[-1], targets.reshape(-1), cfg, prec)
+    t_head = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.layer_bwd(g, cache, W, cfg, prec, rope, B, T)
+    t_bwd = time.perf_counter() - t0
+    n = 1 << 24
+    rng = np.random.default_rng(0)
+    pa, ga = rng.standard_normal(n), rng.standard_normal(n)
+    t0 = time.perf_counter()
+    O.adamw(pa, ga, np.zeros(n), np.zeros(n), 1, cfg)
+    t_adam = (time.perf_counter() - t0) / n
+    layer_params = sum(int(np.prod(s)) for _, s, _ in table[1:10])
+    total_params = w.n_layers * layer_params + 2 * w.vocab * w.d_model + w.d_model
+    step = w.n_layers * (t_fwd + t_bwd) + t_head + total_params * t_adam
+    try:
+        import threadpoolctl
+        cores = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or os.cpu_count()
+    except Exception:
+        cores = os.cpu_count()
+    return {
+        "value": round(B * T / step, 4),
+        "unit": "tokens/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"float64 NumPy oracle, bf16 cast emulation, on 1x{T} tokens of the "
+                   f"{w.name} shape: one decoder layer forward ({t_fwd:.2f}s) and backward "
+                   f"({t_bwd:.2f}s), head forward+backward ({t_head:.2f}s), AdamW "
+                   f"{t_adam * 1e9:.2f} ns/param on 16M params; composed as "
+                   f"{w.n_layers} x (fwd + bwd) + head + AdamW over {total_params / 1e9:.2f}B params "
+                   f"= {step:.1f}s per {T}-token step"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="14b", help="tiny | 1.3b | 14b | 120b (120b: --layers)")
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count")
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp32"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace", default=None, help="write the last step's schedule as Chrome JSON")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the streamed step on one GPU: this build has no multi-GPU path "
+              "(no collectives). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from host_memory_streamed_amd import mt, synth
+
+    if not os.path.exists(mt.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    w = mt.WORKLOADS[args.workload]
+    if args.layers:
+        w = mt.Workload(**{**w.__dict__, "n_layers": args.layers})
+    dtype = mt.MT_BF16 if args.dtype == "bf16" else mt.MT_FP32
+    flags = mt.MT_KERNEL_TIMING | mt.MT_TRACE
+    ctx = build_context(w, dtype, args.seed, flags)
+    tokens, targets = synth.token_batch(args.seed, w.batch, w.seq, w.vocab)
+    M = w.batch * w.seq
+
+    losses = []
+    for i in range(args.warmup):
+        t0 = time.perf_counter()
+        losses.append(ctx.train_step(tokens, targets))
+        log(f"warmup step {i}: {time.perf_counter() - t0:.3f}s loss {losses[-1]:.4f}")
+    torch.cuda.synchronize()
+    stats = []
+    kstats = {}
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        losses.append(ctx.train_step(tokens, targets))
+        s = ctx.stats()
+        stats.append(s)
+        for k in ctx.kernel_stats():
+            acc = kstats.setdefault(k["name"], {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+            for f in ("launches", "ms", "flops", "bytes"):
+                acc[f] += k[f]
+        log(f"step {i}: {s['step_ms']:.1f} ms loss {losses[-1]:.4f} fwd {s['forward_ms']:.0f} ms "
+            f"tail {s['tail_ms']:.0f} ms adamw(sum) {s['adamw_ms']:.0f} ms")
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    if args.trace:
+        ctx.trace_dump(args.trace)
+    sched = ctx.schedule()
+
+    ms = elapsed / args.steps * 1e3
+    tok_s = M * args.steps / elapsed
+    mean = lambda key: float(np.mean([s[key] for s in stats]))
+    peak = PEAK_BF16 if dtype == mt.MT_BF16 else PEAK_FP32
+    mfu = mean("model_flops") / (ms * 1e-3) / peak
+    h2d, d2h = mean("h2d_bytes"), mean("d2h_bytes")
+    # copy engine rates over the last step's copies
+    loads = [e for e in sched if e["phase"] == "load" and e["stream"] == 0]
+    grads = [e for e in sched if e["phase"] == "grad" and e["stream"] == 2]
+    h2d_busy = sum(e["t1"] - e["t0"] for e in loads) * 1e-3
+    d2h_busy = sum(e["t1"] - e["t0"] for e in grads) * 1e-3
+    unit_bytes_h2d = stats[-1]["h2d_bytes"] - M * (w.d_model + 1) * 4
+    unit_bytes_d2h = stats[-1]["d2h_bytes"] - M * (w.d_model + 1) * 4
+
+    # dominant kernel class by time, its algorithmic rate against its peak
+    dom_name, dom = max(kstats.items(), key=lambda kv: kv[1]["ms"])
+    gemm = dom_name.startswith("gemm") or dom_name.startswith("attn")
+    achieved = dom["flops"] / (dom["ms"] * 1e-3) if gemm else dom["bytes"] / (dom["ms"] * 1e-3)
+    kpeak = peak if gemm else PEAK_HBM
+    gpu_ms = sum(v["ms"] for v in kstats.values()) / args.steps
+    out = {
+        "metric": "training tokens/sec, MFU and host-link GB/s for 14B-shaped streamed step",
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dtype == mt.MT_BF16 else "fp32",
+        "data": "synthetic",
+        "config": {"workload": w.name + "-shaped decoder, streamed through 2 layer buffers",
+                   "n_layers": w.n_layers, "d_model": w.d_model, "n_heads": w.n_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ffn_dim": w.ffn_dim,
+                   "vocab": w.vocab, "global_batch": w.batch, "seq_len": w.seq,
+                   "master": "fp32 p/m/v in host memory", "parallelism": "none (1 GPU)"},
+        "mfu": round(mfu, 4),
+        "host_link": {
+            "h2d_GBps_step": round(h2d / (ms * 1e-3) / 1e9, 2),
+            "d2h_GBps_step": round(d2h / (ms * 1e-3) / 1e9, 2),
+            "h2d_GBps_copies": round(unit_bytes_h2d / h2d_busy / 1e9, 2) if h2d_busy > 0 else None,
+            "d2h_GBps_copies": round(unit_bytes_d2h / d2h_busy / 1e9, 2) if d2h_busy > 0 else None,
+            "h2d_bytes_step": h2d, "d2h_bytes_step": d2h,
+        },
+        "host_adamw": {"thread_ms_step": round(mean("adamw_ms"), 1),
+                       "bytes_step": mean("adamw_bytes"),
+                       "tail_ms": round(mean("tail_ms"), 1)},
+        "gpu_kernel_ms_step": round(gpu_ms, 1),
+        "loss_first": round(losses[0], 4),
+        "roofline": {
+            "kernel": dom_name,
+            "bound": "mfma" if gemm else "hbm",
+            "achieved": round(achieved / (1e12 if gemm else 1e9), 2),
+            "peak": round(kpeak / (1e12 if gemm else 1e9), 1),
+            "unit": "TFLOP/s" if gemm else "GB/s",
+            "frac": round(achieved / kpeak, 4),
+            "traffic": None,
+            "launches_per_step": dom["launches"] // args.steps,
+            "avg_launch_us": round(dom["ms"] / dom["launches"] * 1e3, 2),
+        },
+        "kernels": {k: {"ms_step": round(v["ms"] / args.steps, 2), "launches_step": v["launches"] // args.steps,
+                        "TFLOPs": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 1) if v["flops"] else None,
+                        "GBps": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)}
+                    for k, v in sorted(kstats.items(), key=lambda kv: -kv[1]["ms"]) if v["launches"]},
+        "cpu_baseline": None,
+    }
+    ctx.close()
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        out["cpu_baseline"] = cpu_baseline(w)
+        log(f"cpu baseline in {time.perf_counter() - t0:.1f}s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
