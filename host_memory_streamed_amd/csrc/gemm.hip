@@ -222,6 +222,237 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int6
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile kernel: 256x256 output tile per 512-thread workgroup, 8 wave64 in
+// 2 (M) x 4 (N), each wave owning 128x64 (4x2 MFMA 32x32 tiles); two waves per
+// SIMD hide each other's latencies. The K loop moves 128 bytes per row per
+// step (64 bf16 / 32 fp32) through two 64 KB LDS stages (one workgroup per
+// CU). Global loads for the next step go to registers before the current
+// step's products; interior tiles take a branch-free load path, edge tiles a
+// guarded one. LDS rows are 128 bytes with the 16-byte chunks permuted by
+// S(row, c) = c ^ (row & 7) ^ ((row >> 3) & 7): fragment reads (8 consecutive
+// rows, one chunk), row stores (one row, 8 chunks) and the transposed 4-byte
+// stores of M/N-contiguous operands all spread over the banks.
+// ---------------------------------------------------------------------------
+constexpr int BIG = 256;
+constexpr int BIG_THREADS = 512;
+constexpr int BIG_ROW = 128;                      // bytes per LDS row
+constexpr int BIG_TILE_BYTES = BIG * BIG_ROW;     // one operand tile
+constexpr int BIG_STAGE = 2 * BIG_TILE_BYTES;     // A and B
+
+__device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7) ^ ((row >> 3) & 7); }
+
+template <typename T, bool KCONTIG>
+struct BigLoader {
+  static constexpr int VE = 16 / sizeof(T);       // elements per chunk
+  static constexpr int BK = BIG_ROW / sizeof(T);  // k per stage
+  static constexpr int NKC = BIG * 8 / BIG_THREADS;                       // K-contiguous chunks per thread
+  static constexpr int NMN = (BK / 2) * (BIG / VE) / BIG_THREADS;        // transposed tasks per thread
+  static constexpr int NV = KCONTIG ? NKC : 2 * NMN;
+  Vec16 v[NV];
+
+  template <bool CHECK>
+  __device__ __forceinline__ void load(const T* __restrict__ base, int64_t ld, int r0, int rows, int k0,
+                                       int K, int tid) {
+    if (KCONTIG) {
+#pragma unroll
+      for (int j = 0; j < NKC; ++j) {
+        const int u = tid + BIG_THREADS * j;
+        const int r = u >> 3, c = u & 7;
+        const int gr = r0 + r, kk = k0 + c * VE;
+        const T* p = base + (int64_t)gr * ld + kk;
+        if (!CHECK || (gr < rows && kk + VE <= K)) {
+          v[j] = *reinterpret_cast<const Vec16*>(p);
+        } else {
+          T tmp[VE];
+#pragma unroll
+          for (int e = 0; e < VE; ++e) tmp[e] = (gr < rows && kk + e < K) ? p[e] : T(0);
+          __builtin_memcpy(&v[j], tmp, 16);
+        }
+      }
+    } else {
+      constexpr int MNC = BIG / VE;
+#pragma unroll
+      for (int j = 0; j < NMN; ++j) {
+        const int u = tid + BIG_THREADS * j;
+        const int mn_lo = u & 7, kp_lo = (u >> 3) & 7, rest = u >> 6;
+        const int mnc = (rest % (MNC / 8)) * 8 + mn_lo, kp = (rest / (MNC / 8)) * 8 + kp_lo;
+        const int gr = r0 + mnc * VE;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int kk = k0 + 2 * kp + h;
+          const T* p = base + (int64_t)kk * ld + gr;
+          if (!CHECK || (kk < K && gr + VE <= rows)) {
+            v[2 * j + h] = *reinterpret_cast<const Vec16*>(p);
+          } else {
+            T tmp[VE];
+#pragma unroll
+            for (int e = 0; e < VE; ++e) tmp[e] = (kk < K && gr + e < rows) ? p[e] : T(0);
+            __builtin_memcpy(&v[2 * j + h], tmp, 16);
+          }
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+    if (KCONTIG) {
+#pragma unroll
+      for (int j = 0; j < NKC; ++j) {
+        const int u = tid + BIG_THREADS * j;
+        const int r = u >> 3, c = u & 7;
+        *reinterpret_cast<Vec16*>(lds + r * BIG_ROW + (swz(r, c) << 4)) = v[j];
+      }
+    } else {
+      constexpr int MNC = BIG / VE;
+#pragma unroll
+      for (int j = 0; j < NMN; ++j) {
+        const int u = tid + BIG_THREADS * j;
+        const int mn_lo = u & 7, kp_lo = (u >> 3) & 7, rest = u >> 6;
+        const int mnc = (rest % (MNC / 8)) * 8 + mn_lo, kp = (rest / (MNC / 8)) * 8 + kp_lo;
+        const int kb = 2 * kp * (int)sizeof(T);     // byte offset of the k pair in the row
+        const int c = kb >> 4, off = kb & 15;
+        const T* a = reinterpret_cast<const T*>(&v[2 * j]);
+        const T* b = reinterpret_cast<const T*>(&v[2 * j + 1]);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          const int r = mnc * VE + e;
+          T pair[2] = {a[e], b[e]};
+          char* dst = lds + r * BIG_ROW + (swz(r, c) << 4) + off;
+          if (sizeof(T) == 2) {
+            uint32_t w;
+            __builtin_memcpy(&w, pair, 4);
+            *reinterpret_cast<uint32_t*>(dst) = w;
+          } else {
+            uint2 w;
+            __builtin_memcpy(&w, pair, 8);
+            *reinterpret_cast<uint2*>(dst) = w;
+          }
+        }
+      }
+    }
+  }
+};
+
+template <typename T, int LAYOUT>
+__global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __restrict__ A, int64_t lda,
+                                                                  const T* __restrict__ B, int64_t ldb,
+                                                                  float* C, int64_t ldc, const float* R,
+                                                                  int64_t ldr, int M, int N, int K,
+                                                                  int tiles_m, int tiles_n) {
+  constexpr bool A_KC = (LAYOUT != MT_GEMM_TN);
+  constexpr bool B_KC = (LAYOUT == MT_GEMM_NT);
+  typedef Mfma32<T> MF;
+  constexpr int BK = BIG_ROW / sizeof(T);
+  constexpr int NSUB = 16 / (MF::KL * (int)sizeof(T));   // instructions per 16-byte chunk
+
+  extern __shared__ __attribute__((aligned(16))) char smem_big[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;       // 2 x 4 waves
+  const int g = lane >> 5, l32 = lane & 31;
+
+  const int nwg = tiles_m * tiles_n;
+  const int pid = remap_tile(blockIdx.x, nwg);
+  const int group = 8 * tiles_n;
+  const int first_m = (pid / group) * 8;
+  const int gsize = min(tiles_m - first_m, 8);
+  const int tm = first_m + (pid % group) % gsize;
+  const int tn = (pid % group) / gsize;
+  const int m0 = tm * BIG, n0 = tn * BIG;
+  const bool full = (m0 + BIG <= M) && (n0 + BIG <= N);
+
+  // LDS read offsets of this lane's rows (chunk added per k-step)
+  int a_base[4], a_x[4], b_base[2], b_x[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wm * 128 + i * 32 + l32;
+    a_base[i] = r * BIG_ROW;
+    a_x[i] = (r & 7) ^ ((r >> 3) & 7);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = wn * 64 + j * 32 + l32;
+    b_base[j] = BIG_TILE_BYTES + r * BIG_ROW;
+    b_x[j] = (r & 7) ^ ((r >> 3) & 7);
+  }
+
+  BigLoader<T, A_KC> la;
+  BigLoader<T, B_KC> lb;
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
+
+  const int nk = (K + BK - 1) / BK;
+  auto load_stage = [&](int k0) {
+    if (full && k0 + BK <= K) {
+      la.template load<false>(A, lda, m0, M, k0, K, tid);
+      lb.template load<false>(B, ldb, n0, N, k0, K, tid);
+    } else {
+      la.template load<true>(A, lda, m0, M, k0, K, tid);
+      lb.template load<true>(B, ldb, n0, N, k0, K, tid);
+    }
+  };
+  load_stage(0);
+  la.store(smem_big, tid);
+  lb.store(smem_big + BIG_TILE_BYTES, tid);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* cur = smem_big + (kt & 1) * BIG_STAGE;
+    const bool more = kt + 1 < nk;
+    if (more) load_stage((kt + 1) * BK);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int c = 2 * s + g;
+      Vec16 av[4], bv[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const Vec16*>(cur + a_base[i] + ((c ^ a_x[i]) << 4));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bv[j] = *reinterpret_cast<const Vec16*>(cur + b_base[j] + ((c ^ b_x[j]) << 4));
+#pragma unroll
+      for (int q = 0; q < NSUB; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          typename MF::frag fa;
+          __builtin_memcpy(&fa, reinterpret_cast<const char*>(&av[i]) + q * sizeof(fa), sizeof(fa));
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            typename MF::frag fb;
+            __builtin_memcpy(&fb, reinterpret_cast<const char*>(&bv[j]) + q * sizeof(fb), sizeof(fb));
+            acc[i][j] = MF::mma(fa, fb, acc[i][j]);
+          }
+        }
+    }
+    if (more) {
+      char* nxt = smem_big + ((kt + 1) & 1) * BIG_STAGE;
+      la.store(nxt, tid);
+      lb.store(nxt + BIG_TILE_BYTES, tid);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn * 64 + j * 32 + l32;
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+        if (row < M) {
+          float val = acc[i][j][r];
+          if (R) val += R[(int64_t)row * ldr + col];
+          C[(int64_t)row * ldc + col] = val;
+        }
+      }
+    }
+}
+
 // C = R (or 0) for K = 0
 __global__ void fill_kernel(float* C, int64_t ldc, const float* R, int64_t ldr, int M, int N) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -243,12 +474,57 @@ hipError_t launch(const void* A, int64_t lda, const void* B, int64_t ldb, float*
   return hipGetLastError();
 }
 
+template <typename T, int LAYOUT>
+hipError_t launch_big(const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc,
+                      const float* R, int64_t ldr, int M, int N, int K, hipStream_t s) {
+  const int tm = (M + BIG - 1) / BIG, tn = (N + BIG - 1) / BIG;
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)gemm_big_kernel<T, LAYOUT>, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * BIG_STAGE);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((gemm_big_kernel<T, LAYOUT>), dim3(tm * tn), dim3(BIG_THREADS), 2 * BIG_STAGE, s,
+                     (const T*)A, lda, (const T*)B, ldb, C, ldc, R, ldr, M, N, K, tm, tn);
+  return hipGetLastError();
+}
+
+bool big_ok(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N) {
+  const int64_t es = dtype ? 2 : 4;
+  auto al = [&](const void* p, int64_t ld) { return ((uintptr_t)p % 16 == 0) && ((ld * es) % 16 == 0); };
+  return al(A, lda) && al(B, ldb) && M >= 1 && N >= 1;
+}
+
 }  // namespace
 
 hipError_t gemm(int dtype, int layout, const void* A, int64_t lda, const void* B, int64_t ldb,
                 float* C, int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N,
                 int64_t K, hipStream_t s) {
+  return gemm_variant(dtype, layout, A, lda, B, ldb, C, ldc, R, ldr, M, N, K, 0, s);
+}
+
+hipError_t gemm_variant(int dtype, int layout, const void* A, int64_t lda, const void* B, int64_t ldb,
+                        float* C, int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N,
+                        int64_t K, int variant, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (K > 0) {
+    // 256x256 tiles when operands are 16-byte aligned and the grid still has
+    // at least about half a wave of workgroups per CU; else 128x128 tiles
+    const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    const bool use_big = variant == 2 || (variant == 0 && big_tiles >= 128);
+    if (use_big && big_ok(dtype, A, lda, B, ldb, M, N)) {
+      const int m = (int)M, n = (int)N, k = (int)K;
+      if (dtype == 1) {
+        switch (layout) {
+          case MT_GEMM_NT: return launch_big<bf16, MT_GEMM_NT>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
+          case MT_GEMM_NN: return launch_big<bf16, MT_GEMM_NN>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
+          default: return launch_big<bf16, MT_GEMM_TN>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
+        }
+      }
+      switch (layout) {
+        case MT_GEMM_NT: return launch_big<float, MT_GEMM_NT>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
+        case MT_GEMM_NN: return launch_big<float, MT_GEMM_NN>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
+        default: return launch_big<float, MT_GEMM_TN>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
+      }
+    }
+  }
   if (K == 0) {
     const int64_t n = M * N;
     hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, C, ldc, R,

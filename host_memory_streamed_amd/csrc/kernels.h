@@ -13,6 +13,10 @@ namespace mt {
 hipError_t gemm(int dtype, int layout, const void* A, int64_t lda, const void* B, int64_t ldb,
                 float* C, int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N,
                 int64_t K, hipStream_t s);
+// variant: 0 = choose by shape, 1 = 128x128 tiles, 2 = 256x256 tiles (when aligned)
+hipError_t gemm_variant(int dtype, int layout, const void* A, int64_t lda, const void* B, int64_t ldb,
+                        float* C, int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N,
+                        int64_t K, int variant, hipStream_t s);
 
 bool attn_supported(int dtype, int hd);
 int64_t attn_ws_d_bytes(int B, int T, int H);

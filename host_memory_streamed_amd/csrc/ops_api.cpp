@@ -18,6 +18,13 @@ extern "C" {
 int mt_op_gemm(int32_t dtype, int32_t layout, const void* A, int64_t lda, const void* B, int64_t ldb,
                float* C, int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N, int64_t K,
                void* stream) {
+  return mt_op_gemm_variant(dtype, layout, A, lda, B, ldb, C, ldc, R, ldr, M, N, K, 0, stream);
+}
+
+int mt_op_gemm_variant(int32_t dtype, int32_t layout, const void* A, int64_t lda, const void* B,
+                       int64_t ldb, float* C, int64_t ldc, const float* R, int64_t ldr, int64_t M,
+                       int64_t N, int64_t K, int32_t variant, void* stream) {
+  if (variant < 0 || variant > 2) return MT_EINVAL;
   if (!dtype_ok(dtype) || layout < MT_GEMM_NT || layout > MT_GEMM_TN) return MT_EINVAL;
   if (M < 0 || N < 0 || K < 0 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return MT_EINVAL;
   if (M == 0 || N == 0) return MT_OK;
@@ -26,7 +33,7 @@ int mt_op_gemm(int32_t dtype, int32_t layout, const void* A, int64_t lda, const 
   const int64_t a_cols = layout == MT_GEMM_TN ? M : K;
   const int64_t b_cols = layout == MT_GEMM_NT ? K : N;
   if (lda < a_cols || ldb < b_cols || ldc < N || (R && ldr < N)) return MT_EINVAL;
-  return hip_rc(gemm(dtype, layout, A, lda, B, ldb, C, ldc, R, ldr, M, N, K, st(stream)));
+  return hip_rc(gemm_variant(dtype, layout, A, lda, B, ldb, C, ldc, R, ldr, M, N, K, variant, st(stream)));
 }
 
 int mt_op_rmsnorm_fwd(int32_t out_dtype, const float* x, const float* w, void* y, float* rstd, int64_t rows,

@@ -34,6 +34,13 @@ int mt_op_gemm(int32_t dtype, int32_t layout, const void* A, int64_t lda, const 
                int64_t ldb, float* C, int64_t ldc, const float* R, int64_t ldr, int64_t M,
                int64_t N, int64_t K, void* stream);
 
+/* mt_op_gemm with the tile size chosen by the caller: variant 0 = by shape
+ * (as mt_op_gemm), 1 = 128x128 tiles, 2 = 256x256 tiles (used when A and B
+ * rows are 16-byte aligned; otherwise 128x128). For tests and tuning. */
+int mt_op_gemm_variant(int32_t dtype, int32_t layout, const void* A, int64_t lda, const void* B,
+                       int64_t ldb, float* C, int64_t ldc, const float* R, int64_t ldr, int64_t M,
+                       int64_t N, int64_t K, int32_t variant, void* stream);
+
 /* RMSNorm forward over rows of x [rows, d] (fp32): y = x r w with
  * r = (mean(x^2) + eps)^(-1/2), written as out_dtype; rstd[rows] = r. */
 int mt_op_rmsnorm_fwd(int32_t out_dtype, const float* x, const float* w, void* y, float* rstd,

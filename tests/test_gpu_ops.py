@@ -49,7 +49,7 @@ def fp32_close(gpu, ref, absterm, ulps=64):
 
 # -------------------------------------------------------------------- GEMM ---
 
-def _gemm_case(dtype, layout, M, N, K, residual=False, sample=None):
+def _gemm_case(dtype, layout, M, N, K, residual=False, sample=None, variant=0):
     # logical operands: X [M, K], Y [K, N]; stored per layout
     X = RNG.standard_normal((M, K)).astype(np.float32)
     Y = RNG.standard_normal((K, N)).astype(np.float32)
@@ -65,7 +65,7 @@ def _gemm_case(dtype, layout, M, N, K, residual=False, sample=None):
     R = RNG.standard_normal((M, N)).astype(np.float32) if residual else None
     C = torch.full((M, N), float("nan"), device=DEV)
     Rd = dev(R) if residual else None
-    mt.gemm(dtype, layout, A, lda, B, ldb, C, N, M, N, K, R=Rd, ldr=N)
+    mt.gemm(dtype, layout, A, lda, B, ldb, C, N, M, N, K, R=Rd, ldr=N, variant=variant)
     got = host(C)
     X64, Y64 = X.astype(np.float64), Y.astype(np.float64)
     if sample is None:
@@ -86,6 +86,14 @@ def _gemm_case(dtype, layout, M, N, K, residual=False, sample=None):
                                    (64, 172, 300)])
 def test_gemm_small_and_ragged(dtype, layout, M, N, K):
     _gemm_case(dtype, layout, M, N, K, residual=(M % 2 == 0))
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+@pytest.mark.parametrize("dtype", [mt.MT_FP32, mt.MT_BF16])
+@pytest.mark.parametrize("layout", [mt.MT_GEMM_NT, mt.MT_GEMM_NN, mt.MT_GEMM_TN])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (512, 768, 192), (300, 520, 72), (1, 3, 5), (260, 256, 1000)])
+def test_gemm_tile_variants(variant, dtype, layout, M, N, K):
+    _gemm_case(dtype, layout, M, N, K, residual=(K % 2 == 0), variant=variant)
 
 
 @pytest.mark.parametrize("layout,M,N,K", [(mt.MT_GEMM_NT, 4096, 7168, 5120), (mt.MT_GEMM_NN, 4096, 5120, 13824),
