@@ -17,8 +17,10 @@
 // A row fragment puts hd range [g*hd/4, (g+1)*hd/4) in lane group g = lane/16.
 // When an accumulator (rows c = t*16 + g*4 + r) feeds the next product as its
 // B operand, the contraction runs over those rows in the same slot order on
-// both operands, so the A operand reads 4 consecutive entries per 16-row
-// sub-tile from a transposed LDS tile.
+// both operands, so the A operand needs 4 consecutive contraction entries per
+// 16-row sub-tile: bf16 gets them from the row-major tile with the LDS
+// transpose read (ds_read_b64_tr_b16); fp32 reads an explicitly transposed
+// LDS copy.
 //
 // Online softmax keeps a running max and sum per query in the log2 domain.
 // In bf16 mode P (for P.V and for dV) and dS are rounded to bf16 before their
@@ -44,7 +46,10 @@ struct Cfg {
   static constexpr int VE = 16 / sizeof(T);      // elements per 16-byte vector
   static constexpr int PAD = VE;                 // LDS row padding (elements)
   static constexpr int BKV = sizeof(T) == 2 ? 64 : 32;  // keys per tile (forward, dQ)
-  static constexpr int BQ = sizeof(T) == 2 ? 32 : 16;   // queries per tile (dK/dV)
+  static constexpr int BQ = sizeof(T) == 2 ? 64 : 16;   // queries per tile (dK/dV)
+  // bf16 reads transposed operands straight from the row-major tiles with the
+  // LDS transpose read; fp32 keeps explicitly transposed copies
+  static constexpr bool TR = sizeof(T) == 2;
 };
 
 // Copy n_rows rows of HD elements (global row stride ld, rows >= valid are
@@ -138,6 +143,28 @@ struct AccFrag<bf16, NT16> {
         f[s][4 + r] = to_bf16(p[2 * s + 1][r]);
       }
   }
+  // acc += A . B where A[row][c] = tile[c][col0 + row] of a row-major LDS tile
+  // (pitch elements per row): the LDS transpose read gives lane l (group
+  // g = l/16, i = l%16) rows row0 + 4g + e, e = 0..3, of column col0 + i when
+  // lane 4e + q of the group supplies the address of row row0 + 4g + e,
+  // column col0 + 4q. Two reads per slice cover contraction rows
+  // 32s + 4g + r and 32s + 16 + 4g + r, the accumulator's slot order.
+  __device__ __forceinline__ floatx4 apply_tr(const bf16* tile, int pitch, int col0, int lane,
+                                              floatx4 acc) const {
+    const int g = lane >> 4, j = lane & 15;
+    const bf16* base = tile + (4 * g + (j >> 2)) * pitch + col0 + 4 * (j & 3);
+#pragma unroll
+    for (int s = 0; s < NT16 / 2; ++s) {
+      typedef __attribute__((address_space(3))) bf16x4 lds4;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(base + (32 * s) * pitch));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(base + (32 * s + 16) * pitch));
+      bf16x8 a;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) { a[r] = lo[r]; a[4 + r] = hi[r]; }
+      acc = Mfma16<bf16>::mma(a, f[s], acc);
+    }
+    return acc;
+  }
   // acc += A . B where A's row (this lane's) is arow[c] over the contraction c.
   __device__ __forceinline__ floatx4 apply(const bf16* arow, int g, floatx4 acc) const {
 #pragma unroll
@@ -159,6 +186,9 @@ struct AccFrag<float, NT16> {
 #pragma unroll
     for (int t = 0; t < NT16; ++t) f[t] = p[t];
   }
+  __device__ __forceinline__ floatx4 apply_tr(const float*, int, int, int, floatx4 acc) const {
+    return acc;   // fp32 reads explicitly transposed tiles (apply)
+  }
   __device__ __forceinline__ floatx4 apply(const float* arow, int g, floatx4 acc) const {
 #pragma unroll
     for (int t = 0; t < NT16; ++t) {
@@ -179,7 +209,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
   typedef Cfg<T, HD> C;
   constexpr int BKV = C::BKV, NKT = BKV / 16, KP = HD + C::PAD, VP = BKV + C::PAD;
   __shared__ __attribute__((aligned(16))) T Ks[BKV * KP];
-  __shared__ __attribute__((aligned(16))) T Vt[HD * VP];
+  __shared__ __attribute__((aligned(16))) T Vt[C::TR ? BKV * KP : HD * VP];   // bf16: V row-major
 
   const int qb = n_qblk - 1 - (int)blockIdx.x;   // longest rows first
   const int h = blockIdx.y, b = blockIdx.z;
@@ -207,7 +237,10 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
     const int k0 = kt * BKV;
     __syncthreads();
     load_rows<T, HD>(Ks, Kg, ld, k0, BKV, Tn, tid);
-    load_rows_t<T, HD>(Vt, Vg, ld, k0, BKV, Tn, tid);
+    if constexpr (C::TR)
+      load_rows<T, HD>(Vt, Vg, ld, k0, BKV, Tn, tid);
+    else
+      load_rows_t<T, HD>(Vt, Vg, ld, k0, BKV, Tn, tid);
     __syncthreads();
 
     floatx4 s[NKT];
@@ -245,7 +278,10 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
 #pragma unroll
     for (int ht = 0; ht < C::HT; ++ht) {
       oacc[ht] *= alpha;
-      oacc[ht] = pf.apply(Vt + (ht * 16 + l16) * VP, g, oacc[ht]);
+      if constexpr (C::TR)
+        oacc[ht] = pf.apply_tr(Vt, KP, ht * 16, lane, oacc[ht]);
+      else
+        oacc[ht] = pf.apply(Vt + (ht * 16 + l16) * VP, g, oacc[ht]);
     }
   }
 
@@ -306,9 +342,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(const T* __restrict__
   typedef Cfg<T, HD> C;
   constexpr int BQ = C::BQ, NQT = BQ / 16, RP = HD + C::PAD, TP = BQ + C::PAD;
   __shared__ __attribute__((aligned(16))) T Qs[BQ * RP];
-  __shared__ __attribute__((aligned(16))) T Qt[HD * TP];
+  __shared__ __attribute__((aligned(16))) T Qt[C::TR ? 8 : HD * TP];   // fp32 only
   __shared__ __attribute__((aligned(16))) T Ds[BQ * RP];
-  __shared__ __attribute__((aligned(16))) T Dt[HD * TP];
+  __shared__ __attribute__((aligned(16))) T Dt[C::TR ? 8 : HD * TP];   // fp32 only
   __shared__ float lse_s[BQ], D_s[BQ];
 
   const int kb = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -338,9 +374,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(const T* __restrict__
       const int q0 = qt * BQ;
       __syncthreads();
       load_rows<T, HD>(Qs, base + h * HD, ld, q0, BQ, Tn, tid);
-      load_rows_t<T, HD>(Qt, base + h * HD, ld, q0, BQ, Tn, tid);
       load_rows<T, HD>(Ds, dbase + h * HD, ldo, q0, BQ, Tn, tid);
-      load_rows_t<T, HD>(Dt, dbase + h * HD, ldo, q0, BQ, Tn, tid);
+      if constexpr (!C::TR) {
+        load_rows_t<T, HD>(Qt, base + h * HD, ld, q0, BQ, Tn, tid);
+        load_rows_t<T, HD>(Dt, dbase + h * HD, ldo, q0, BQ, Tn, tid);
+      }
       if (tid < BQ) {
         const bool ok = q0 + tid < Tn;
         lse_s[tid] = ok ? lse_h[q0 + tid] * LOG2E : 0.f;
@@ -367,8 +405,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(const T* __restrict__
       sf.set(ds);
 #pragma unroll
       for (int ht = 0; ht < C::HT; ++ht) {
-        dv[ht] = pf.apply(Dt + (ht * 16 + l16) * TP, g, dv[ht]);
-        dk[ht] = sf.apply(Qt + (ht * 16 + l16) * TP, g, dk[ht]);
+        if constexpr (C::TR) {
+          dv[ht] = pf.apply_tr(Ds, RP, ht * 16, lane, dv[ht]);
+          dk[ht] = sf.apply_tr(Qs, RP, ht * 16, lane, dk[ht]);
+        } else {
+          dv[ht] = pf.apply(Dt + (ht * 16 + l16) * TP, g, dv[ht]);
+          dk[ht] = sf.apply(Qt + (ht * 16 + l16) * TP, g, dk[ht]);
+        }
       }
     }
   }
@@ -396,7 +439,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const T* __restrict__ 
   typedef Cfg<T, HD> C;
   constexpr int BKV = C::BKV, NKT = BKV / 16, KP = HD + C::PAD, TP = BKV + C::PAD;
   __shared__ __attribute__((aligned(16))) T Ks[BKV * KP];
-  __shared__ __attribute__((aligned(16))) T Kt[HD * TP];
+  __shared__ __attribute__((aligned(16))) T Kt[C::TR ? 8 : HD * TP];   // fp32 only
   __shared__ __attribute__((aligned(16))) T Vs[BKV * KP];
 
   const int qb = n_qblk - 1 - (int)blockIdx.x;
@@ -427,7 +470,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const T* __restrict__ 
     const int k0 = kt * BKV;
     __syncthreads();
     load_rows<T, HD>(Ks, Kg, ld, k0, BKV, Tn, tid);
-    load_rows_t<T, HD>(Kt, Kg, ld, k0, BKV, Tn, tid);
+    if constexpr (!C::TR) load_rows_t<T, HD>(Kt, Kg, ld, k0, BKV, Tn, tid);
     load_rows<T, HD>(Vs, Vg, ld, k0, BKV, Tn, tid);
     __syncthreads();
     floatx4 ds[NKT];
@@ -445,7 +488,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const T* __restrict__ 
     AccFrag<T, NKT> sf;
     sf.set(ds);
 #pragma unroll
-    for (int ht = 0; ht < C::HT; ++ht) dq[ht] = sf.apply(Kt + (ht * 16 + l16) * TP, g, dq[ht]);
+    for (int ht = 0; ht < C::HT; ++ht) {
+      if constexpr (C::TR)
+        dq[ht] = sf.apply_tr(Ks, KP, ht * 16, lane, dq[ht]);
+      else
+        dq[ht] = sf.apply(Kt + (ht * 16 + l16) * TP, g, dq[ht]);
+    }
   }
   if (qok) {
     const float scale = 1.f / sqrtf((float)HD);
