@@ -27,7 +27,8 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function",
 ]
-HOST_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-fopenmp", "-Wall", "-D__HIP_PLATFORM_AMD__",
+HOST_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-fopenmp", "-Wall", "-ffp-contract=off",
+              "-D__HIP_PLATFORM_AMD__",
               f"-I{ROCM}/include"]
 
 

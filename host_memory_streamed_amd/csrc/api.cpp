@@ -125,6 +125,9 @@ static int validate(const mt_model_cfg* c, std::string& why) {
       !(c->beta2 >= 0.0 && c->beta2 < 1.0) || !(c->adam_eps >= 0.0))
     return bad("invalid eps / rope_base / AdamW hyperparameters");
   if (c->flags & ~(MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE)) return bad("unknown flags");
+  if (c->chunk_rows < 0) return bad("chunk_rows must be >= 0");
+  if (c->ckpt_host < 0 || (c->ckpt_host > 0 && c->ckpt_host > c->n_layers - 2))
+    return bad("ckpt_host must be 0 or in [1, n_layers - 2]");
   return MT_OK;
 }
 
@@ -144,6 +147,7 @@ static void free_ctx(Ctx* c) {
     if (u.shadow) hipHostFree(u.shadow);
   }
   for (auto* p : c->ring_slot) hipHostFree(p);
+  for (auto* p : c->ck_host) hipHostFree(p);
   for (void* p : {(void*)c->x0_host, (void*)c->dx0_host, (void*)c->tgt_host, (void*)c->loss_host})
     if (p) hipHostFree(p);
   for (void* p : c->dev_allocs) hipFree(p);
@@ -292,33 +296,42 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
   for (int i = 0; i < c.nbuf; ++i) ok &= dalloc(img, &c.buf[i]);
   ok &= dalloc((size_t)max_unit * 4, (void**)&c.gbuf[0]);
   ok &= dalloc((size_t)max_unit * 4, (void**)&c.gbuf[1]);
-  ok &= dalloc((size_t)(D.L + 1) * c.M_max * D.d * 4, (void**)&c.ckpt);
   Workspace& w = c.ws;
   const int64_t M = c.M_max, d = D.d, F = D.F, V = D.V;
   const size_t es = S ? 2 : 4;
+  // token chunk of the QKV projection and the MLP
+  {
+    const int64_t mlp_row = 2 * F * 4 + F * (int64_t)es + F * 4 + 2 * F * (int64_t)es + d * (int64_t)es;
+    int64_t ch = cfg->chunk_rows > 0 ? cfg->chunk_rows : M;
+    if (cfg->chunk_rows == 0 && M * mlp_row > (4LL << 30))
+      ch = std::max<int64_t>(256, (4LL << 30) / mlp_row / 256 * 256);
+    w.chunk = std::min(ch, M);
+  }
+  const int64_t Q = w.chunk;
   ok &= dalloc(M * d * es, &w.h);
   ok &= dalloc(M * 4, (void**)&w.rstd1);
   ok &= dalloc(M * 4, (void**)&w.rstd2);
-  ok &= dalloc(M * D.qkvd * 4, (void**)&w.qkv_f);
+  ok &= dalloc(Q * D.qkvd * 4, (void**)&w.qkv_f);
   ok &= dalloc(M * D.qkvd * es, &w.qkv_s);
   ok &= dalloc(M * D.qd * 4, (void**)&w.o_f);
   if (S) ok &= dalloc(M * D.qd * es, &w.o_s); else w.o_s = w.o_f;
   ok &= dalloc(M * D.H * 4, (void**)&w.lse);
   ok &= dalloc(M * d * 4, (void**)&w.x1);
-  ok &= dalloc(M * d * es, &w.h2);
-  ok &= dalloc(M * 2 * F * 4, (void**)&w.gu_f);
-  ok &= dalloc(M * F * es, &w.act);
+  ok &= dalloc(Q * d * es, &w.h2);
+  ok &= dalloc(Q * 2 * F * 4, (void**)&w.gu_f);
+  ok &= dalloc(Q * F * es, &w.act);
   ok &= dalloc(M * d * 4, (void**)&w.g_f);
   if (S) ok &= dalloc(M * d * es, &w.g_s); else w.g_s = w.g_f;
-  ok &= dalloc(M * F * 4, (void**)&w.dact_f);
-  ok &= dalloc(M * 2 * F * es, &w.dgu_s);
-  ok &= dalloc(M * d * 4, (void**)&w.dh_f);
-  ok &= dalloc(M * D.qd * 4, (void**)&w.do_f);
-  ok &= dalloc(M * D.qkvd * 4, (void**)&w.dqkv_f);
+  ok &= dalloc(Q * F * 4, (void**)&w.dact_f);
+  ok &= dalloc(Q * 2 * F * es, &w.dgu_s);
+  // dO (consumed by the attention backward) and the projections' input
+  // gradients (consumed by the RMSNorm backwards) are never live together
+  ok &= dalloc(M * std::max<int64_t>(d, D.qd) * 4, (void**)&w.dh_f);
+  w.do_f = w.dh_f;
   ok &= dalloc(M * D.qkvd * es, &w.dqkv_s);
   ok &= dalloc((size_t)mt_op_attn_bwd_ws_bytes(S, cfg->max_batch, cfg->max_seq, D.H, D.hd), &w.attn_ws);
   ok &= dalloc((size_t)rmsnorm_bwd_partials(M) * d * 4, (void**)&w.rms_ws);
-  ok &= dalloc(M * d * es, &w.hf);
+  w.hf = w.h;   // the head runs between the last forward and the first recompute
   ok &= dalloc(M * 4, (void**)&w.rstdf);
   // logits in token chunks of at most ~4 GiB (multiples of 128 rows)
   int64_t chunk = (int64_t)((4LL << 30) / ((int64_t)V * 4));
@@ -332,6 +345,39 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
   ok &= dalloc((size_t)cfg->max_seq * half * 4, (void**)&w.rope_cos);
   ok &= dalloc((size_t)cfg->max_seq * half * 4, (void**)&w.rope_sin);
   if (!ok) { mt_destroy(h); return set_error(nullptr, MT_EDEVOOM, "device allocation failed"); }
+
+  // ---- residual checkpoints: device slots, parking the rest in host memory ----
+  {
+    const size_t slot = (size_t)M * d * 4;
+    int k = cfg->ckpt_host;
+    if (k == 0) {
+      size_t free_b = 0, total_b = 0;
+      HIP_OR(hipMemGetInfo(&free_b, &total_b), MT_EHIP, "hipMemGetInfo");
+      const size_t margin = (size_t)1 << 30;
+      const int64_t fit = free_b > margin ? (int64_t)((free_b - margin) / slot) : 0;
+      if (fit < D.L + 1) {
+        if (D.L < 3 || fit < 2) {
+          mt_destroy(h);
+          return set_error(nullptr, MT_EDEVOOM, "device memory cannot hold two residual checkpoints next to the workspace");
+        }
+        k = (int)(D.L - fit);   // device slots = L - k
+      }
+    }
+    c.ck_nh = k > 0 ? k + 3 : 0;
+    const int dev_slots = D.L + 1 - c.ck_nh;
+    if (k > 0) {
+      ok &= dalloc(slot, (void**)&c.stage[0]);
+      ok &= dalloc(slot, (void**)&c.stage[1]);
+    }
+    ok &= dalloc(slot * (size_t)dev_slots, (void**)&c.ckpt);
+    if (!ok) { mt_destroy(h); return set_error(nullptr, MT_EDEVOOM, "device allocation of residual checkpoints failed"); }
+    for (int i = 0; i < k; ++i) {
+      float* p = nullptr;
+      HIP_OR(hipHostMalloc((void**)&p, slot, hipHostMallocDefault), MT_EHOSTOOM, "pinned checkpoint slab");
+      c.ck_host.push_back(p);
+    }
+  }
+
 
   // ---- streams (default priority) ----
   hipStream_t* ss[3] = {&c.s_in, &c.s_comp, &c.s_out};
@@ -468,7 +514,7 @@ int mt_trace_dump(mt_ctx* h, const char* path) {
   if (!h || !path) return MT_EINVAL;
   FILE* f = fopen(path, "w");
   if (!f) return set_error(&h->c, MT_EINVAL, std::string("cannot open ") + path);
-  static const char* ph[] = {"load", "fwd", "head", "bwd", "grad", "adamw"};
+  static const char* ph[] = {"load", "fwd", "head", "bwd", "grad", "adamw", "ckpt out", "ckpt in"};
   static const char* st[] = {"copy-in", "compute", "copy-out", "host AdamW"};
   fprintf(f, "{\"traceEvents\":[\n");
   bool first = true;
@@ -481,6 +527,7 @@ int mt_trace_dump(mt_ctx* h, const char* path) {
     char unit[32];
     if (e.unit == MT_UNIT_HEAD) snprintf(unit, sizeof unit, "head");
     else if (e.unit == MT_UNIT_EMB) snprintf(unit, sizeof unit, "embedding");
+    else if (e.phase >= MT_PH_CKPT_OUT) snprintf(unit, sizeof unit, "x_%d", e.unit);
     else snprintf(unit, sizeof unit, "layer %d", e.unit);
     fprintf(f, ",\n{\"name\":\"%s %s\",\"ph\":\"X\",\"pid\":0,\"tid\":%d,\"ts\":%.3f,\"dur\":%.3f,\"args\":{\"buffer\":%d}}",
             ph[e.phase], unit, e.stream, e.t0_ms * 1000.0, (e.t1_ms - e.t0_ms) * 1000.0, e.buffer);
@@ -493,6 +540,15 @@ int mt_trace_dump(mt_ctx* h, const char* path) {
 int mt_device_bytes(mt_ctx* h, int64_t* bytes) {
   if (!h || !bytes) return MT_EINVAL;
   *bytes = h->c.dev_bytes;
+  return MT_OK;
+}
+
+int mt_layout_info(mt_ctx* h, int64_t* chunk_rows, int32_t* ckpt_host, int32_t* ckpt_device_slots) {
+  if (!h) return MT_EINVAL;
+  const Ctx& c = h->c;
+  if (chunk_rows) *chunk_rows = c.ws.chunk;
+  if (ckpt_host) *ckpt_host = (int32_t)c.ck_host.size();
+  if (ckpt_device_slots) *ckpt_device_slots = c.D.L + 1 - c.ck_nh + (c.ck_nh ? 2 : 0);
   return MT_OK;
 }
 

@@ -305,6 +305,64 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
 
 // --------------------------------------------------------------- backward ---
 
+template <typename OutT>
+__device__ __forceinline__ void put4(OutT* p, floatx4 v) {
+  if constexpr (sizeof(OutT) == 4) {
+    *reinterpret_cast<floatx4*>(p) = v;
+  } else {
+    bf16x4 b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = to_bf16(v[i]);
+    *reinterpret_cast<bf16x4*>(p) = b;
+  }
+}
+
+// One head's gradient row held by the 4 lanes of a column group: lane group g
+// owns columns ht*16 + g*4 + r. Scaled, then (if cs is not NULL) rotated by
+// the negative RoPE angle of the row's position -- the backward of the
+// half-split rotation pairs column i with i + HD/2 -- and stored as OutT.
+template <typename OutT, int HD>
+__device__ __forceinline__ void store_grad_row(OutT* row, const floatx4 (&acc)[HD / 16], float scale,
+                                               const float* cs, const float* sn, int g) {
+  constexpr int HT = HD / 16, HALF = HD / 2;
+  if (!cs) {
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) put4<OutT>(row + ht * 16 + g * 4, acc[ht] * scale);
+    return;
+  }
+  if constexpr (HT >= 2) {
+#pragma unroll
+    for (int ht = 0; ht < HT / 2; ++ht) {
+      const int c0 = ht * 16 + g * 4;
+      const floatx4 x1 = acc[ht] * scale, x2 = acc[ht + HT / 2] * scale;
+      floatx4 o1, o2;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float c = cs[c0 + r], s = sn[c0 + r];
+        o1[r] = x1[r] * c + x2[r] * s;
+        o2[r] = x2[r] * c - x1[r] * s;
+      }
+      put4<OutT>(row + c0, o1);
+      put4<OutT>(row + HALF + c0, o2);
+    }
+  } else {
+    // hd = 16: the partner column sits in the lane 32 apart (g ^ 2)
+    const floatx4 x = acc[0] * scale;
+    floatx4 y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] = __shfl_xor(x[r], 32, 64);
+    const bool lo = g < 2;
+    const int c0 = (g & 1) * 4;   // column within the half
+    floatx4 o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float c = cs[c0 + r], s = sn[c0 + r];
+      o[r] = lo ? x[r] * c + y[r] * s : x[r] * c - y[r] * s;
+    }
+    put4<OutT>(row + g * 4, o);
+  }
+}
+
 // D[b,h,t] = sum_i dO[m, h*HD+i] O[m, h*HD+i]; dO also rounded to T.
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const float* __restrict__ o,
@@ -332,13 +390,15 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const float* __restri
 
 // dK, dV for one 64-key block of kv head kvh, summed over the query heads of
 // its group and every query block at or after the diagonal.
-template <typename T, int HD>
+template <typename T, int HD, typename OutT>
 __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(const T* __restrict__ qkv,
                                                            const T* __restrict__ dcast,
                                                            const float* __restrict__ lse,
                                                            const float* __restrict__ D,
-                                                           float* __restrict__ dqkv, int Tn, int H,
-                                                           int Hkv) {
+                                                           OutT* __restrict__ dqkv,
+                                                           const float* __restrict__ rcos,
+                                                           const float* __restrict__ rsin, int Tn,
+                                                           int H, int Hkv) {
   typedef Cfg<T, HD> C;
   constexpr int BQ = C::BQ, NQT = BQ / 16, RP = HD + C::PAD, TP = BQ + C::PAD;
   __shared__ __attribute__((aligned(16))) T Qs[BQ * RP];
@@ -416,26 +476,27 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(const T* __restrict__
     }
   }
 
+  // lanes l and l ^ 32 (the hd = 16 rotation partners) hold the same key, so
+  // both take this branch or neither does
   if (key < Tn) {
-    const float scale = 1.f / sqrtf((float)HD);
-    const int64_t ldq = ld;   // dqkv has the qkv layout
-    float* row = dqkv + ((int64_t)b * Tn + key) * ldq;
-#pragma unroll
-    for (int ht = 0; ht < C::HT; ++ht) {
-      *reinterpret_cast<floatx4*>(row + (H + kvh) * HD + ht * 16 + g * 4) = dk[ht] * scale;
-      *reinterpret_cast<floatx4*>(row + (H + Hkv + kvh) * HD + ht * 16 + g * 4) = dv[ht];
-    }
+    OutT* row = dqkv + ((int64_t)b * Tn + key) * ld;   // dqkv has the qkv layout
+    const float* cs = rcos ? rcos + (int64_t)key * (HD / 2) : nullptr;
+    const float* sn = rsin ? rsin + (int64_t)key * (HD / 2) : nullptr;
+    store_grad_row<OutT, HD>(row + (H + kvh) * HD, dk, 1.f / sqrtf((float)HD), cs, sn, g);
+    store_grad_row<OutT, HD>(row + (H + Hkv + kvh) * HD, dv, 1.f, nullptr, nullptr, g);
   }
 }
 
 // dQ for one 64-query block of head h over the key tiles up to the diagonal.
-template <typename T, int HD>
+template <typename T, int HD, typename OutT>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const T* __restrict__ qkv,
                                                           const T* __restrict__ dcast,
                                                           const float* __restrict__ lse,
                                                           const float* __restrict__ D,
-                                                          float* __restrict__ dqkv, int Tn, int H,
-                                                          int Hkv, int n_qblk) {
+                                                          OutT* __restrict__ dqkv,
+                                                          const float* __restrict__ rcos,
+                                                          const float* __restrict__ rsin, int Tn,
+                                                          int H, int Hkv, int n_qblk) {
   typedef Cfg<T, HD> C;
   constexpr int BKV = C::BKV, NKT = BKV / 16, KP = HD + C::PAD, TP = BKV + C::PAD;
   __shared__ __attribute__((aligned(16))) T Ks[BKV * KP];
@@ -495,12 +556,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const T* __restrict__ 
         dq[ht] = sf.apply(Kt + (ht * 16 + l16) * TP, g, dq[ht]);
     }
   }
-  if (qok) {
-    const float scale = 1.f / sqrtf((float)HD);
-    float* row = dqkv + ((int64_t)b * Tn + q) * ld + h * HD;
-#pragma unroll
-    for (int ht = 0; ht < C::HT; ++ht)
-      *reinterpret_cast<floatx4*>(row + ht * 16 + g * 4) = dq[ht] * scale;
+  if (qok) {   // uniform across the hd = 16 rotation partners (same query)
+    OutT* row = dqkv + ((int64_t)b * Tn + q) * ld + h * HD;
+    const float* cs = rcos ? rcos + (int64_t)q * (HD / 2) : nullptr;
+    const float* sn = rsin ? rsin + (int64_t)q * (HD / 2) : nullptr;
+    store_grad_row<OutT, HD>(row, dq, 1.f / sqrtf((float)HD), cs, sn, g);
   }
 }
 
@@ -513,9 +573,11 @@ hipError_t fwd_launch(const void* qkv, float* o, void* oc, float* lse, int B, in
   return hipGetLastError();
 }
 
-template <typename T, int HD>
+template <typename T, int HD, typename OutT>
 hipError_t bwd_launch(const void* qkv, const float* o, const float* dout, const float* lse,
-                      float* dqkv, void* ws, int B, int Tn, int H, int Hkv, hipStream_t s) {
+                      void* dqkv_v, const float* rcos, const float* rsin, void* ws, int B, int Tn,
+                      int H, int Hkv, hipStream_t s) {
+  OutT* dqkv = static_cast<OutT*>(dqkv_v);
   const int64_t M = (int64_t)B * Tn;
   float* D = reinterpret_cast<float*>(ws);
   T* dcast = reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + attn_ws_d_bytes(B, Tn, H));
@@ -525,12 +587,13 @@ hipError_t bwd_launch(const void* qkv, const float* o, const float* dout, const 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nk = (Tn + 63) / 64;
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, HD>), dim3(nk, Hkv, B), dim3(256), 0, s, (const T*)qkv,
-                     (const T*)dcast, lse, (const float*)D, dqkv, Tn, H, Hkv);
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, HD, OutT>), dim3(nk, Hkv, B), dim3(256), 0, s,
+                     (const T*)qkv, (const T*)dcast, lse, (const float*)D, dqkv, rcos, rsin, Tn, H, Hkv);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), dim3(nk, H, B), dim3(256), 0, s, (const T*)qkv,
-                     (const T*)dcast, lse, (const float*)D, dqkv, Tn, H, Hkv, nk);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD, OutT>), dim3(nk, H, B), dim3(256), 0, s,
+                     (const T*)qkv, (const T*)dcast, lse, (const float*)D, dqkv, rcos, rsin, Tn, H,
+                     Hkv, nk);
   return hipGetLastError();
 }
 
@@ -560,17 +623,20 @@ hipError_t attn_fwd(int dtype, const void* qkv, float* o, void* o_cast, float* l
 }
 
 hipError_t attn_bwd(int dtype, const void* qkv, const float* o, const float* dout, const float* lse,
-                    float* dqkv, void* ws, int B, int Tn, int H, int Hkv, int hd, hipStream_t s) {
+                    void* dqkv, int out_dtype, const float* rcos, const float* rsin, void* ws, int B,
+                    int Tn, int H, int Hkv, int hd, hipStream_t s) {
+#define MT_BWD(T, HD, O) bwd_launch<T, HD, O>(qkv, o, dout, lse, dqkv, rcos, rsin, ws, B, Tn, H, Hkv, s)
   if (dtype == 1) {
-    if (hd == 64) return bwd_launch<bf16, 64>(qkv, o, dout, lse, dqkv, ws, B, Tn, H, Hkv, s);
-    return bwd_launch<bf16, 128>(qkv, o, dout, lse, dqkv, ws, B, Tn, H, Hkv, s);
+    if (hd == 64) return out_dtype ? MT_BWD(bf16, 64, bf16) : MT_BWD(bf16, 64, float);
+    return out_dtype ? MT_BWD(bf16, 128, bf16) : MT_BWD(bf16, 128, float);
   }
   switch (hd) {
-    case 16: return bwd_launch<float, 16>(qkv, o, dout, lse, dqkv, ws, B, Tn, H, Hkv, s);
-    case 32: return bwd_launch<float, 32>(qkv, o, dout, lse, dqkv, ws, B, Tn, H, Hkv, s);
-    case 64: return bwd_launch<float, 64>(qkv, o, dout, lse, dqkv, ws, B, Tn, H, Hkv, s);
-    default: return bwd_launch<float, 128>(qkv, o, dout, lse, dqkv, ws, B, Tn, H, Hkv, s);
+    case 16: return MT_BWD(float, 16, float);
+    case 32: return MT_BWD(float, 32, float);
+    case 64: return MT_BWD(float, 64, float);
+    default: return MT_BWD(float, 128, float);
   }
+#undef MT_BWD
 }
 
 }  // namespace mt

@@ -144,7 +144,14 @@ __attribute__((target("avx512f,avx512bw,avx512vl"))) static void adamw_avx512(
                omb2 = _mm512_set1_ps(k.omb2), ss = _mm512_set1_ps(k.step_size),
                isb = _mm512_set1_ps(k.inv_sqrt_bc2), eps = _mm512_set1_ps(k.eps);
   const __m512i rbias = _mm512_set1_epi32(0x7FFF), one = _mm512_set1_epi32(1);
+  // The bf16 image is write-only here and is next read by the DMA engine, so
+  // it is written with streaming stores (no read-for-ownership of its lines).
+  // Those need 32-byte aligned destinations: a short scalar head gets there.
   int64_t i = 0;
+  if (bo) {
+    while (i < n && (reinterpret_cast<uintptr_t>(bo + i) & 31)) ++i;
+    adamw_scalar(p, m, v, g, 0, i, k, bo, fo);
+  }
   for (; i + 16 <= n; i += 16) {
     const __m512 gi = _mm512_loadu_ps(g + i);
     __m512 pi = _mm512_mul_ps(_mm512_loadu_ps(p + i), decay);
@@ -160,11 +167,14 @@ __attribute__((target("avx512f,avx512bw,avx512vl"))) static void adamw_avx512(
       const __m512i u = _mm512_castps_si512(pi);
       const __m512i r = _mm512_add_epi32(_mm512_add_epi32(u, rbias),
                                          _mm512_and_si512(_mm512_srli_epi32(u, 16), one));
-      _mm256_storeu_si256(reinterpret_cast<__m256i*>(bo + i), _mm512_cvtepi32_epi16(_mm512_srli_epi32(r, 16)));
+      _mm256_stream_si256(reinterpret_cast<__m256i*>(bo + i), _mm512_cvtepi32_epi16(_mm512_srli_epi32(r, 16)));
     }
     if (fo) _mm512_storeu_ps(fo + i, pi);
   }
   adamw_scalar(p, m, v, g, i, n, k, bo, fo);
+  // streaming stores are weakly ordered: make them visible before the caller
+  // reports the range done
+  if (bo) _mm_sfence();
 }
 
 void adamw_range(float* p, float* m, float* v, const float* g, int64_t n, const AdamConst& k,

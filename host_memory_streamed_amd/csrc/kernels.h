@@ -22,8 +22,12 @@ bool attn_supported(int dtype, int hd);
 int64_t attn_ws_d_bytes(int B, int T, int H);
 hipError_t attn_fwd(int dtype, const void* qkv, float* o, void* o_cast, float* lse, int B, int T,
                     int H, int Hkv, int hd, hipStream_t s);
+// dqkv of out_dtype (fp32, or bf16 when dtype is bf16); with rcos/rsin (the
+// RoPE tables) the q and k gradients are rotated back to the unrotated
+// projection output, else they are the gradients of the rotated operands.
 hipError_t attn_bwd(int dtype, const void* qkv, const float* o, const float* dout, const float* lse,
-                    float* dqkv, void* ws, int B, int T, int H, int Hkv, int hd, hipStream_t s);
+                    void* dqkv, int out_dtype, const float* rcos, const float* rsin, void* ws, int B,
+                    int T, int H, int Hkv, int hd, hipStream_t s);
 
 int rmsnorm_bwd_partials(int64_t rows);
 hipError_t rmsnorm_fwd(int out_dtype, const float* x, const float* w, void* y, float* rstd,
@@ -31,8 +35,11 @@ hipError_t rmsnorm_fwd(int out_dtype, const float* x, const float* w, void* y, f
 hipError_t rmsnorm_bwd(const float* x, const float* w, const float* rstd, const float* dy,
                        float* dx, int accumulate, float* dw, float* ws, int64_t rows, int d,
                        hipStream_t s);
+// rows [row0, row0 + rows) of the token sequence (positions (row0 + i) % T);
+// `in` and `out` point at the first of those rows
 hipError_t rope(int out_dtype, int backward, const float* in, void* out, const float* cos,
-                const float* sin, int B, int T, int H, int Hkv, int hd, hipStream_t s);
+                const float* sin, int64_t row0, int64_t rows, int T, int H, int Hkv, int hd,
+                hipStream_t s);
 hipError_t swiglu_fwd(int out_dtype, const float* gu, void* act, int64_t M, int F, hipStream_t s);
 hipError_t swiglu_bwd(int out_dtype, const float* gu, const float* dact, void* dgu, int64_t M,
                       int F, hipStream_t s);

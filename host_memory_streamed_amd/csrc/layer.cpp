@@ -11,7 +11,8 @@
 // Binding is an offset computation over the unit layout: no allocation and no
 // per-layer device object. Only the residual stream at layer boundaries is
 // kept (checkpoints x_0..x_L); the backward of layer l recomputes the block
-// from x_l up to the SwiGLU output and then runs the hand-written backward.
+// from x_l through the attention output projection, then rebuilds the MLP
+// input side chunk by chunk inside the hand-written backward.
 #include <cmath>
 
 #include "kernels.h"
@@ -71,32 +72,64 @@ static inline double gemm_bytes(int64_t M, int64_t N, int64_t K, int dt, bool r)
   return (double)(M * K + K * N) * esz(dt) + (double)M * N * 4 * (r ? 2 : 1);
 }
 
+// QKV projection and its rotation, chunk by chunk: qkv_s = rope(h Wqkv^T).
+static int qkv_forward(Ctx& c, const LayerPtrs& W, int64_t M, int T) {
+  const Dims& D = c.D;
+  const int S = c.dtype;
+  Workspace& w = c.ws;
+  const int64_t d = D.d;
+  for (int64_t r0 = 0; r0 < M; r0 += w.chunk) {
+    const int64_t mc = std::min(w.chunk, M - r0);
+    const void* h = static_cast<const char*>(w.h) + r0 * d * esz(S);
+    void* qs = static_cast<char*>(w.qkv_s) + r0 * D.qkvd * esz(S);
+    RUN(K_GEMM_NT, 2.0 * mc * D.qkvd * d, gemm_bytes(mc, D.qkvd, d, S, false),
+        gemm(S, MT_GEMM_NT, h, d, W.wqkv, d, w.qkv_f, D.qkvd, nullptr, 0, mc, D.qkvd, d, c.s_comp));
+    RUN(K_ROPE, 0, (double)mc * D.qkvd * (4 + esz(S)),
+        rope(S, 0, w.qkv_f, qs, w.rope_cos, w.rope_sin, r0, mc, T, D.H, D.Hkv, D.hd, c.s_comp));
+  }
+  return MT_OK;
+}
+
+// MLP input side for rows [r0, r0 + mc): h2 = RMSNorm(x1), gu = h2 Wgu^T,
+// act = silu(gate) up (chunk buffers).
+static int mlp_front(Ctx& c, const LayerPtrs& W, int64_t r0, int64_t mc) {
+  const Dims& D = c.D;
+  const int S = c.dtype;
+  Workspace& w = c.ws;
+  const int64_t d = D.d, F = D.F;
+  RUN(K_RMS_FWD, 0, (double)mc * d * (4 + esz(S)),
+      rmsnorm_fwd(S, w.x1 + r0 * d, W.mlp_norm, w.h2, w.rstd2 + r0, mc, D.d, c.cfg.rms_eps, c.s_comp));
+  RUN(K_GEMM_NT, 2.0 * mc * 2 * F * d, gemm_bytes(mc, 2 * F, d, S, false),
+      gemm(S, MT_GEMM_NT, w.h2, d, W.wgu, d, w.gu_f, 2 * F, nullptr, 0, mc, 2 * F, d, c.s_comp));
+  RUN(K_SWIGLU, 0, (double)mc * F * (8 + esz(S)), swiglu_fwd(S, w.gu_f, w.act, mc, D.F, c.s_comp));
+  return MT_OK;
+}
+
 int layer_forward(Ctx& c, const LayerPtrs& W, int l, int B, int T, bool recompute) {
   const Dims& D = c.D;
   const int S = c.dtype;
   Workspace& w = c.ws;
   const int64_t M = (int64_t)B * T, d = D.d, F = D.F;
-  const float* x = c.ckpt + (int64_t)l * c.M_max * d;
-  float* xn = c.ckpt + (int64_t)(l + 1) * c.M_max * d;
+  const float* x = c.ckpt_dev(l);
   const float eps = c.cfg.rms_eps;
   const double attn_fl = 2.0 * B * (double)T * T * D.H * D.hd;
 
   RUN(K_RMS_FWD, 0, (double)M * d * (4 + esz(S)), rmsnorm_fwd(S, x, W.attn_norm, w.h, w.rstd1, M, D.d, eps, c.s_comp));
-  RUN(K_GEMM_NT, 2.0 * M * D.qkvd * d, gemm_bytes(M, D.qkvd, d, S, false),
-      gemm(S, MT_GEMM_NT, w.h, d, W.wqkv, d, w.qkv_f, D.qkvd, nullptr, 0, M, D.qkvd, d, c.s_comp));
-  RUN(K_ROPE, 0, (double)M * D.qkvd * (4 + esz(S)),
-      rope(S, 0, w.qkv_f, w.qkv_s, w.rope_cos, w.rope_sin, B, T, D.H, D.Hkv, D.hd, c.s_comp));
+  int rc = qkv_forward(c, W, M, T);
+  if (rc) return rc;
   RUN(K_ATTN_FWD, attn_fl, (double)M * D.qkvd * esz(S) + (double)M * D.qd * (4 + (S ? 2 : 0)),
       attn_fwd(S, w.qkv_s, w.o_f, S ? w.o_s : nullptr, w.lse, B, T, D.H, D.Hkv, D.hd, c.s_comp));
   RUN(K_GEMM_NT, 2.0 * M * d * D.qd, gemm_bytes(M, d, D.qd, S, true),
       gemm(S, MT_GEMM_NT, w.o_s, D.qd, W.wo, D.qd, w.x1, d, x, d, M, d, D.qd, c.s_comp));
-  RUN(K_RMS_FWD, 0, (double)M * d * (4 + esz(S)), rmsnorm_fwd(S, w.x1, W.mlp_norm, w.h2, w.rstd2, M, D.d, eps, c.s_comp));
-  RUN(K_GEMM_NT, 2.0 * M * 2 * F * d, gemm_bytes(M, 2 * F, d, S, false),
-      gemm(S, MT_GEMM_NT, w.h2, d, W.wgu, d, w.gu_f, 2 * F, nullptr, 0, M, 2 * F, d, c.s_comp));
-  RUN(K_SWIGLU, 0, (double)M * F * (8 + esz(S)), swiglu_fwd(S, w.gu_f, w.act, M, D.F, c.s_comp));
-  if (!recompute)
-    RUN(K_GEMM_NT, 2.0 * M * d * F, gemm_bytes(M, d, F, S, true),
-        gemm(S, MT_GEMM_NT, w.act, F, W.wdown, F, xn, d, w.x1, d, M, d, F, c.s_comp));
+  // the recompute stops here: the backward rebuilds the MLP chunk by chunk
+  if (recompute) return MT_OK;
+  float* xn = c.ckpt_dev(l + 1);
+  for (int64_t r0 = 0; r0 < M; r0 += w.chunk) {
+    const int64_t mc = std::min(w.chunk, M - r0);
+    if ((rc = mlp_front(c, W, r0, mc))) return rc;
+    RUN(K_GEMM_NT, 2.0 * mc * d * F, gemm_bytes(mc, d, F, S, true),
+        gemm(S, MT_GEMM_NT, w.act, F, W.wdown, F, xn + r0 * d, d, w.x1 + r0 * d, d, mc, d, F, c.s_comp));
+  }
   return MT_OK;
 }
 
@@ -107,24 +140,33 @@ int layer_backward(Ctx& c, const LayerPtrs& W, int l, int B, int T, float* gu) {
   Workspace& w = c.ws;
   const UnitLayout& U = c.units[0].lay;
   const int64_t M = (int64_t)B * T, d = D.d, F = D.F, qd = D.qd, qkvd = D.qkvd;
-  const float* x = c.ckpt + (int64_t)l * c.M_max * d;
+  const float* x = c.ckpt_dev(l);
   const double attn_fl = 2.0 * B * (double)T * T * D.H * D.hd;
 
   int rc = layer_forward(c, W, l, B, T, true);
   if (rc) return rc;
 
-  // down projection: x_{l+1} = x1 + act Wd^T
+  // MLP, chunk by chunk: recompute h2, gu, act; then
+  // down: x_{l+1} = x1 + act Wd^T;  gate/up: gu = h2 Wgu^T.
+  // The weight gradients accumulate over the chunks in chunk order.
   if (S) RUN(K_CAST, 0, (double)M * d * 6, cast(S, w.g_f, w.g_s, M * d, c.s_comp));
-  RUN(K_GEMM_NN, 2.0 * M * F * d, gemm_bytes(M, F, d, S, false),
-      gemm(S, MT_GEMM_NN, w.g_s, d, W.wdown, F, w.dact_f, F, nullptr, 0, M, F, d, c.s_comp));
-  RUN(K_GEMM_TN, 2.0 * d * F * M, gemm_bytes(d, F, M, S, false),
-      gemm(S, MT_GEMM_TN, w.g_s, d, w.act, F, gu + U.off[5], F, nullptr, 0, d, F, M, c.s_comp));
-  RUN(K_SWIGLU, 0, (double)M * F * (12 + 2 * esz(S)), swiglu_bwd(S, w.gu_f, w.dact_f, w.dgu_s, M, D.F, c.s_comp));
-  // gate/up projection: gu = h2 Wgu^T
-  RUN(K_GEMM_NN, 2.0 * M * d * 2 * F, gemm_bytes(M, d, 2 * F, S, false),
-      gemm(S, MT_GEMM_NN, w.dgu_s, 2 * F, W.wgu, d, w.dh_f, d, nullptr, 0, M, d, 2 * F, c.s_comp));
-  RUN(K_GEMM_TN, 2.0 * 2 * F * d * M, gemm_bytes(2 * F, d, M, S, false),
-      gemm(S, MT_GEMM_TN, w.dgu_s, 2 * F, w.h2, d, gu + U.off[4], d, nullptr, 0, 2 * F, d, M, c.s_comp));
+  for (int64_t r0 = 0; r0 < M; r0 += w.chunk) {
+    const int64_t mc = std::min(w.chunk, M - r0);
+    const bool acc = r0 > 0;
+    const void* gs = static_cast<const char*>(w.g_s) + r0 * d * esz(S);
+    if ((rc = mlp_front(c, W, r0, mc))) return rc;
+    RUN(K_GEMM_NN, 2.0 * mc * F * d, gemm_bytes(mc, F, d, S, false),
+        gemm(S, MT_GEMM_NN, gs, d, W.wdown, F, w.dact_f, F, nullptr, 0, mc, F, d, c.s_comp));
+    RUN(K_GEMM_TN, 2.0 * d * F * mc, gemm_bytes(d, F, mc, S, acc),
+        gemm(S, MT_GEMM_TN, gs, d, w.act, F, gu + U.off[5], F, acc ? gu + U.off[5] : nullptr, F, d, F, mc,
+             c.s_comp));
+    RUN(K_SWIGLU, 0, (double)mc * F * (12 + 2 * esz(S)), swiglu_bwd(S, w.gu_f, w.dact_f, w.dgu_s, mc, D.F, c.s_comp));
+    RUN(K_GEMM_NN, 2.0 * mc * d * 2 * F, gemm_bytes(mc, d, 2 * F, S, false),
+        gemm(S, MT_GEMM_NN, w.dgu_s, 2 * F, W.wgu, d, w.dh_f + r0 * d, d, nullptr, 0, mc, d, 2 * F, c.s_comp));
+    RUN(K_GEMM_TN, 2.0 * 2 * F * d * mc, gemm_bytes(2 * F, d, mc, S, acc),
+        gemm(S, MT_GEMM_TN, w.dgu_s, 2 * F, w.h2, d, gu + U.off[4], d, acc ? gu + U.off[4] : nullptr, d, 2 * F,
+             d, mc, c.s_comp));
+  }
   RUN(K_RMS_BWD, 0, (double)M * d * 20,
       rmsnorm_bwd(w.x1, W.mlp_norm, w.rstd2, w.dh_f, w.g_f, 1, gu + U.off[1], w.rms_ws, M, D.d, c.s_comp));
   // out projection: x1 = x + o Wo^T
@@ -133,11 +175,10 @@ int layer_backward(Ctx& c, const LayerPtrs& W, int l, int B, int T, float* gu) {
       gemm(S, MT_GEMM_NN, w.g_s, d, W.wo, qd, w.do_f, qd, nullptr, 0, M, qd, d, c.s_comp));
   RUN(K_GEMM_TN, 2.0 * d * qd * M, gemm_bytes(d, qd, M, S, false),
       gemm(S, MT_GEMM_TN, w.g_s, d, w.o_s, qd, gu + U.off[3], qd, nullptr, 0, d, qd, M, c.s_comp));
-  // attention and rotation
-  RUN(K_ATTN_BWD, 2.5 * attn_fl, (double)M * qkvd * (esz(S) + 4) + (double)M * qd * 8,
-      attn_bwd(S, w.qkv_s, w.o_f, w.do_f, w.lse, w.dqkv_f, w.attn_ws, B, T, D.H, D.Hkv, D.hd, c.s_comp));
-  RUN(K_ROPE, 0, (double)M * qkvd * (4 + esz(S)),
-      rope(S, 1, w.dqkv_f, w.dqkv_s, w.rope_cos, w.rope_sin, B, T, D.H, D.Hkv, D.hd, c.s_comp));
+  // attention, with the rotation's backward applied as the gradients are written
+  RUN(K_ATTN_BWD, 2.5 * attn_fl, (double)M * qkvd * 2 * esz(S) + (double)M * qd * 8,
+      attn_bwd(S, w.qkv_s, w.o_f, w.do_f, w.lse, w.dqkv_s, S, w.rope_cos, w.rope_sin, w.attn_ws, B, T, D.H,
+               D.Hkv, D.hd, c.s_comp));
   // qkv projection
   RUN(K_GEMM_NN, 2.0 * M * d * qkvd, gemm_bytes(M, d, qkvd, S, false),
       gemm(S, MT_GEMM_NN, w.dqkv_s, qkvd, W.wqkv, d, w.dh_f, d, nullptr, 0, M, d, qkvd, c.s_comp));
@@ -157,7 +198,7 @@ int head_forward_backward(Ctx& c, const void* image, int B, int T, float* gu) {
   const char* base = static_cast<const char*>(image);
   const float* w_norm = reinterpret_cast<const float*>(base + U.image_offset(U.off[0], S));
   const void* w_head = base + U.image_offset(U.off[1], S);
-  const float* x = c.ckpt + (int64_t)D.L * c.M_max * d;
+  const float* x = c.ckpt_dev(D.L);
   float* d_head = gu + U.off[1];
 
   RUN(K_RMS_FWD, 0, (double)M * d * (4 + esz(S)), rmsnorm_fwd(S, x, w_norm, w.hf, w.rstdf, M, D.d, c.cfg.rms_eps, c.s_comp));

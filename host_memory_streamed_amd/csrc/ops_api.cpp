@@ -66,14 +66,14 @@ int mt_op_rope_fwd(int32_t out_dtype, const float* qkv, void* out, const float* 
                    int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd, void* stream) {
   int rc = rope_check(out_dtype, qkv, out, cos, sin, B, T, H, Hkv, hd);
   if (rc) return rc;
-  return hip_rc(rope(out_dtype, 0, qkv, out, cos, sin, B, T, H, Hkv, hd, st(stream)));
+  return hip_rc(rope(out_dtype, 0, qkv, out, cos, sin, 0, (int64_t)B * T, T, H, Hkv, hd, st(stream)));
 }
 
 int mt_op_rope_bwd(int32_t out_dtype, const float* dqkv, void* out, const float* cos, const float* sin,
                    int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd, void* stream) {
   int rc = rope_check(out_dtype, dqkv, out, cos, sin, B, T, H, Hkv, hd);
   if (rc) return rc;
-  return hip_rc(rope(out_dtype, 1, dqkv, out, cos, sin, B, T, H, Hkv, hd, st(stream)));
+  return hip_rc(rope(out_dtype, 1, dqkv, out, cos, sin, 0, (int64_t)B * T, T, H, Hkv, hd, st(stream)));
 }
 
 static int attn_check(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd) {
@@ -103,7 +103,18 @@ int mt_op_attn_bwd(int32_t dtype, const void* qkv, const float* o, const float* 
   if (rc) return rc;
   if ((int64_t)B * T == 0) return MT_OK;
   if (!qkv || !o || !dout || !lse || !dqkv || !ws) return MT_EINVAL;
-  return hip_rc(attn_bwd(dtype, qkv, o, dout, lse, dqkv, ws, B, T, H, Hkv, hd, st(stream)));
+  return hip_rc(attn_bwd(dtype, qkv, o, dout, lse, dqkv, MT_FP32, nullptr, nullptr, ws, B, T, H, Hkv, hd,
+                         st(stream)));
+}
+
+int mt_op_attn_bwd_rope(int32_t dtype, const void* qkv, const float* o, const float* dout, const float* lse,
+                        const float* cos, const float* sin, void* dqkv, void* ws, int32_t B, int32_t T,
+                        int32_t H, int32_t Hkv, int32_t hd, void* stream) {
+  int rc = attn_check(dtype, B, T, H, Hkv, hd);
+  if (rc) return rc;
+  if ((int64_t)B * T == 0) return MT_OK;
+  if (!qkv || !o || !dout || !lse || !cos || !sin || !dqkv || !ws) return MT_EINVAL;
+  return hip_rc(attn_bwd(dtype, qkv, o, dout, lse, dqkv, dtype, cos, sin, ws, B, T, H, Hkv, hd, st(stream)));
 }
 
 int mt_op_swiglu_fwd(int32_t out_dtype, const float* gu, void* act, int64_t M, int32_t F, void* stream) {

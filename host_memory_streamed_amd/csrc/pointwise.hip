@@ -137,10 +137,10 @@ __global__ void reduce_rows_kernel(const float* __restrict__ ws, float* __restri
 template <typename OutT>
 __global__ __launch_bounds__(256) void rope_kernel(const float* __restrict__ in, OutT* __restrict__ out,
                                                    const float* __restrict__ cosv,
-                                                   const float* __restrict__ sinv, int Tn, int H,
-                                                   int Hkv, int hd, int backward) {
+                                                   const float* __restrict__ sinv, int64_t row0,
+                                                   int Tn, int H, int Hkv, int hd, int backward) {
   const int64_t m = blockIdx.x;
-  const int t = (int)(m % Tn);
+  const int t = (int)((row0 + m) % Tn);
   const int half = hd / 2;
   const int rot = (H + Hkv) * half;       // rotated pairs
   const int width = (H + 2 * Hkv) * hd;
@@ -294,13 +294,13 @@ hipError_t rmsnorm_bwd(const float* x, const float* w, const float* rstd, const 
 }
 
 hipError_t rope(int out_dtype, int backward, const float* in, void* out, const float* cosv,
-                const float* sinv, int B, int Tn, int H, int Hkv, int hd, hipStream_t s) {
-  const int64_t M = (int64_t)B * Tn;
-  if (M == 0) return hipSuccess;
+                const float* sinv, int64_t row0, int64_t rows, int Tn, int H, int Hkv, int hd,
+                hipStream_t s) {
+  if (rows == 0) return hipSuccess;
   if (out_dtype == 1)
-    hipLaunchKernelGGL(rope_kernel<bf16>, dim3((unsigned)M), dim3(256), 0, s, in, (bf16*)out, cosv, sinv, Tn, H, Hkv, hd, backward);
+    hipLaunchKernelGGL(rope_kernel<bf16>, dim3((unsigned)rows), dim3(256), 0, s, in, (bf16*)out, cosv, sinv, row0, Tn, H, Hkv, hd, backward);
   else
-    hipLaunchKernelGGL(rope_kernel<float>, dim3((unsigned)M), dim3(256), 0, s, in, (float*)out, cosv, sinv, Tn, H, Hkv, hd, backward);
+    hipLaunchKernelGGL(rope_kernel<float>, dim3((unsigned)rows), dim3(256), 0, s, in, (float*)out, cosv, sinv, row0, Tn, H, Hkv, hd, backward);
   return hipGetLastError();
 }
 

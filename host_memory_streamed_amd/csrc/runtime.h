@@ -112,33 +112,37 @@ struct KTiming {
 
 // ----------------------------------------------------- device workspace ---
 
+// Full-batch buffers hold M = max_batch * max_seq rows; chunk buffers hold
+// `chunk` rows: the QKV projection output before its rotation and the MLP's
+// intermediates are produced and consumed chunk by chunk, so their size does
+// not grow with the sequence.
 struct Workspace {
-  // per-layer activations (M = max_batch * max_seq rows)
+  int64_t chunk = 0;        // token rows per chunk
+  // per-layer activations
   void* h = nullptr;        // RMSNorm out (S)
   float* rstd1 = nullptr;
   float* rstd2 = nullptr;
-  float* qkv_f = nullptr;   // projection out
+  float* qkv_f = nullptr;   // projection out [chunk]
   void* qkv_s = nullptr;    // rotated, cast
   float* o_f = nullptr;
   void* o_s = nullptr;      // bf16 mode: cast of o (fp32 mode: o_f)
   float* lse = nullptr;
   float* x1 = nullptr;
-  void* h2 = nullptr;
-  float* gu_f = nullptr;
-  void* act = nullptr;
+  void* h2 = nullptr;       // [chunk]
+  float* gu_f = nullptr;    // [chunk]
+  void* act = nullptr;      // [chunk]
   // backward
   float* g_f = nullptr;     // running residual gradient
   void* g_s = nullptr;      // its cast (fp32 mode: g_f)
-  float* dact_f = nullptr;
-  void* dgu_s = nullptr;
+  float* dact_f = nullptr;  // [chunk]
+  void* dgu_s = nullptr;    // [chunk]
   float* dh_f = nullptr;
-  float* do_f = nullptr;
-  float* dqkv_f = nullptr;
-  void* dqkv_s = nullptr;
+  float* do_f = nullptr;    // shares dh_f's memory (disjoint lifetimes)
+  void* dqkv_s = nullptr;   // gradient of the unrotated projection output
   void* attn_ws = nullptr;
   float* rms_ws = nullptr;
   // head
-  void* hf = nullptr;
+  void* hf = nullptr;       // shares h's memory
   float* rstdf = nullptr;
   float* logits = nullptr;  // [head_chunk, V]
   void* dz_s = nullptr;     // bf16 mode cast of dlogits (fp32 mode: logits)
@@ -177,10 +181,23 @@ struct Ctx {
   std::vector<float> token_loss; // last step
   std::vector<int32_t> prev_rows;  // embedding rows touched by the previous step
 
+  // Residual checkpoints x_0..x_L (x_i is layer i's input, x_L the head's).
+  // x_i with i >= ck_nh stays in a device slot from its forward to its
+  // backward use. The others pass through two device staging buffers (x_i in
+  // stage[i % 2]): x_1..x_{ck_nh-3} are copied to pinned host slabs after
+  // their forward and back before their backward, x_0 comes back from the
+  // gathered embedding rows, and the last two fit in the stages throughout.
+  int ck_nh = 0;                 // 0, or (host slabs) + 3
+  std::vector<float*> ck_host;   // slabs for x_1..x_{ck_nh-3}
+  float* stage[2] = {nullptr, nullptr};
+  float* ckpt_dev(int i) const {
+    return i >= ck_nh ? ckpt + (int64_t)(i - ck_nh) * M_max * D.d : stage[i & 1];
+  }
+
   // device
   std::vector<void*> buf;        // layer buffers
   float* gbuf[2] = {nullptr, nullptr};
-  float* ckpt = nullptr;         // (L+1) * M_max * d
+  float* ckpt = nullptr;         // device slots for x_{ck_nh}..x_L
   Workspace ws;
   std::vector<void*> dev_allocs;
   int64_t dev_bytes = 0;

@@ -67,8 +67,10 @@ double ms_since(std::chrono::steady_clock::time_point t0) {
 
 struct StepEvents {
   std::vector<hipEvent_t> loaded, freed, drained;
+  std::vector<hipEvent_t> ck_saved, ck_loaded;   // parked checkpoints, by index
   hipEvent_t x0 = nullptr, loss = nullptr, dx0 = nullptr, start = nullptr;
   std::vector<hipEvent_t> trace;   // timing events: per item 6 (load, compute, copy-out)
+  std::vector<hipEvent_t> ck_trace;   // per checkpoint index 4 (out, in)
 };
 
 int create_step_events(Ctx& c, StepEvents*& out);
@@ -86,9 +88,13 @@ int create_step_events(Ctx& c, StepEvents*& out) {
   e->loaded.resize(n);
   e->freed.resize(n);
   e->drained.resize(c.D.L + 1);
+  e->ck_saved.resize(c.D.L + 1);
+  e->ck_loaded.resize(c.D.L + 1);
   for (auto& ev : e->loaded) ok &= mk(ev, sync);
   for (auto& ev : e->freed) ok &= mk(ev, sync);
   for (auto& ev : e->drained) ok &= mk(ev, host);
+  for (auto& ev : e->ck_saved) ok &= mk(ev, sync);
+  for (auto& ev : e->ck_loaded) ok &= mk(ev, sync);
   ok &= mk(e->x0, sync);
   ok &= mk(e->loss, host);
   ok &= mk(e->dx0, host);
@@ -96,6 +102,8 @@ int create_step_events(Ctx& c, StepEvents*& out) {
   if (c.cfg.flags & MT_TRACE) {
     e->trace.resize((size_t)n * 6 + 4);
     for (auto& ev : e->trace) ok &= mk(ev, hipEventDefault);
+    e->ck_trace.resize((size_t)(c.D.L + 1) * 4);
+    for (auto& ev : e->ck_trace) ok &= mk(ev, hipEventDefault);
   }
   out = e;
   if (!ok) return set_error(&c, MT_EHIP, "hipEventCreate failed");
@@ -104,7 +112,7 @@ int create_step_events(Ctx& c, StepEvents*& out) {
 
 void destroy_step_events(StepEvents* e) {
   if (!e) return;
-  for (auto* v : {&e->loaded, &e->freed, &e->drained, &e->trace})
+  for (auto* v : {&e->loaded, &e->freed, &e->drained, &e->trace, &e->ck_saved, &e->ck_loaded, &e->ck_trace})
     for (auto ev : *v)
       if (ev) hipEventDestroy(ev);
   for (auto ev : {e->x0, e->loss, e->dx0, e->start})
@@ -179,7 +187,7 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
       std::memcpy(c.x0_host + r * d, emb.p + (int64_t)tokens[r] * d, (size_t)d * 4);
   });
   HIPCK(hipMemcpyAsync(c.ws.targets, c.tgt_host, (size_t)M * 4, hipMemcpyHostToDevice, c.s_in));
-  HIPCK(hipMemcpyAsync(c.ckpt, c.x0_host, (size_t)M * d * 4, hipMemcpyHostToDevice, c.s_in));
+  HIPCK(hipMemcpyAsync(c.ckpt_dev(0), c.x0_host, (size_t)M * d * 4, hipMemcpyHostToDevice, c.s_in));
   HIPCK(hipEventRecord(E.x0, c.s_in));
   double h2d_bytes = (double)M * 4 + (double)M * d * 4, d2h_bytes = 0;
 
@@ -276,6 +284,38 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
   int next_c = 0, next_g = 0, next_a = 0;
   bool loss_issued = false, loss_checked = false, dx0_issued = false, dx0_done = false;
 
+  // parked residual checkpoints (see Ctx::ckpt_dev): x_i, i in [1, kpark],
+  // goes to its host slab once the forward that wrote it has finished, and
+  // x_j, j in [0, kpark], comes back into stage[j % 2] once the last reader
+  // of x_{j+2} (which shares that stage) has finished
+  const int nh = c.ck_nh, kpark = nh ? nh - 3 : 0;
+  const size_t ck_bytes = (size_t)M * d * 4;
+  std::vector<char> save_issued(L + 1, 0), reload_issued(L + 1, 0);
+  int next_s = 1, next_r = kpark;
+  auto ck_ev = [&](int i, int slot) -> hipEvent_t { return E.ck_trace[(size_t)i * 4 + slot]; };
+  auto issue_save = [&](int i) -> int {
+    if (trace) HIPCK(hipEventRecord(ck_ev(i, 0), c.s_out));
+    HIPCK(hipMemcpyAsync(c.ck_host[i - 1], c.stage[i & 1], ck_bytes, hipMemcpyDeviceToHost, c.s_out));
+    if (trace) HIPCK(hipEventRecord(ck_ev(i, 1), c.s_out));
+    HIPCK(hipEventRecord(E.ck_saved[i], c.s_out));
+    save_issued[i] = 1;
+    d2h_bytes += (double)ck_bytes;
+    return MT_OK;
+  };
+  auto issue_reload = [&](int j) -> int {
+    const float* src = j == 0 ? c.x0_host : c.ck_host[j - 1];
+    if (trace) HIPCK(hipEventRecord(ck_ev(j, 2), c.s_in));
+    HIPCK(hipMemcpyAsync(c.stage[j & 1], src, ck_bytes, hipMemcpyHostToDevice, c.s_in));
+    if (trace) HIPCK(hipEventRecord(ck_ev(j, 3), c.s_in));
+    HIPCK(hipEventRecord(E.ck_loaded[j], c.s_in));
+    reload_issued[j] = 1;
+    h2d_bytes += (double)ck_bytes;
+    return MT_OK;
+  };
+  // forward of layer l overwrites stage[(l+1) % 2], which held x_{l-1}
+  auto fwd_needs_save = [&](int l) { return nh && l + 1 < nh && l - 1 >= 1 && l - 1 <= kpark; };
+  auto bwd_needs_reload = [&](int l) { return nh && l <= kpark; };
+
   auto issue_load = [&](int j) -> int {
     const Item& it = items[j];
     const Unit& u = it.phase == PH_HEAD ? c.head() : c.layer(it.unit);
@@ -294,6 +334,10 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
     const Item& it = items[i];
     if (it.load) HIPCK(hipStreamWaitEvent(c.s_comp, E.loaded[i], 0));
     if (i == 0) HIPCK(hipStreamWaitEvent(c.s_comp, E.x0, 0));
+    if (it.phase == PH_FWD && fwd_needs_save(it.unit))
+      HIPCK(hipStreamWaitEvent(c.s_comp, E.ck_saved[it.unit - 1], 0));
+    if (it.phase == PH_BWD && bwd_needs_reload(it.unit))
+      HIPCK(hipStreamWaitEvent(c.s_comp, E.ck_loaded[it.unit], 0));
     if (it.grad_k >= 2) HIPCK(hipStreamWaitEvent(c.s_comp, E.drained[it.grad_k - 2], 0));
     if (trace) HIPCK(hipEventRecord(trace_ev(i, 2), c.s_comp));
     float* gdev = it.grad_k >= 0 ? c.gbuf[it.grad_k % 2] : nullptr;
@@ -368,10 +412,33 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
       progress = true;
     }
     if (rc) break;
+    // parked checkpoints out, in order, once the forward that wrote them is done
+    while (next_s <= kpark) {
+      const int st = item_done(next_s - 1);
+      if (st < 0) { rc = st; break; }
+      if (!st) break;
+      if ((rc = issue_save(next_s))) break;
+      ++next_s;
+      progress = true;
+    }
+    if (rc) break;
+    // and back, in backward order, once the stage they return to is free
+    while (next_r >= 0 && nh) {
+      const int reader = next_r + 2 == L ? head_item : 2 * L - (next_r + 2);
+      const int st = item_done(reader);
+      if (st < 0) { rc = st; break; }
+      if (!st) break;
+      if ((rc = issue_reload(next_r))) break;
+      --next_r;
+      progress = true;
+    }
+    if (rc) break;
     // next compute item, once its weights and its gradient buffer are on their way
     if (next_c < n_items) {
       const Item& it = items[next_c];
-      const bool ready = (!it.load || load_issued[next_c]) && (it.grad_k < 2 || grad_issued[it.grad_k - 2]);
+      bool ready = (!it.load || load_issued[next_c]) && (it.grad_k < 2 || grad_issued[it.grad_k - 2]);
+      if (it.phase == PH_FWD && fwd_needs_save(it.unit)) ready = ready && save_issued[it.unit - 1];
+      if (it.phase == PH_BWD && bwd_needs_reload(it.unit)) ready = ready && reload_issued[it.unit];
       if (ready) {
         if ((rc = issue_compute(next_c))) break;
         ++next_c;
@@ -537,6 +604,16 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
         c.sched.push_back({MT_PH_GRAD, unit, it.grad_k % 2, 2, a2, b2});
         st.d2h_busy_ms += b2 - a2;
       }
+    }
+    for (int i = 1; i <= kpark; ++i) {
+      const double a = rel(ck_ev(i, 0)), b = rel(ck_ev(i, 1));
+      c.sched.push_back({MT_PH_CKPT_OUT, i, i & 1, 2, a, b});
+      st.d2h_busy_ms += b - a;
+    }
+    for (int j = 0; j <= kpark && nh; ++j) {
+      const double a = rel(ck_ev(j, 2)), b = rel(ck_ev(j, 3));
+      c.sched.push_back({MT_PH_CKPT_IN, j, j & 1, 0, a, b});
+      st.h2d_busy_ms += b - a;
     }
     // host AdamW entries on the same clock (device times are relative to the
     // start event, host times to the moment it completed)

@@ -20,7 +20,7 @@ MT_OK, MT_EINVAL, MT_EHOSTOOM, MT_EDEVOOM, MT_EHIP, MT_ENONFINITE, MT_ETIMEOUT, 
 MT_FP32, MT_BF16 = 0, 1
 MT_KEEP_GRADS, MT_KERNEL_TIMING, MT_TRACE = 1, 2, 4
 MT_GEMM_NT, MT_GEMM_NN, MT_GEMM_TN = 0, 1, 2
-PHASES = {0: "load", 1: "fwd", 2: "head", 3: "bwd", 4: "grad", 5: "adamw"}
+PHASES = {0: "load", 1: "fwd", 2: "head", 3: "bwd", 4: "grad", 5: "adamw", 6: "ckpt_out", 7: "ckpt_in"}
 UNIT_EMB, UNIT_HEAD = -1, -2
 
 
@@ -35,7 +35,8 @@ class ModelConfig(ctypes.Structure):
         "n_layers", "d_model", "n_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab", "max_batch",
         "max_seq", "compute_dtype", "n_layer_buffers", "host_threads")] + [
         ("flags", ctypes.c_uint32), ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float)] + [
-        (n, ctypes.c_double) for n in ("lr", "beta1", "beta2", "adam_eps", "weight_decay")]
+        (n, ctypes.c_double) for n in ("lr", "beta1", "beta2", "adam_eps", "weight_decay")] + [
+        ("chunk_rows", ctypes.c_int32), ("ckpt_host", ctypes.c_int32)]
 
 
 class DeviceEnv(ctypes.Structure):
@@ -80,6 +81,7 @@ _SIGS = {
     "mt_schedule": (ctypes.c_int, [_P, ctypes.POINTER(SchedEntry), _I32, ctypes.POINTER(_I32)]),
     "mt_trace_dump": (ctypes.c_int, [_P, ctypes.c_char_p]),
     "mt_device_bytes": (ctypes.c_int, [_P, ctypes.POINTER(_I64)]),
+    "mt_layout_info": (ctypes.c_int, [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
     "mt_last_error": (ctypes.c_char_p, [_P]),
     "mt_destroy": (None, [_P]),
     "mt_op_gemm": (ctypes.c_int, [_I32, _I32, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _P]),
@@ -94,6 +96,8 @@ _SIGS = {
     "mt_op_attn_fwd": (ctypes.c_int, [_I32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
     "mt_op_attn_bwd_ws_bytes": (_I64, [_I32, _I32, _I32, _I32, _I32]),
     "mt_op_attn_bwd": (ctypes.c_int, [_I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
+    "mt_op_attn_bwd_rope": (ctypes.c_int, [_I32, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                           _P]),
     "mt_op_swiglu_fwd": (ctypes.c_int, [_I32, _P, _P, _I64, _I32, _P]),
     "mt_op_swiglu_bwd": (ctypes.c_int, [_I32, _P, _P, _P, _I64, _I32, _P]),
     "mt_op_xent": (ctypes.c_int, [_I32, _P, _P, _P, _P, _I64, _I32, _F, _P]),
@@ -143,10 +147,10 @@ def _ptr(a) -> int:
 def make_config(n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab, max_batch, max_seq,
                 dtype=MT_FP32, n_layer_buffers=2, host_threads=0, flags=0, rms_eps=1e-5,
                 rope_base=10000.0, lr=1e-3, beta1=0.9, beta2=0.999, adam_eps=1e-8,
-                weight_decay=0.01) -> ModelConfig:
+                weight_decay=0.01, chunk_rows=0, ckpt_host=0) -> ModelConfig:
     return ModelConfig(n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab, max_batch,
                        max_seq, dtype, n_layer_buffers, host_threads, flags, rms_eps, rope_base, lr,
-                       beta1, beta2, adam_eps, weight_decay)
+                       beta1, beta2, adam_eps, weight_decay, chunk_rows, ckpt_host)
 
 
 def tensor_table(cfg: ModelConfig):
@@ -264,6 +268,12 @@ class Context:
         _check(lib().mt_device_bytes(self.h, ctypes.byref(b)), self.h)
         return b.value
 
+    def layout_info(self) -> dict:
+        """Token rows per chunk, parked (host) checkpoints, device checkpoint slots."""
+        ch, kh, kd = _I64(), _I32(), _I32()
+        _check(lib().mt_layout_info(self.h, ctypes.byref(ch), ctypes.byref(kh), ctypes.byref(kd)), self.h)
+        return {"chunk_rows": ch.value, "ckpt_host": kh.value, "ckpt_device_slots": kd.value}
+
 
 # ----------------------------------------------------------------- ops ---
 
@@ -317,6 +327,11 @@ def attn_bwd_ws_bytes(dtype, B, T, H, hd):
 def attn_bwd(dtype, qkv, o, dout, lse, dqkv, ws, B, T, H, Hkv, hd, stream=None):
     _check(lib().mt_op_attn_bwd(dtype, _ptr(qkv), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dqkv), _ptr(ws), B, T,
                                 H, Hkv, hd, _stream(stream)))
+
+
+def attn_bwd_rope(dtype, qkv, o, dout, lse, cos, sin, dqkv, ws, B, T, H, Hkv, hd, stream=None):
+    _check(lib().mt_op_attn_bwd_rope(dtype, _ptr(qkv), _ptr(o), _ptr(dout), _ptr(lse), _ptr(cos), _ptr(sin),
+                                     _ptr(dqkv), _ptr(ws), B, T, H, Hkv, hd, _stream(stream)))
 
 
 def swiglu_fwd(out_dtype, gu, act, M, F, stream=None):

@@ -79,6 +79,20 @@ typedef struct mt_model_cfg {
   float rms_eps;
   float rope_base;
   double lr, beta1, beta2, adam_eps, weight_decay;   /* AdamW hyperparameters */
+  /* Token rows per chunk of the QKV projection and the MLP (forward,
+   * recompute and backward): their intermediates are sized by the chunk, not
+   * the batch. 0 = automatic (the whole batch unless the MLP intermediates of
+   * max_batch * max_seq rows would exceed 4 GiB). Weight gradients sum the
+   * chunks in order, so a different chunk size changes their rounding. */
+  int32_t chunk_rows;
+  /* Residual checkpoints x_1..x_k (layer inputs) parked in pinned host memory
+   * between the forward and the backward instead of device memory; each
+   * parked one crosses the host link once each way. 0 = automatic (none
+   * unless the device cannot hold all L + 1 of them next to the workspace);
+   * k in [1, n_layers - 2] = exactly k. Parking k of them frees k + 1
+   * device slots (x_0 is re-sent from the gathered embedding rows). Results
+   * do not depend on k. */
+  int32_t ckpt_host;
 } mt_model_cfg;
 
 /* Optional streams for the three pipeline stages (hipStream_t values passed as
@@ -171,6 +185,8 @@ int mt_kernel_stats(mt_ctx* ctx, mt_kernel_stat* out, int32_t cap, int32_t* n);
 #define MT_PH_BWD 3       /* recompute + backward of a layer (stream 1) */
 #define MT_PH_GRAD 4      /* D2H of a unit's gradients (stream 2) */
 #define MT_PH_ADAMW 5     /* host AdamW of a unit (stream 3 = host) */
+#define MT_PH_CKPT_OUT 6  /* D2H of a parked residual checkpoint (stream 2; unit = its index) */
+#define MT_PH_CKPT_IN 7   /* H2D of a parked residual checkpoint (stream 0; unit = its index) */
 #define MT_UNIT_EMB -1
 #define MT_UNIT_HEAD -2
 typedef struct mt_sched_entry {
@@ -189,6 +205,10 @@ int mt_trace_dump(mt_ctx* ctx, const char* path);
 
 /* Device bytes the context holds (buffers, checkpoints, workspace). */
 int mt_device_bytes(mt_ctx* ctx, int64_t* bytes);
+
+/* Placement chosen at creation: token rows per chunk, residual checkpoints
+ * parked in host memory, and checkpoint slots held in device memory. */
+int mt_layout_info(mt_ctx* ctx, int64_t* chunk_rows, int32_t* ckpt_host, int32_t* ckpt_device_slots);
 
 /* Text of the last error on ctx (or of the last failed mt_create on this
  * thread when ctx is NULL). Never NULL. */

@@ -88,6 +88,17 @@ int mt_op_attn_bwd(int32_t dtype, const void* qkv, const float* o, const float* 
                    const float* lse, float* dqkv, void* ws, int32_t B, int32_t T, int32_t H,
                    int32_t Hkv, int32_t hd, void* stream);
 
+/* mt_op_attn_bwd followed by the RoPE backward, in one pass: the q and k
+ * gradients are rotated by the negative angle of their position (cos/sin as
+ * in mt_op_rope_bwd, [T][hd/2]) and every gradient is written as `dtype`
+ * into dqkv [M, (H+2Hkv) hd]: the gradient of the unrotated projection
+ * output. Same values as mt_op_attn_bwd then mt_op_rope_bwd(dtype, ...),
+ * without the fp32 intermediate. */
+int mt_op_attn_bwd_rope(int32_t dtype, const void* qkv, const float* o, const float* dout,
+                        const float* lse, const float* cos, const float* sin, void* dqkv,
+                        void* ws, int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
+                        void* stream);
+
 /* SwiGLU on gu [M, 2F] fp32 (gate = columns [0, F), up = [F, 2F)):
  * act = silu(gate) up as out_dtype [M, F]. Backward: from dact [M, F] fp32,
  * dgu [M, 2F] as out_dtype with dgate = dact up s (1 + gate (1 - s)),

@@ -55,8 +55,10 @@ def test_tensor_table_matches_oracle(name):
 
 @pytest.mark.parametrize("field,value", [("n_layers", 0), ("n_kv_heads", 3), ("head_dim", 48),
                                          ("compute_dtype", 7), ("n_layer_buffers", 1), ("d_model", 66),
-                                         ("max_seq", 0), ("flags", 1 << 10)])
+                                         ("max_seq", 0), ("flags", 1 << 10), ("chunk_rows", -1),
+                                         ("ckpt_host", -1), ("ckpt_host", 1)])
 def test_create_rejects_bad_config(field, value):
+    # two layers: no checkpoint can be parked (x_1..x_k with k <= n_layers - 2)
     c = mt.make_config(2, 64, 4, 4, 16, 172, 256, 2, 32)
     setattr(c, field, value)
     h = ctypes.c_void_p()

@@ -206,7 +206,13 @@ def test_attention_fwd_bwd(dtype, hd, B, T, H, Hkv):
     got = host(o).reshape(B, T, H, hd)
     np.testing.assert_allclose(host(lse), lref, rtol=1e-5, atol=1e-5)
     if dtype:
-        bf16_close(got, oref, tol=2e-3)
+        # the flash-block reading fixes where P is rounded; the fp32 logits it
+        # rounds differ from the oracle's in the last bits, which can flip an
+        # isolated rounding decision (one bf16 ulp of that P): nearly every
+        # element sits within 2e-3, every element within the bf16 bound
+        bf16_close(got, oref)
+        rms_o = np.sqrt(np.mean(oref ** 2))
+        assert np.mean(np.abs(got - oref) <= 2e-3 * (np.abs(oref) + rms_o)) >= 0.999
         assert np.linalg.norm(got - oplain) <= 2e-2 * np.linalg.norm(oplain)
         assert np.all(np.abs(host(oc).reshape(got.shape) - got) <= 2.0 ** -8 * np.abs(got) + 1e-30)
     else:
@@ -247,6 +253,124 @@ def test_attention_full_14b_shape_sampled_rows(B, T, H, Hkv):
         ref = (O.bf16(p / p.sum()) @ v[0, :t + 1, h // (H // Hkv)])
         assert abs(gl[0, h, t] - (mx + math.log(p.sum()))) < 1e-4
         bf16_close(got[0, t, h], ref)
+
+
+@pytest.mark.parametrize("dtype,hd", [(mt.MT_FP32, 16), (mt.MT_FP32, 32), (mt.MT_FP32, 128), (mt.MT_BF16, 64),
+                                      (mt.MT_BF16, 128)])
+@pytest.mark.parametrize("B,T,H,Hkv", [(2, 100, 4, 2), (1, 257, 8, 1)])
+def test_attention_bwd_with_rope(dtype, hd, B, T, H, Hkv):
+    """The fused backward (attention, then the rotation's backward, written in
+    the compute dtype) against the oracle's attention backward followed by
+    its RoPE backward, and against the two separate GPU passes."""
+    tdt = torch.bfloat16 if dtype else torch.float32
+    qkv = _attn_inputs(B, T, H, Hkv, hd, dtype)
+    q, k, v = _split(qkv, B, T, H, Hkv, hd)
+    prec = O.decoder._Prec("bf16-flash64" if dtype else "fp32")
+    M = B * T
+    qd = dev(qkv, tdt)
+    o = torch.empty(M, H * hd, device=DEV)
+    oc = torch.empty(M, H * hd, device=DEV, dtype=tdt) if dtype else None
+    lse = torch.empty(B, H, T, device=DEV)
+    mt.attn_fwd(dtype, qd, o, oc, lse, B, T, H, Hkv, hd)
+    do = RNG.standard_normal((B, T, H, hd))
+    dod = dev(do.reshape(M, H * hd))
+    c32, s32 = mt.rope_table(T, hd, 10000.0)
+    cd, sd = dev(c32), dev(s32)
+    ws = torch.empty(mt.attn_bwd_ws_bytes(dtype, B, T, H, hd), device=DEV, dtype=torch.uint8)
+    W = (H + 2 * Hkv) * hd
+    fused = torch.full((M, W), float("nan"), device=DEV, dtype=tdt)
+    mt.attn_bwd_rope(dtype, qd, o, dod, lse, cd, sd, fused, ws, B, T, H, Hkv, hd)
+    # two passes: fp32 gradients of the rotated operands, then the rotation's backward
+    raw = torch.full((M, W), float("nan"), device=DEV)
+    mt.attn_bwd(dtype, qd, o, dod, lse, raw, ws, B, T, H, Hkv, hd)
+    two = torch.full((M, W), float("nan"), device=DEV, dtype=tdt)
+    mt.rope(dtype, 1, raw, two, cd, sd, B, T, H, Hkv, hd)
+    got, sep = host(fused), host(two)
+    if dtype:
+        assert np.all(np.abs(got - sep) <= 2.0 ** -7 * np.abs(sep) + 1e-30)
+    else:
+        np.testing.assert_allclose(got, sep, rtol=1e-6, atol=1e-7 * np.max(np.abs(sep)))
+    # oracle: attention backward from the GPU's forward output, then RoPE backward
+    dqr, dkr, dvr = O.attention_bwd(q, k, v, host(o).reshape(B, T, H, hd), host(lse), do, prec)
+    cos, sin = O.rope_tables(T, hd, 10000.0)
+    dq, dk, dv = _split(got.astype(np.float32), B, T, H, Hkv, hd)
+    rms = lambda a: np.sqrt(np.mean(np.square(a)))
+    term_qk = rms(do) * rms(v) * rms(k) * math.sqrt(hd)
+    for g, r, term in ((dq, O.rope_bwd(dqr, cos, sin), term_qk), (dk, O.rope_bwd(dkr, cos, sin), term_qk),
+                       (dv, dvr, rms(do))):
+        if dtype:
+            bf16_close(g, r, floor=1e-2 * term)
+        else:
+            np.testing.assert_allclose(g, r, rtol=1e-4, atol=1e-4 * rms(r) + 1e-5 * term)
+
+
+def test_attention_512k_tokens_sampled():
+    """Causal attention over one 524288-token sequence (the long-context
+    workload's length; 2 heads of dim 128 keep the check to seconds): forward
+    rows and the dq rows of sampled queries, and dk/dv of the last 64-key
+    tile, against float64 computed row by row; plus, over the whole length,
+    sum_t dv[t] = sum_q dO[q] (each probability row sums to one)."""
+    T, H, Hkv, hd, dtype = 524288, 2, 2, 128, mt.MT_BF16
+    rng = np.random.default_rng(524288)
+    W = (H + 2 * Hkv) * hd
+    qkv = O.bf16(rng.standard_normal((T, W), dtype=np.float32)).astype(np.float32)
+    do = rng.standard_normal((T, H * hd), dtype=np.float32)
+    qd = dev(qkv, torch.bfloat16)
+    o = torch.empty(T, H * hd, device=DEV)
+    lse = torch.empty(1, H, T, device=DEV)
+    mt.attn_fwd(dtype, qd, o, None, lse, 1, T, H, Hkv, hd)
+    dqkv = torch.empty(T, W, device=DEV)
+    ws = torch.empty(mt.attn_bwd_ws_bytes(dtype, 1, T, H, hd), device=DEV, dtype=torch.uint8)
+    mt.attn_bwd(dtype, qd, o, dev(do), lse, dqkv, ws, 1, T, H, Hkv, hd)
+    og, lg = host(o).reshape(T, H, hd), host(lse)[0]
+    g = host(dqkv).reshape(T, H + 2 * Hkv, hd)
+    del qd, dqkv, ws
+    Q = qkv[:, :H * hd].reshape(T, H, hd).astype(np.float64)
+    K = qkv[:, H * hd:(H + Hkv) * hd].reshape(T, Hkv, hd).astype(np.float64)
+    V = qkv[:, (H + Hkv) * hd:].reshape(T, Hkv, hd).astype(np.float64)
+    dO = do.reshape(T, H, hd).astype(np.float64)
+    dOb = O.bf16(dO)
+    sc = 1.0 / math.sqrt(hd)
+    # sampled query rows: o, lse and dq
+    rows = [0, 1, 63, 64, 4095, T // 2 + 17, T - 65, T - 1] + [int(x) for x in rng.integers(0, T, 4)]
+    for t in rows:
+        for h in range(H):
+            kv = h // (H // Hkv)
+            s = K[:t + 1, kv] @ Q[t, h] * sc
+            m = s.max()
+            p = np.exp(s - m)
+            P = p / p.sum()
+            assert abs(lg[h, t] - (m + math.log(p.sum()))) < 1e-4, (t, h)
+            bf16_close(og[t, h], P @ V[:t + 1, kv])
+            dP = V[:t + 1, kv] @ dOb[t, h]
+            dS = P * (dP - dO[t, h] @ og[t, h])
+            ref = sc * (dS @ K[:t + 1, kv])
+            bf16_close(g[t, h], ref, floor=1e-2 * np.sqrt(np.mean(ref ** 2)))
+    # dk, dv of the last 64 keys: only the last 64 queries reach them
+    q0 = T - 64
+    for kv in range(Hkv):
+        dk = np.zeros((64, hd))
+        dv = np.zeros((64, hd))
+        for h in range(kv * (H // Hkv), (kv + 1) * (H // Hkv)):
+            S = Q[q0:, h] @ K[:, kv].T * sc                       # [64, T]
+            S[np.arange(64)[:, None] < (np.arange(T)[None, :] - q0)] = -np.inf
+            m = S.max(axis=1, keepdims=True)
+            Pf = np.exp(S - m)
+            Pf /= Pf.sum(axis=1, keepdims=True)
+            P = Pf[:, q0:]                                          # [64 q, 64 k]
+            D = np.sum(dO[q0:, h] * og[q0:, h], axis=1)
+            dS = P * (dOb[q0:, h] @ V[q0:, kv].T - D[:, None])
+            dk += sc * dS.T @ Q[q0:, h]
+            dv += P.T @ dOb[q0:, h]
+        bf16_close(g[q0:, H + kv], dk, floor=1e-2 * np.sqrt(np.mean(dk ** 2)))
+        bf16_close(g[q0:, H + Hkv + kv], dv, floor=1e-2 * np.sqrt(np.mean(dv ** 2)))
+    # whole length: sum over keys of dv equals the sum of the (rounded) dO over the group's queries
+    for kv in range(Hkv):
+        grp = slice(kv * (H // Hkv), (kv + 1) * (H // Hkv))
+        lhs = g[:, H + Hkv + kv].sum(axis=0)
+        rhs = dOb[:, grp].sum(axis=(0, 1))
+        scale = np.sqrt(np.sum(dOb[:, grp] ** 2) / hd)
+        assert np.max(np.abs(lhs - rhs)) <= 2e-3 * scale, np.max(np.abs(lhs - rhs)) / scale
 
 
 # ------------------------------------------------------- SwiGLU / CE / cast ---

@@ -3,8 +3,11 @@
 fp32 mode: loss, per-token losses, every gradient, updated parameters and
 AdamW moments within rtol 1e-4 / atol 1e-5 of the oracle. bf16-compute mode:
 every tensor within rtol 2e-2 normwise (||gpu - ref|| <= 2e-2 ||ref||) of the
-oracle under both readings of where attention probabilities are rounded, and
-elementwise within 2e-2 |ref| + 0.2 rms(ref) of the flash-block reading. Two
+oracle under the flash-block reading of where attention probabilities are
+rounded (the one the kernels implement) and elementwise within
+2e-2 |ref| + 0.2 rms(row) of it (all but 0.1% of the elements; every element
+within 2e-2 |ref| + 0.5 rms(row)); against the normalised-P reading within
+2e-2 plus the distance between the two readings themselves. Two
 bf16 implementations that differ in any one rounding decision diverge by a
 cascade of flipped decisions downstream, so individual elements formed by
 heavy cancellation carry noise of a few percent of the tensor's rms; the
@@ -29,12 +32,13 @@ def init_params(cfg, seed, std=0.02):
     return [synth.init_tensor(seed, i, shp, gain, std) for i, (_, shp, gain) in enumerate(O.tensor_table(cfg))]
 
 
-def make_ctx(cfg, B, T, params, dtype=mt.MT_FP32, resident=False, flags=mt.MT_KEEP_GRADS, threads=8):
+def make_ctx(cfg, B, T, params, dtype=mt.MT_FP32, resident=False, flags=mt.MT_KEEP_GRADS, threads=8,
+             chunk_rows=0, ckpt_host=0):
     c = mt.make_config(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn_dim,
                        cfg.vocab, B, T, dtype=dtype, n_layer_buffers=(cfg.n_layers + 1 if resident else 2),
                        host_threads=threads, flags=flags, rms_eps=cfg.rms_eps, rope_base=cfg.rope_base,
                        lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, adam_eps=cfg.adam_eps,
-                       weight_decay=cfg.weight_decay)
+                       weight_decay=cfg.weight_decay, chunk_rows=chunk_rows, ckpt_host=ckpt_host)
     return mt.Context(c, params)
 
 
@@ -42,18 +46,34 @@ def check_fp32(name, got, ref, rtol=1e-4, atol=1e-5):
     np.testing.assert_allclose(got, ref, rtol=rtol, atol=atol, err_msg=name)
 
 
-def check_bf16(name, got, ref, tol=2e-2, rms_frac=0.2):
+def check_bf16(name, got, ref, tol=2e-2, rms_frac=0.2, hard_frac=0.5, spill=1e-3):
     check_normwise(name, got, ref, tol)
-    # elementwise guard on each row's own scale (a row is one output unit)
+    # elementwise guard on each row's own scale (a row is one output unit):
+    # at most a fraction `spill` of the elements beyond rms_frac rms(row), none
+    # beyond hard_frac rms(row). The two oracle readings of where P is rounded
+    # differ on query/key gradients by up to ~0.06% of elements beyond
+    # 0.2 rms(row) and at most ~0.3 rms(row); a localised bug (a wrong tile,
+    # row, tail or head) moves whole blocks by O(rms).
     r2 = ref.reshape(ref.shape[0], -1) if ref.ndim > 1 else ref.reshape(1, -1)
     rms = np.sqrt(np.mean(np.square(r2), axis=1, keepdims=True))
-    bad = np.abs(got.reshape(r2.shape) - r2) > tol * np.abs(r2) + rms_frac * rms
-    assert not bad.any(), f"{name}: {bad.sum()} elements beyond 2e-2|ref| + {rms_frac} rms(row)"
+    dev_ = np.abs(got.reshape(r2.shape) - r2) - tol * np.abs(r2)
+    n_soft = int((dev_ > rms_frac * rms).sum())
+    assert n_soft <= spill * r2.size, f"{name}: {n_soft} elements beyond 2e-2|ref| + {rms_frac} rms(row)"
+    n_hard = int((dev_ > hard_frac * rms).sum())
+    assert n_hard == 0, f"{name}: {n_hard} elements beyond 2e-2|ref| + {hard_frac} rms(row)"
 
 
 def check_normwise(name, got, ref, tol=2e-2):
     n = np.linalg.norm(ref)
     assert np.linalg.norm(got - ref) <= tol * n + 1e-30, f"{name}: normwise {np.linalg.norm(got - ref) / n:.3g}"
+
+
+def check_other_reading(name, got, plain, flash):
+    """Against the normalised-P reading, allowing for the distance between the
+    two readings of where P is rounded (the oracle's own flash-block and
+    normalised results differ by up to ~2% normwise on sensitive tensors)."""
+    gap = np.linalg.norm(flash - plain) / (np.linalg.norm(plain) + 1e-300)
+    check_normwise(name, got, plain, 2e-2 + gap)
 
 
 def compare_step(ctx, res, cfg, mode, prev, plain=None, tokens=None):
@@ -75,11 +95,12 @@ def compare_step(ctx, res, cfg, mode, prev, plain=None, tokens=None):
             assert not g[other].any(), "embedding rows outside the batch must have zero gradient"
             chk(f"grad {name}", g[rows], res.grads[i][rows])
             if plain is not None:
-                check_normwise(f"grad {name} (normalised-P reading)", g[rows], plain.grads[i][rows])
+                check_other_reading(f"grad {name} (normalised-P reading)", g[rows], plain.grads[i][rows],
+                                    res.grads[i][rows])
         else:
             chk(f"grad {name}", g, res.grads[i])
             if plain is not None:
-                check_normwise(f"grad {name} (normalised-P reading)", g, plain.grads[i])
+                check_other_reading(f"grad {name} (normalised-P reading)", g, plain.grads[i], res.grads[i])
         p = ctx.params(i)
         m, v, t = ctx.opt_state(i)
         assert t == res.t == t0 + 1
@@ -111,11 +132,11 @@ def compare_step(ctx, res, cfg, mode, prev, plain=None, tokens=None):
             check_fp32(f"v {name}", v, rv, rtol=2e-4, atol=1e-12)
 
 
-def run_parity(cfg, B, T, mode, steps=1, seed=0, std=0.02):
+def run_parity(cfg, B, T, mode, steps=1, seed=0, std=0.02, **ctx_kw):
     params = init_params(cfg, seed, std)
     zeros = [np.zeros_like(p) for p in params]
     dtype = mt.MT_BF16 if mode == "bf16" else mt.MT_FP32
-    with make_ctx(cfg, B, T, params, dtype=dtype) as ctx:
+    with make_ctx(cfg, B, T, params, dtype=dtype, **ctx_kw) as ctx:
         P, Mm, Vv, t = params, zeros, zeros, 0
         for s in range(steps):
             tokens, targets = synth.token_batch(seed + 10 * s, B, T, cfg.vocab)
@@ -173,6 +194,74 @@ def test_14b_layer_shape_one_layer_bf16():
     # per-layer and head shape of the 14B workload (GQA 40/8, vocab 152064), 1 layer
     cfg, _, _ = shape("14b", n_layers=1)
     run_parity(cfg, 1, 64, "bf16", seed=13)
+
+
+def test_120b_layer_shape_one_layer_bf16():
+    # per-layer shape of the 120B-shaped workload (d 10240, GQA 80/8, FFN 28672,
+    # 1.11B parameters per layer), 1 layer; the vocabulary is cut to 2048 so
+    # that two fp64 oracle steps fit in host memory (the head is not part of
+    # the per-layer shape; its full-size product runs in the 14B test)
+    cfg, _, _ = shape("120b", n_layers=1)
+    cfg = O.Config(**{**cfg.__dict__, "vocab": 2048})
+    run_parity(cfg, 1, 64, "bf16", seed=17)
+
+
+@pytest.mark.parametrize("mode", ["fp32", "bf16"])
+def test_token_chunks_and_parked_checkpoints(mode):
+    # 2 x 48 tokens in chunks of 40 rows (40, 40, 16) for the QKV projection
+    # and the MLP; 3 of the 5 layers' input checkpoints parked in host memory
+    cfg = O.Config(5, 128, 2, 1, 64, 200, 300)
+    run_parity(cfg, 2, 48, mode, steps=2, seed=19, std=0.05, chunk_rows=40, ckpt_host=3)
+
+
+def _run_steps(cfg, B, T, dtype, steps=2, **kw):
+    params = init_params(cfg, 23, 0.05)
+    out = []
+    with make_ctx(cfg, B, T, params, dtype=dtype, flags=mt.MT_KEEP_GRADS | mt.MT_TRACE, **kw) as ctx:
+        for s in range(steps):
+            tokens, targets = synth.token_batch(23 + s, B, T, cfg.vocab)
+            out.append(ctx.train_step(tokens, targets))
+        n = len(params)
+        out += [ctx.params(i).copy() for i in range(n)] + [ctx.grads(i).copy() for i in range(n)]
+        return out, ctx.layout_info(), ctx.schedule()
+
+
+@pytest.mark.parametrize("dtype", [mt.MT_FP32, mt.MT_BF16])
+def test_parked_checkpoints_are_bitwise_neutral(dtype):
+    """Where a residual checkpoint waits between forward and backward does not
+    change any result: every parking depth gives the same bits as none. The
+    schedule shows each parked checkpoint going out once and coming back once,
+    x_0 from the gathered embedding rows."""
+    L = 6
+    cfg = O.Config(L, 128, 2, 1, 64, 200, 300)
+    ref, info, _ = _run_steps(cfg, 2, 40, dtype, chunk_rows=32)
+    assert info == {"chunk_rows": 32, "ckpt_host": 0, "ckpt_device_slots": L + 1}
+    for k in (1, 2, L - 2):
+        got, info, sched = _run_steps(cfg, 2, 40, dtype, chunk_rows=32, ckpt_host=k)
+        assert info == {"chunk_rows": 32, "ckpt_host": k, "ckpt_device_slots": L - k}
+        for a, b in zip(ref, got):
+            assert np.array_equal(np.asarray(a), np.asarray(b))
+        outs = sorted(e["unit"] for e in sched if e["phase"] == "ckpt_out")
+        ins = sorted(e["unit"] for e in sched if e["phase"] == "ckpt_in")
+        assert outs == list(range(1, k + 1)) and ins == list(range(0, k + 1))
+
+
+def test_token_chunks_change_only_rounding():
+    """Chunking the projections changes only the order in which the weight
+    gradients add up the chunks."""
+    cfg = O.Config(3, 128, 2, 1, 64, 200, 300)
+    ref, info0, _ = _run_steps(cfg, 2, 40, mt.MT_FP32, steps=1)
+    got, info1, _ = _run_steps(cfg, 2, 40, mt.MT_FP32, steps=1, chunk_rows=24)
+    assert info0["chunk_rows"] == 80 and info1["chunk_rows"] == 24
+    assert abs(ref[0] - got[0]) <= 1e-6 * abs(ref[0])
+    n = (len(ref) - 1) // 2
+    for i in range(n):
+        pa, pb, ga, gb = ref[1 + i], got[1 + i], ref[1 + n + i], got[1 + n + i]
+        np.testing.assert_allclose(gb, ga, rtol=1e-5, atol=1e-7 * (np.max(np.abs(ga)) + 1e-30))
+        # the first AdamW step moves p by about lr g / (|g| + eps): only where
+        # |g| >> eps does a gradient within rounding give an update within rounding
+        ok = np.abs(ga) >= 1e-5
+        np.testing.assert_allclose(pb[ok], pa[ok], rtol=1e-5, atol=1e-9)
 
 
 @pytest.mark.parametrize("dtype", [mt.MT_FP32, mt.MT_BF16])
