@@ -34,14 +34,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_context(w, dtype, seed, flags, host_threads=0):
+def build_context(w, dtype, seed, flags, host_threads=0, chunk_rows=0, ckpt_host=0):
     from host_memory_streamed_amd import mt, synth
     cfg = mt.make_config(w.n_layers, w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn_dim, w.vocab,
                          w.batch, w.seq, dtype=dtype, n_layer_buffers=2, host_threads=host_threads,
-                         flags=flags)
+                         flags=flags, chunk_rows=chunk_rows, ckpt_host=ckpt_host)
     t0 = time.perf_counter()
     ctx = mt.Context(cfg)
-    log(f"context created in {time.perf_counter() - t0:.1f}s; device bytes {ctx.device_bytes() / 1e9:.2f} GB")
+    log(f"context created in {time.perf_counter() - t0:.1f}s; device bytes {ctx.device_bytes() / 1e9:.2f} GB; "
+        f"{ctx.layout_info()}")
     t0 = time.perf_counter()
     biggest = max(int(np.prod(s)) for _, s in ctx.table)
     buf = np.empty(biggest, dtype=np.float32)
@@ -121,6 +122,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace", default=None, help="write the last step's schedule as Chrome JSON")
+    ap.add_argument("--chunk-rows", type=int, default=0, help="token rows per projection/MLP chunk (0 = auto)")
+    ap.add_argument("--ckpt-host", type=int, default=0, help="checkpoints parked in host memory (0 = auto)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -139,7 +142,8 @@ def main():
         w = mt.Workload(**{**w.__dict__, "n_layers": args.layers})
     dtype = mt.MT_BF16 if args.dtype == "bf16" else mt.MT_FP32
     flags = mt.MT_KERNEL_TIMING | mt.MT_TRACE
-    ctx = build_context(w, dtype, args.seed, flags)
+    ctx = build_context(w, dtype, args.seed, flags, chunk_rows=args.chunk_rows, ckpt_host=args.ckpt_host)
+    layout = ctx.layout_info()
     tokens, targets = synth.token_batch(args.seed, w.batch, w.seq, w.vocab)
     M = w.batch * w.seq
 
@@ -189,7 +193,8 @@ def main():
     kpeak = peak if gemm else PEAK_HBM
     gpu_ms = sum(v["ms"] for v in kstats.values()) / args.steps
     out = {
-        "metric": "training tokens/sec, MFU and host-link GB/s for 14B-shaped streamed step",
+        "metric": ("training tokens/sec, MFU and host-link GB/s for 14B-shaped streamed step" if w.name == "14b"
+                   else f"training tokens/sec, MFU and host-link GB/s for {w.name}-shaped streamed step"),
         "value": round(tok_s, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -205,7 +210,7 @@ def main():
                    "n_layers": w.n_layers, "d_model": w.d_model, "n_heads": w.n_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ffn_dim": w.ffn_dim,
                    "vocab": w.vocab, "global_batch": w.batch, "seq_len": w.seq,
-                   "master": "fp32 p/m/v in host memory", "parallelism": "none (1 GPU)"},
+                   "master": "fp32 p/m/v in host memory", "parallelism": "none (1 GPU)", **layout},
         "mfu": round(mfu, 4),
         "host_link": {
             "h2d_GBps_step": round(h2d / (ms * 1e-3) / 1e9, 2),
