@@ -610,10 +610,7 @@ bool attn_supported(int dtype, int hd) {
 
 hipError_t attn_fwd(int dtype, const void* qkv, float* o, void* o_cast, float* lse, int B, int Tn,
                     int H, int Hkv, int hd, hipStream_t s) {
-  if (dtype == 1) {
-    if (hd == 64) return fwd_launch<bf16, 64>(qkv, o, o_cast, lse, B, Tn, H, Hkv, s);
-    return fwd_launch<bf16, 128>(qkv, o, o_cast, lse, B, Tn, H, Hkv, s);
-  }
+  if (dtype == 1) return attn_fwd_bf16(qkv, o, o_cast, lse, B, Tn, H, Hkv, hd, s);
   switch (hd) {
     case 16: return fwd_launch<float, 16>(qkv, o, o_cast, lse, B, Tn, H, Hkv, s);
     case 32: return fwd_launch<float, 32>(qkv, o, o_cast, lse, B, Tn, H, Hkv, s);

@@ -1,0 +1,266 @@
+// bf16 causal flash-attention forward on the gfx950 32x32x16 matrix cores.
+//
+// Same operation and rounding points as the generic forward in attention.hip
+// (scaled, masked scores in fp32; online softmax in the log2 domain with one
+// running maximum per 64-key tile; P rounded to bf16 before P.V; fp32 output,
+// optional bf16 copy, natural-log logsumexp), laid out for throughput:
+//
+//  - a workgroup owns 128 queries of one head (4 waves x 32 queries), so each
+//    K/V tile brought on chip serves 128 queries;
+//  - 64-key K and V tiles are double buffered in LDS: the global loads of
+//    tile k+1 are in flight while tile k is consumed, one barrier per tile;
+//  - S^T = K Q^T runs with K rows from LDS as the A operand and the wave's 32
+//    queries held in registers as B; O^T += V^T P^T takes P^T straight from
+//    the S^T accumulator (the k-slots of each 16-key step are ordered as the
+//    accumulator holds them) and V^T from the row-major V tile through the
+//    LDS transpose read, two 4-key reads per step;
+//  - key sub-tiles that lie wholly above a wave's last query are skipped;
+//  - work items are numbered so that the query blocks of one head run on the
+//    same XCD (workgroup i goes to XCD i % 8) and share its L2, longest
+//    blocks first.
+#include "dev_common.h"
+#include "kernels.h"
+
+namespace mt {
+namespace {
+
+constexpr float F_LOG2E = 1.4426950408889634f;
+constexpr float F_LN2 = 0.6931471805599453f;
+constexpr int FQ = 128;   // queries per workgroup
+constexpr int FK = 64;    // keys per tile
+constexpr int FT = 256;   // threads
+
+template <int HD>
+struct F32Cfg {
+  static constexpr int P = HD + 8;          // LDS row pitch in elements (16-byte row skew)
+  static constexpr int VPR = HD / 8;        // 16-byte vectors per row
+  static constexpr int NV = FK * VPR / FT;  // vectors per thread per matrix per tile
+  static constexpr int NS = HD / 16;        // 16-wide hd steps of Q K^T
+  static constexpr int NH = HD / 32;        // 32-row hd sub-tiles of O^T
+};
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// One 64-row tile of K or V: NV 16-byte vectors per thread, rows past the end
+// of the sequence read as zero.
+template <int HD>
+struct TileRegs {
+  u32x4 v[F32Cfg<HD>::NV];
+  __device__ __forceinline__ void fetch(const bf16* __restrict__ src, int64_t ld, int k0, int Tn, int tid) {
+    typedef F32Cfg<HD> C;
+#pragma unroll
+    for (int j = 0; j < C::NV; ++j) {
+      const int u = tid + FT * j;
+      const int row = u / C::VPR, col = (u % C::VPR) * 8;
+      const int key = min(k0 + row, Tn - 1);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src + (int64_t)key * ld + col);
+      v[j] = k0 + row < Tn ? x : u32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(bf16* dst, int tid) const {
+    typedef F32Cfg<HD> C;
+#pragma unroll
+    for (int j = 0; j < C::NV; ++j) {
+      const int u = tid + FT * j;
+      const int row = u / C::VPR, col = (u % C::VPR) * 8;
+      *reinterpret_cast<u32x4*>(dst + row * C::P + col) = v[j];
+    }
+  }
+};
+
+template <int HD>
+__global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __restrict__ qkv,
+                                                             float* __restrict__ o,
+                                                             bf16* __restrict__ o_cast,
+                                                             float* __restrict__ lse, int Tn, int H,
+                                                             int Hkv, int nq, int xcd_groups) {
+  typedef F32Cfg<HD> C;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][FK * C::P];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][FK * C::P];
+
+  // work item: (head, query block), longest blocks first
+  const int id = blockIdx.x;
+  int h, qb;
+  if (xcd_groups) {
+    const int per = (nq * H) >> 3;
+    const int item = (id & 7) * per + (id >> 3);
+    h = item / nq;
+    qb = nq - 1 - item % nq;
+  } else {
+    h = id % H;
+    qb = nq - 1 - id / H;
+  }
+  const int b = blockIdx.z;
+  const int kvh = h / (H / Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c = lane & 31, G = lane >> 5, k16 = lane >> 4, i16 = lane & 15;
+  const int64_t ld = (int64_t)(H + 2 * Hkv) * HD;
+  const bf16* base = qkv + (int64_t)b * Tn * ld;
+  const bf16* Kg = base + (H + kvh) * HD;
+  const bf16* Vg = base + (H + Hkv + kvh) * HD;
+
+  const int wq0 = qb * FQ + w * 32;   // the wave's first query
+  const int q = wq0 + c;              // this lane's query
+  bf16x8 qf[C::NS];
+  {
+    const bf16* qrow = base + (int64_t)min(q, Tn - 1) * ld + h * HD + G * 8;
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + s * 16);
+      qf[s] = q < Tn ? x : bf16x8{};
+    }
+  }
+
+  const float sl2 = F_LOG2E / sqrtf((float)HD);
+  float m = -INFINITY, l = 0.f;
+  floatx16 oacc[C::NH];
+#pragma unroll
+  for (int i = 0; i < C::NH; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+
+  const int q_hi = min(Tn, qb * FQ + FQ);   // end of the block's valid queries
+  const int n_kt = (q_hi - 1) / FK + 1;
+
+  TileRegs<HD> kr, vr;
+  kr.fetch(Kg, ld, 0, Tn, tid);
+  vr.fetch(Vg, ld, 0, Tn, tid);
+  kr.store(Ks[0], tid);
+  vr.store(Vs[0], tid);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    const int k0 = kt * FK;
+    const bool more = kt + 1 < n_kt;
+    if (more) {
+      kr.fetch(Kg, ld, k0 + FK, Tn, tid);
+      vr.fetch(Vg, ld, k0 + FK, Tn, tid);
+    }
+    const bf16* Kb = Ks[buf];
+    const bf16* Vb = Vs[buf];
+
+    // scores of the two 32-key sub-tiles (wave-uniform skip above the diagonal)
+    floatx16 s[2];
+    bool live[2];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int kb = k0 + 32 * st;
+      live[st] = kb <= wq0 + 31;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[st][r] = 0.f;
+      if (live[st]) {
+        const bf16* arow = Kb + (32 * st + c) * C::P + G * 8;
+#pragma unroll
+        for (int ss = 0; ss < C::NS; ++ss) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + ss * 16);
+          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ss], s[st], 0, 0, 0);
+        }
+        const bool full = kb + 31 <= wq0;   // every key visible to every query of the wave
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + (r >> 2) * 8 + G * 4 + (r & 3);
+          const float v = (full || key <= q) ? s[st][r] * sl2 : -INFINITY;
+          s[st][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = exp2f(m - m_new);
+    float rs = 0.f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = live[st] ? exp2f(s[st][r] - m_new) : 0.f;
+        s[st][r] = p;
+        rs += p;
+      }
+    rs += __shfl_xor(rs, 32, WAVE);
+    l = l * alpha + rs;
+    m = m_new;
+    // P^T operands: 16-key step kk = 2*st + j takes accumulator slots 8j..8j+7
+    bf16x8 pb0, pb1, pb2, pb3;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pb0[e] = to_bf16(s[0][e]);
+      pb1[e] = to_bf16(s[0][8 + e]);
+      pb2[e] = to_bf16(s[1][e]);
+      pb3[e] = to_bf16(s[1][8 + e]);
+    }
+
+    // O^T += V^T P^T over four 16-key steps
+#pragma unroll
+    for (int ht = 0; ht < C::NH; ++ht) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[ht][r] *= alpha;
+      const bf16* vcol = Vb + ht * 32 + 16 * (k16 & 1) + 4 * (i16 & 3) + (4 * G + (i16 >> 2)) * C::P;
+      auto step = [&](int kk, const bf16x8& pb) {
+        const bf16* p0 = vcol + 16 * kk * C::P;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 8 * C::P));
+        bf16x8 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { a[e] = lo[e]; a[4 + e] = hi[e]; }
+        oacc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[ht], 0, 0, 0);
+      };
+      if (live[0]) { step(0, pb0); step(1, pb1); }
+      if (live[1]) { step(2, pb2); step(3, pb3); }
+    }
+
+    if (more) {
+      kr.store(Ks[buf ^ 1], tid);
+      vr.store(Vs[buf ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  if (q < Tn) {
+    const float inv = 1.f / l;
+    const int64_t row = (int64_t)b * Tn + q;
+    float* orow = o + row * (int64_t)H * HD + h * HD;
+    bf16* crow = o_cast ? o_cast + row * (int64_t)H * HD + h * HD : nullptr;
+#pragma unroll
+    for (int ht = 0; ht < C::NH; ++ht)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int col = ht * 32 + r4 * 8 + G * 4;
+        floatx4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = oacc[ht][r4 * 4 + e] * inv;
+        *reinterpret_cast<floatx4*>(orow + col) = v;
+        if (crow) {
+          bf16x4 cv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cv[e] = to_bf16(v[e]);
+          *reinterpret_cast<bf16x4*>(crow + col) = cv;
+        }
+      }
+    if (G == 0) lse[((int64_t)b * H + h) * Tn + q] = (m + log2f(l)) * F_LN2;
+  }
+}
+
+template <int HD>
+hipError_t launch(const void* qkv, float* o, void* oc, float* lse, int B, int Tn, int H, int Hkv,
+                  hipStream_t s) {
+  const int nq = (Tn + FQ - 1) / FQ;
+  const int64_t items = (int64_t)nq * H;
+  const int xcd = (items % 8 == 0) && (H % 8 == 0);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<HD>), dim3((unsigned)items, 1, B), dim3(FT), 0, s,
+                     (const bf16*)qkv, o, (bf16*)oc, lse, Tn, H, Hkv, nq, xcd);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t attn_fwd_bf16(const void* qkv, float* o, void* o_cast, float* lse, int B, int Tn, int H,
+                         int Hkv, int hd, hipStream_t s) {
+  if (hd == 64) return launch<64>(qkv, o, o_cast, lse, B, Tn, H, Hkv, s);
+  return launch<128>(qkv, o, o_cast, lse, B, Tn, H, Hkv, s);
+}
+
+}  // namespace mt

@@ -19,6 +19,9 @@ hipError_t gemm_variant(int dtype, int layout, const void* A, int64_t lda, const
                         int64_t K, int variant, hipStream_t s);
 
 bool attn_supported(int dtype, int hd);
+// bf16 forward on 32x32 matrix-core tiles (hd 64 or 128), attn_fwd_bf16.hip
+hipError_t attn_fwd_bf16(const void* qkv, float* o, void* o_cast, float* lse, int B, int T, int H,
+                         int Hkv, int hd, hipStream_t s);
 int64_t attn_ws_d_bytes(int B, int T, int H);
 hipError_t attn_fwd(int dtype, const void* qkv, float* o, void* o_cast, float* lse, int B, int T,
                     int H, int Hkv, int hd, hipStream_t s);
