@@ -623,10 +623,7 @@ hipError_t attn_bwd(int dtype, const void* qkv, const float* o, const float* dou
                     void* dqkv, int out_dtype, const float* rcos, const float* rsin, void* ws, int B,
                     int Tn, int H, int Hkv, int hd, hipStream_t s) {
 #define MT_BWD(T, HD, O) bwd_launch<T, HD, O>(qkv, o, dout, lse, dqkv, rcos, rsin, ws, B, Tn, H, Hkv, s)
-  if (dtype == 1) {
-    if (hd == 64) return out_dtype ? MT_BWD(bf16, 64, bf16) : MT_BWD(bf16, 64, float);
-    return out_dtype ? MT_BWD(bf16, 128, bf16) : MT_BWD(bf16, 128, float);
-  }
+  if (dtype == 1) return attn_bwd_bf16(qkv, o, dout, lse, dqkv, out_dtype, rcos, rsin, ws, B, Tn, H, Hkv, hd, s);
   switch (hd) {
     case 16: return MT_BWD(float, 16, float);
     case 32: return MT_BWD(float, 32, float);

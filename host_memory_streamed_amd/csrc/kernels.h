@@ -22,6 +22,11 @@ bool attn_supported(int dtype, int hd);
 // bf16 forward on 32x32 matrix-core tiles (hd 64 or 128), attn_fwd_bf16.hip
 hipError_t attn_fwd_bf16(const void* qkv, float* o, void* o_cast, float* lse, int B, int T, int H,
                          int Hkv, int hd, hipStream_t s);
+// bf16 backward on 32x32 matrix-core tiles (hd 64 or 128), attn_bwd_bf16.hip;
+// arguments as attn_bwd
+hipError_t attn_bwd_bf16(const void* qkv, const float* o, const float* dout, const float* lse, void* dqkv,
+                         int out_dtype, const float* rcos, const float* rsin, void* ws, int B, int T, int H,
+                         int Hkv, int hd, hipStream_t s);
 int64_t attn_ws_d_bytes(int B, int T, int H);
 hipError_t attn_fwd(int dtype, const void* qkv, float* o, void* o_cast, float* lse, int B, int T,
                     int H, int Hkv, int hd, hipStream_t s);
