@@ -55,6 +55,27 @@ def build_context(w, dtype, seed, flags, host_threads=0, chunk_rows=0, ckpt_host
     return ctx
 
 
+def recorded_traffic(kernel_class):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, if it covers this kernel class and the kernel's
+    source has not changed since the counters were taken; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm_nt_bf16_14b_traffic.md")
+    src = os.path.join(ROOT, "host_memory_streamed_amd", "csrc", "gemm.hip")
+    try:
+        kv = {}
+        for line in open(path):
+            if ":" in line and not line.startswith(("|", "#", "`")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        if kv.get("kernel_class") == kernel_class and kv.get("gemm_source_sha256_16") == digest:
+            return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        pass
+    return None
+
+
 def cpu_baseline(w, budget_tokens=512):
     """The CPU oracle (plain float64 NumPy) timed on a bounded sample of the
     same workload: one decoder layer of the real shape and the real head on
@@ -124,6 +145,9 @@ def main():
     ap.add_argument("--trace", default=None, help="write the last step's schedule as Chrome JSON")
     ap.add_argument("--chunk-rows", type=int, default=0, help="token rows per projection/MLP chunk (0 = auto)")
     ap.add_argument("--ckpt-host", type=int, default=0, help="checkpoints parked in host memory (0 = auto)")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="after the run, one plain device copy of this many MiB (a known-size reference "
+                         "dispatch for hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -231,7 +255,8 @@ def main():
             "peak": round(kpeak / (1e12 if gemm else 1e9), 1),
             "unit": "TFLOP/s" if gemm else "GB/s",
             "frac": round(achieved / kpeak, 4),
-            "traffic": None,
+            "traffic": (recorded_traffic(dom_name) if w.name == "14b" else None),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "launches_per_step": dom["launches"] // args.steps,
             "avg_launch_us": round(dom["ms"] / dom["launches"] * 1e3, 2),
         },
@@ -242,6 +267,14 @@ def main():
         "cpu_baseline": None,
     }
     ctx.close()
+    if args.copy_probe:
+        n = args.copy_probe << 18   # fp32 elements
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {n * 4} bytes read, {n * 4} bytes written")
+        del src, dst
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
         out["cpu_baseline"] = cpu_baseline(w)
