@@ -145,6 +145,9 @@ def main():
     ap.add_argument("--trace", default=None, help="write the last step's schedule as Chrome JSON")
     ap.add_argument("--chunk-rows", type=int, default=0, help="token rows per projection/MLP chunk (0 = auto)")
     ap.add_argument("--ckpt-host", type=int, default=0, help="checkpoints parked in host memory (0 = auto)")
+    ap.add_argument("--sync-opt", action="store_true",
+                    help="every AdamW update lands before its step returns (default: updates may finish "
+                         "during the next step's forward, in the order it loads the units)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="after the run, one plain device copy of this many MiB (a known-size reference "
                          "dispatch for hardware byte counters)")
@@ -165,7 +168,7 @@ def main():
     if args.layers:
         w = mt.Workload(**{**w.__dict__, "n_layers": args.layers})
     dtype = mt.MT_BF16 if args.dtype == "bf16" else mt.MT_FP32
-    flags = mt.MT_KERNEL_TIMING | mt.MT_TRACE
+    flags = mt.MT_KERNEL_TIMING | mt.MT_TRACE | (0 if args.sync_opt else mt.MT_OVERLAP_OPT)
     ctx = build_context(w, dtype, args.seed, flags, chunk_rows=args.chunk_rows, ckpt_host=args.ckpt_host)
     layout = ctx.layout_info()
     tokens, targets = synth.token_batch(args.seed, w.batch, w.seq, w.vocab)
@@ -176,6 +179,9 @@ def main():
         t0 = time.perf_counter()
         losses.append(ctx.train_step(tokens, targets))
         log(f"warmup step {i}: {time.perf_counter() - t0:.3f}s loss {losses[-1]:.4f}")
+    # the timed region holds exactly the K steps' work: the warmup's updates
+    # land before it starts, the last step's updates before it ends
+    ctx.sync()
     torch.cuda.synchronize()
     stats = []
     kstats = {}
@@ -190,6 +196,7 @@ def main():
                 acc[f] += k[f]
         log(f"step {i}: {s['step_ms']:.1f} ms loss {losses[-1]:.4f} fwd {s['forward_ms']:.0f} ms "
             f"tail {s['tail_ms']:.0f} ms adamw(sum) {s['adamw_ms']:.0f} ms")
+    ctx.sync()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     if args.trace:
@@ -234,7 +241,10 @@ def main():
                    "n_layers": w.n_layers, "d_model": w.d_model, "n_heads": w.n_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ffn_dim": w.ffn_dim,
                    "vocab": w.vocab, "global_batch": w.batch, "seq_len": w.seq,
-                   "master": "fp32 p/m/v in host memory", "parallelism": "none (1 GPU)", **layout},
+                   "master": "fp32 p/m/v in host memory", "parallelism": "none (1 GPU)",
+                   "optimizer": ("host AdamW, each update landing before its step returns" if args.sync_opt else
+                                 "host AdamW, updates finishing during the next step's forward in load order"),
+                   **layout},
         "mfu": round(mfu, 4),
         "host_link": {
             "h2d_GBps_step": round(h2d / (ms * 1e-3) / 1e9, 2),

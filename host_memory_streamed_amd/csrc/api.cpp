@@ -124,15 +124,21 @@ static int validate(const mt_model_cfg* c, std::string& why) {
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f) || !(c->lr >= 0.0) || !(c->beta1 >= 0.0 && c->beta1 < 1.0) ||
       !(c->beta2 >= 0.0 && c->beta2 < 1.0) || !(c->adam_eps >= 0.0))
     return bad("invalid eps / rope_base / AdamW hyperparameters");
-  if (c->flags & ~(MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE)) return bad("unknown flags");
+  if (c->flags & ~(MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE | MT_OVERLAP_OPT)) return bad("unknown flags");
   if (c->chunk_rows < 0) return bad("chunk_rows must be >= 0");
   if (c->ckpt_host < 0 || (c->ckpt_host > 0 && c->ckpt_host > c->n_layers - 2))
     return bad("ckpt_host must be 0 or in [1, n_layers - 2]");
   return MT_OK;
 }
 
+void adam_drain(Ctx& c) {
+  std::unique_lock<std::mutex> lk(c.amu);
+  c.acv.wait(lk, [&] { return c.adam_pending == 0; });
+}
+
 static void free_ctx(Ctx* c) {
   if (!c) return;
+  adam_drain(*c);   // no update may still be reading host memory
   if (c->s_comp) hipStreamSynchronize(c->s_comp);
   if (c->s_in) hipStreamSynchronize(c->s_in);
   if (c->s_out) hipStreamSynchronize(c->s_out);
@@ -256,13 +262,30 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
   }
   int64_t max_unit = std::max(c.units[0].lay.n, c.units[D.L].lay.n);
   if (!keep) {
-    c.ring = 3;
-    for (int i = 0; i < c.ring; ++i) {
+    // Synchronous updates keep up with the gradients: three slots that fit
+    // any unit. Overlapped updates fall behind during the backward and catch
+    // up in the next forward: layer-sized slots for as many layers as fit in
+    // 16 GiB (3 to 16), plus one slot kept for the head.
+    std::vector<int64_t> sizes;
+    if (cfg->flags & MT_OVERLAP_OPT) {
+      const int64_t ln = c.units[0].lay.n;
+      const int r = (int)std::max<int64_t>(3, std::min<int64_t>(16, (16LL << 30) / (ln * 4)));
+      sizes.assign(r, ln);
+      sizes.push_back(c.units[D.L].lay.n);
+      c.head_slot = r;
+    } else {
+      sizes.assign(3, max_unit);
+    }
+    for (int64_t n : sizes) {
       float* p = nullptr;
-      HIP_OR(hipHostMalloc((void**)&p, (size_t)max_unit * 4, hipHostMallocDefault), MT_EHOSTOOM, "pinned gradient ring");
+      HIP_OR(hipHostMalloc((void**)&p, (size_t)n * 4, hipHostMallocDefault), MT_EHOSTOOM, "pinned gradient ring");
       c.ring_slot.push_back(p);
+      c.ring_elems.push_back(n);
     }
   }
+  c.slot_busy.assign(c.ring_slot.size(), 0);
+  c.unit_busy.assign(D.L + 2, 0);
+  c.adam_end.assign(D.L + 2, std::chrono::steady_clock::time_point{});
   HIP_OR(hipHostMalloc((void**)&c.x0_host, (size_t)c.M_max * D.d * 4, hipHostMallocDefault), MT_EHOSTOOM, "pinned staging");
   HIP_OR(hipHostMalloc((void**)&c.dx0_host, (size_t)c.M_max * D.d * 4, hipHostMallocDefault), MT_EHOSTOOM, "pinned staging");
   HIP_OR(hipHostMalloc((void**)&c.tgt_host, (size_t)c.M_max * 4, hipHostMallocDefault), MT_EHOSTOOM, "pinned staging");
@@ -410,9 +433,16 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
   return MT_OK;
 }
 
+int mt_sync(mt_ctx* h) {
+  if (!h) return MT_EINVAL;
+  adam_drain(h->c);
+  return MT_OK;
+}
+
 int mt_set_param(mt_ctx* h, int32_t id, const float* src) {
   if (!h) return MT_EINVAL;
   Ctx& c = h->c;
+  adam_drain(c);
   if (id < 0 || id >= (int32_t)c.tensors.size() || !src) return set_error(&c, MT_EINVAL, "bad tensor id or NULL source");
   const TensorRef& r = c.tensors[id];
   Unit& u = r.unit < 0 ? c.emb() : c.units[r.unit];
@@ -459,6 +489,7 @@ int mt_token_losses(mt_ctx* h, const float** ptr, int64_t* n) {
 }
 
 static int tensor_ptr(Ctx& c, int32_t id, int which, const float** ptr, int64_t* numel) {
+  adam_drain(c);
   if (id < 0 || id >= (int32_t)c.tensors.size() || !ptr) return set_error(&c, MT_EINVAL, "bad tensor id or NULL pointer");
   const TensorRef& r = c.tensors[id];
   Unit& u = r.unit < 0 ? c.emb() : c.units[r.unit];

@@ -30,7 +30,7 @@ Pool::~Pool() {
   for (auto& t : workers_) t.join();
 }
 
-void Pool::submit(int64_t n, std::function<void(int64_t)> fn, std::function<void()> done) {
+void Pool::submit(int64_t n, std::function<void(int64_t)> fn, std::function<void()> done, int64_t priority) {
   if (n <= 0) {
     if (done) done();
     return;
@@ -39,9 +39,12 @@ void Pool::submit(int64_t n, std::function<void(int64_t)> fn, std::function<void
   job->fn = std::move(fn);
   job->done = std::move(done);
   job->n = n;
+  job->priority = priority;
   {
     std::lock_guard<std::mutex> g(mu_);
-    jobs_.push_back(job);
+    auto it = jobs_.begin();
+    while (it != jobs_.end() && (*it)->priority <= priority) ++it;
+    jobs_.insert(it, job);
   }
   cv_.notify_all();
 }
@@ -50,11 +53,14 @@ void Pool::run(int64_t n, const std::function<void(int64_t)>& fn) {
   std::mutex m;
   std::condition_variable cv;
   bool finished = false;
-  submit(n, fn, [&] {
-    std::lock_guard<std::mutex> g(m);
-    finished = true;
-    cv.notify_all();
-  });
+  submit(
+      n, fn,
+      [&] {
+        std::lock_guard<std::mutex> g(m);
+        finished = true;
+        cv.notify_all();
+      },
+      INT64_MIN);
   std::unique_lock<std::mutex> lk(m);
   cv.wait(lk, [&] { return finished; });
 }
@@ -67,14 +73,17 @@ void Pool::loop() {
       std::unique_lock<std::mutex> lk(mu_);
       cv_.wait(lk, [&] { return stop_ || !jobs_.empty(); });
       if (stop_ && jobs_.empty()) return;
-      job = jobs_.front();
-      i = job->next.fetch_add(1);
-      if (i >= job->n) {
-        // every index of the front job is taken; drop it from the queue
-        if (!jobs_.empty() && jobs_.front() == job) jobs_.pop_front();
-        continue;
+      // Urgent jobs (run()) first; then a job already under way, so that a
+      // started job finishes before the next one starts; then the lowest
+      // priority value. The queue is kept in priority order.
+      auto pick = jobs_.begin();
+      if ((*pick)->priority != INT64_MIN) {
+        for (auto it = jobs_.begin(); it != jobs_.end(); ++it)
+          if ((*it)->next.load() > 0) { pick = it; break; }
       }
-      if (i == job->n - 1 && !jobs_.empty() && jobs_.front() == job) jobs_.pop_front();
+      job = *pick;
+      i = job->next.fetch_add(1);
+      if (i >= job->n - 1) jobs_.erase(pick);   // the last index takes it off the queue
     }
     job->fn(i);
     if (job->finished.fetch_add(1) + 1 == job->n && job->done) job->done();

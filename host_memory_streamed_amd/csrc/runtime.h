@@ -27,9 +27,13 @@ class Pool {
   ~Pool();
   int size() const { return (int)workers_.size(); }
   // Run fn(i) for i in [0, n) on the workers; when all have finished, call
-  // done() (on the worker that finished last). Returns immediately.
-  void submit(int64_t n, std::function<void(int64_t)> fn, std::function<void()> done = nullptr);
-  // Run fn(i) for i in [0, n) and wait for all of them.
+  // done() (on the worker that finished last). Returns immediately. Workers
+  // take indices from the job with the lowest priority value first (in
+  // submission order among equals), so a later, more urgent job overtakes
+  // the rest of an earlier one at index granularity.
+  void submit(int64_t n, std::function<void(int64_t)> fn, std::function<void()> done = nullptr,
+              int64_t priority = 0);
+  // Run fn(i) for i in [0, n) ahead of every queued job and wait for all of them.
   void run(int64_t n, const std::function<void(int64_t)>& fn);
 
  private:
@@ -37,6 +41,7 @@ class Pool {
     std::function<void(int64_t)> fn;
     std::function<void()> done;
     int64_t n;
+    int64_t priority;
     std::atomic<int64_t> next{0};
     std::atomic<int64_t> finished{0};
   };
@@ -170,9 +175,22 @@ struct Ctx {
   Unit& emb() { return units[D.L + 1]; }
   std::vector<TensorRef> tensors;
 
-  // grad staging ring (MT_KEEP_GRADS off)
-  int ring = 0;
+  // Gradient staging (MT_KEEP_GRADS off): slots of ring_elems[i] floats. A
+  // slot is busy from its D2H until the AdamW that reads it has finished.
   std::vector<float*> ring_slot;
+  std::vector<int64_t> ring_elems;
+  int head_slot = -1;              // slot reserved for the head (-1: any slot fits it)
+
+  // Host AdamW jobs in flight, shared with the worker threads. With
+  // MT_OVERLAP_OPT they may finish during the next step; a unit is loaded
+  // again only when none of its updates is in flight.
+  std::mutex amu;
+  std::condition_variable acv;
+  int adam_pending = 0;
+  std::vector<int> unit_busy;      // [L + 2]: layers, head, embedding
+  std::vector<char> slot_busy;
+  std::vector<std::chrono::steady_clock::time_point> adam_end;   // per unit, last update
+  std::atomic<int64_t> adam_ns{0};
   // pinned staging
   float* x0_host = nullptr;      // [M_max, d]
   float* dx0_host = nullptr;     // [M_max, d]
@@ -216,6 +234,8 @@ struct Ctx {
 // ----------------------------------------------------------- helpers ---
 
 int set_error(Ctx* c, int code, const std::string& msg);
+// Wait until every submitted AdamW job has finished.
+void adam_drain(Ctx& c);
 void* host_alloc_plain(size_t bytes);
 void host_free_plain(void* p, size_t bytes);
 

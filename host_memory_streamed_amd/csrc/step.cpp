@@ -128,17 +128,26 @@ void destroy_step_events(StepEvents* e) {
 
 // AdamW over element ranges of one unit as a single pool job of chunks of at
 // most 1M elements; writes p, m, v and the unit's device image (bf16 mode:
-// fp32 gains + bf16 matrices).
-static void submit_adamw(Ctx& c, Unit& u, const float* g, std::vector<std::pair<int64_t, int64_t>> ranges,
-                         const AdamConst& k, std::function<void()> done, std::atomic<int64_t>* adam_ns) {
+// fp32 gains + bf16 matrices). `uidx` is the unit's index in Ctx::units; the
+// unit counts as busy until the job has finished, and the gradient staging
+// slot `slot` (or -1) is released then.
+static void submit_adamw(Ctx& c, int uidx, const float* g, std::vector<std::pair<int64_t, int64_t>> ranges,
+                         const AdamConst& k, int slot, int64_t priority) {
   constexpr int64_t CH = 1 << 20;
+  Unit& u = c.units[uidx];
   auto chunks = std::make_shared<std::vector<std::pair<int64_t, int64_t>>>();
   for (auto& r : ranges)
     for (int64_t a = r.first; a < r.second; a += CH) chunks->push_back({a, std::min(r.second, a + CH)});
   const int dt = c.dtype;
+  {
+    std::lock_guard<std::mutex> lk(c.amu);
+    c.unit_busy[uidx]++;
+    c.adam_pending++;
+  }
+  Ctx* cp = &c;
   c.pool->submit(
       (int64_t)chunks->size(),
-      [&u, g, chunks, k, dt, adam_ns](int64_t i) {
+      [&u, g, chunks, k, dt, cp](int64_t i) {
         const auto t0 = std::chrono::steady_clock::now();
         const int64_t a = (*chunks)[i].first, b = (*chunks)[i].second;
         const int64_t mb = u.lay.mat_base;
@@ -154,10 +163,20 @@ static void submit_adamw(Ctx& c, Unit& u, const float* g, std::vector<std::pair<
                              : nullptr;
           adamw_range(u.p + s, u.m + s, u.v + s, g + s, b - s, k, bo, nullptr);
         }
-        adam_ns->fetch_add((int64_t)(std::chrono::duration<double, std::nano>(
-                                          std::chrono::steady_clock::now() - t0).count()));
+        cp->adam_ns.fetch_add((int64_t)(std::chrono::duration<double, std::nano>(
+                                            std::chrono::steady_clock::now() - t0).count()));
       },
-      std::move(done));
+      [cp, uidx, slot] {
+        {
+          std::lock_guard<std::mutex> lk(cp->amu);
+          cp->unit_busy[uidx]--;
+          if (slot >= 0) cp->slot_busy[slot] = 0;
+          cp->adam_pending--;
+          cp->adam_end[uidx] = std::chrono::steady_clock::now();
+        }
+        cp->acv.notify_all();
+      },
+      priority);
 }
 
 int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t* targets, int B,
@@ -169,6 +188,7 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
   const auto t_begin = std::chrono::steady_clock::now();
   const bool trace = (c.cfg.flags & MT_TRACE) != 0;
   const bool keep = (c.cfg.flags & MT_KEEP_GRADS) != 0;
+  const bool overlap = (c.cfg.flags & MT_OVERLAP_OPT) != 0;
   c.kt.on = (c.cfg.flags & MT_KERNEL_TIMING) != 0;
   c.kt.used = 0;
   c.kt.recs.clear();
@@ -179,6 +199,11 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
   const auto t_dev0 = std::chrono::steady_clock::now();
 
   // ---- inputs: targets and the embedding gather x0 = E[tokens] (host) ----
+  // (an overlapped update of the embedding from the last step lands first)
+  {
+    std::unique_lock<std::mutex> lk(c.amu);
+    c.acv.wait(lk, [&] { return c.unit_busy[L + 1] == 0; });
+  }
   std::memcpy(c.tgt_host, targets, (size_t)M * 4);
   Unit& emb = c.emb();
   c.pool->run((M + 255) / 256, [&](int64_t i) {
@@ -209,38 +234,44 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
   const int n_items = (int)items.size();
   const AdamConst k = adam_const(c.cfg, c.step + 1);
 
-  std::atomic<int64_t> adam_ns{0};
-  std::vector<double> adam_end_ms(L + 2, 0.0), adam_start_ms(L + 2, 0.0);
+  const int64_t adam_ns0 = c.adam_ns.load();
+  std::vector<double> adam_start_ms(L + 2, -1.0);
   bool abort = false;
   double loss_sum = 0.0, forward_ms = 0.0, last_land_ms = 0.0;
 
-  auto grad_unit = [&](int kk) -> Unit& { return kk == 0 ? c.head() : c.layer(L - kk); };
-  auto grad_dest = [&](int kk) -> float* { return keep ? grad_unit(kk).g : c.ring_slot[kk % c.ring]; };
+  // gradient item kk: 0 = head, kk >= 1 = layer L - kk; units index Ctx::units
+  auto grad_uidx = [&](int kk) { return kk == 0 ? L : L - kk; };
+  auto grad_unit = [&](int kk) -> Unit& { return c.units[grad_uidx(kk)]; };
+  std::vector<int> slot_of(L + 1, -1);
+  auto grad_dest = [&](int kk) -> float* { return keep ? grad_unit(kk).g : c.ring_slot[slot_of[kk]]; };
   auto unit_id = [&](const Item& it) { return it.phase == PH_HEAD ? MT_UNIT_HEAD : it.unit; };
-
-  // AdamW tasks in flight and their completion (set from pool threads)
-  std::mutex amu;
-  std::condition_variable acv;
-  int pending = 0;
-  std::vector<char> adam_done(L + 1, 0);
-  auto job_done = [&](int kk) {
-    {
-      std::lock_guard<std::mutex> g(amu);
-      if (kk >= 0) {
-        adam_done[kk] = 1;
-        adam_end_ms[kk] = ms_since(t_begin);
+  // AdamW order: synchronous updates in arrival order (embedding's untouched
+  // rows first); overlapped updates in the order the next forward needs them
+  auto adam_priority = [&](int uidx) -> int64_t {
+    if (overlap) return uidx == L + 1 ? 0 : uidx == L ? L + 1 : 1 + uidx;
+    return uidx == L + 1 ? -1 : uidx == L ? 0 : L - uidx;
+  };
+  auto unit_idle = [&](int uidx) {
+    std::lock_guard<std::mutex> lk(c.amu);
+    return c.unit_busy[uidx] == 0;
+  };
+  // a free staging slot that fits gradient item kk (-1: none yet)
+  auto take_slot = [&](int kk) -> int {
+    std::lock_guard<std::mutex> lk(c.amu);
+    const int64_t need = grad_unit(kk).lay.n;
+    for (int sidx = 0; sidx < (int)c.ring_slot.size(); ++sidx) {
+      if (c.head_slot >= 0 && (sidx == c.head_slot) != (kk == 0)) continue;
+      if (!c.slot_busy[sidx] && c.ring_elems[sidx] >= need) {
+        c.slot_busy[sidx] = 1;
+        return sidx;
       }
-      pending--;
     }
-    acv.notify_all();
+    return -1;
   };
-  auto adam_is_done = [&](int kk) {
-    std::lock_guard<std::mutex> g(amu);
-    return adam_done[kk] != 0;
-  };
-  auto add_pending = [&] {
-    std::lock_guard<std::mutex> g(amu);
-    pending++;
+  auto free_slot = [&](int sidx) {
+    if (sidx < 0) return;
+    std::lock_guard<std::mutex> lk(c.amu);
+    c.slot_busy[sidx] = 0;
   };
 
   // ---- host dispatcher ----
@@ -392,13 +423,14 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
     }
     if (prev < D.V) runs.push_back({prev, D.V});
     for (auto& rr : runs) rr = {rr.first * d, rr.second * d};
-    add_pending();
-    submit_adamw(c, emb, emb.g, std::move(runs), k, [&] { job_done(-1); }, &adam_ns);
+    adam_start_ms[L + 1] = ms_since(t_begin);
+    submit_adamw(c, L + 1, emb.g, std::move(runs), k, -1, adam_priority(L + 1));
   };
 
   for (;;) {
     bool progress = false;
-    // loads, in order, once the buffer's previous user has finished
+    // loads, in order, once the buffer's previous user has finished (and,
+    // with overlapped updates, once the unit's last update has landed)
     while (next_l < loads.size()) {
       const int j = loads[next_l];
       const int p = items[j].prev_user;
@@ -407,6 +439,7 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
         if (st < 0) { rc = st; break; }
         if (!st) break;
       }
+      if (overlap && items[j].phase != PH_BWD && !unit_idle(items[j].phase == PH_HEAD ? L : items[j].unit)) break;
       if ((rc = issue_load(j))) break;
       ++next_l;
       progress = true;
@@ -466,12 +499,16 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
       }
     }
     // gradient copies, in order, once their compute has finished (and, with
-    // the staging ring, once the AdamW that used the slot has finished)
+    // the staging ring, once a slot is free: its last AdamW has finished)
     while (loss_issued && next_g <= L) {
       const int st = item_done(grad_item[next_g]);
       if (st < 0) { rc = st; break; }
       if (!st) break;
-      if (!keep && next_g >= c.ring && !abort && !adam_is_done(next_g - c.ring)) break;
+      if (!keep) {
+        const int sidx = take_slot(next_g);
+        if (sidx < 0) break;
+        slot_of[next_g] = sidx;
+      }
       if ((rc = issue_grad(next_g))) break;
       ++next_g;
       progress = true;
@@ -483,15 +520,13 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
       if (st < 0) { rc = st; break; }
       if (!st) break;
       last_land_ms = ms_since(t_begin);
+      const int kk = next_a, ui = grad_uidx(kk);
       if (!abort) {
-        Unit& u = grad_unit(next_a);
-        add_pending();
-        adam_start_ms[next_a] = last_land_ms;
-        const int kk = next_a;
-        submit_adamw(c, u, grad_dest(kk), {{0, u.lay.n}}, k, [&, kk] { job_done(kk); }, &adam_ns);
-      } else {
-        std::lock_guard<std::mutex> g(amu);
-        adam_done[next_a] = 1;
+        adam_start_ms[ui] = last_land_ms;
+        submit_adamw(c, ui, grad_dest(kk), {{0, c.units[ui].lay.n}}, k, keep ? -1 : slot_of[kk],
+                     adam_priority(ui));
+      } else if (!keep) {
+        free_slot(slot_of[kk]);
       }
       ++next_a;
       progress = true;
@@ -515,8 +550,11 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
     hipStreamSynchronize(c.s_in);
     hipStreamSynchronize(c.s_comp);
     hipStreamSynchronize(c.s_out);
-    std::unique_lock<std::mutex> lk(amu);
-    acv.wait(lk, [&] { return pending == 0; });
+    adam_drain(c);
+    {
+      std::lock_guard<std::mutex> lk(c.amu);
+      std::fill(c.slot_busy.begin(), c.slot_busy.end(), 0);
+    }
     return rc;
   }
 
@@ -525,7 +563,6 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
   if (!abort) {
     const int64_t nr = (int64_t)rows.size();
     const int64_t per = 64;
-    adam_start_ms[L + 1] = ms_since(t_begin);
     c.pool->run((nr + per - 1) / per, [&](int64_t i) {
       for (int64_t j = i * per; j < std::min(nr, (i + 1) * per); ++j) {
         const int32_t v = rows[j];
@@ -545,14 +582,10 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
       runs.push_back({(int64_t)rows[a] * d, (int64_t)(rows[b - 1] + 1) * d});
       a = b;
     }
-    add_pending();
-    submit_adamw(c, emb, emb.g, std::move(runs), k, [&] { job_done(-1); }, &adam_ns);
+    submit_adamw(c, L + 1, emb.g, std::move(runs), k, -1, adam_priority(L + 1));
   }
-  {
-    std::unique_lock<std::mutex> lk(amu);
-    acv.wait(lk, [&] { return pending == 0; });
-  }
-  adam_end_ms[L + 1] = ms_since(t_begin);
+  // synchronous mode: every update lands before the step returns
+  if (!overlap) adam_drain(c);
   const hipError_t s1 = hipStreamSynchronize(c.s_in), s2 = hipStreamSynchronize(c.s_comp),
                    s3 = hipStreamSynchronize(c.s_out);
   if (s1 != hipSuccess || s2 != hipSuccess || s3 != hipSuccess)
@@ -570,7 +603,7 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
   st.forward_ms = forward_ms;
   st.h2d_bytes = h2d_bytes;
   st.d2h_bytes = d2h_bytes;
-  st.adamw_ms = (double)adam_ns.load() * 1e-6;
+  st.adamw_ms = (double)(c.adam_ns.load() - adam_ns0) * 1e-6;
   int64_t n_all = 0;
   for (auto& u : c.units) n_all += u.lay.n;
   st.adamw_bytes = (double)n_all * (16.0 + 12.0 + (c.dtype ? 2.0 : 0.0));
@@ -618,11 +651,20 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
     // host AdamW entries on the same clock (device times are relative to the
     // start event, host times to the moment it completed)
     const double off = std::chrono::duration<double, std::milli>(t_dev0 - t_begin).count();
-    for (int kk = 0; kk <= L; ++kk) {
-      const int unit = kk == 0 ? MT_UNIT_HEAD : L - kk;
-      c.sched.push_back({MT_PH_ADAMW, unit, -1, 3, adam_start_ms[kk] - off, adam_end_ms[kk] - off});
+    // (an update still running, overlapped into the next step, is left out)
+    for (int kk = 0; kk <= L + 1; ++kk) {
+      const int ui = kk <= L ? grad_uidx(kk) : L + 1;
+      if (adam_start_ms[ui] < 0) continue;
+      std::chrono::steady_clock::time_point te;
+      {
+        std::lock_guard<std::mutex> lk(c.amu);
+        if (c.unit_busy[ui]) continue;
+        te = c.adam_end[ui];
+      }
+      const double end_ms = std::chrono::duration<double, std::milli>(te - t_begin).count();
+      const int unit = ui == L ? MT_UNIT_HEAD : ui == L + 1 ? MT_UNIT_EMB : ui;
+      c.sched.push_back({MT_PH_ADAMW, unit, -1, 3, adam_start_ms[ui] - off, end_ms - off});
     }
-    c.sched.push_back({MT_PH_ADAMW, MT_UNIT_EMB, -1, 3, adam_start_ms[L + 1] - off, adam_end_ms[L + 1] - off});
     for (auto& h : host_spans) c.sched.push_back({h.phase, h.unit, -1, 4, h.t0 - off, h.t1 - off});
   }
   if (c.kt.on) {

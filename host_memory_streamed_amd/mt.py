@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmt.so")
 MT_OK, MT_EINVAL, MT_EHOSTOOM, MT_EDEVOOM, MT_EHIP, MT_ENONFINITE, MT_ETIMEOUT, MT_ENOGRADS, MT_ESTATE = (
     0, -1, -2, -3, -4, -5, -6, -7, -8)
 MT_FP32, MT_BF16 = 0, 1
-MT_KEEP_GRADS, MT_KERNEL_TIMING, MT_TRACE = 1, 2, 4
+MT_KEEP_GRADS, MT_KERNEL_TIMING, MT_TRACE, MT_OVERLAP_OPT = 1, 2, 4, 8
 MT_GEMM_NT, MT_GEMM_NN, MT_GEMM_TN = 0, 1, 2
 PHASES = {0: "load", 1: "fwd", 2: "head", 3: "bwd", 4: "grad", 5: "adamw", 6: "ckpt_out", 7: "ckpt_in"}
 UNIT_EMB, UNIT_HEAD = -1, -2
@@ -81,6 +81,7 @@ _SIGS = {
     "mt_schedule": (ctypes.c_int, [_P, ctypes.POINTER(SchedEntry), _I32, ctypes.POINTER(_I32)]),
     "mt_trace_dump": (ctypes.c_int, [_P, ctypes.c_char_p]),
     "mt_device_bytes": (ctypes.c_int, [_P, ctypes.POINTER(_I64)]),
+    "mt_sync": (ctypes.c_int, [_P]),
     "mt_layout_info": (ctypes.c_int, [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
     "mt_last_error": (ctypes.c_char_p, [_P]),
     "mt_destroy": (None, [_P]),
@@ -232,6 +233,10 @@ class Context:
         mm = np.ctypeslib.as_array(ctypes.cast(m, fp), shape=(n,)).reshape(self.table[tid][1]).copy()
         vv = np.ctypeslib.as_array(ctypes.cast(v, fp), shape=(n,)).reshape(self.table[tid][1]).copy()
         return mm, vv, t.value
+
+    def sync(self):
+        """Wait for every AdamW update submitted so far (overlapped mode)."""
+        _check(lib().mt_sync(self.h), self.h)
 
     def token_losses(self) -> np.ndarray:
         p, n = _P(), _I64()

@@ -61,6 +61,14 @@ extern "C" {
 #define MT_KEEP_GRADS 1u     /* keep every tensor's gradient in host memory (mt_grads) */
 #define MT_KERNEL_TIMING 2u  /* time every kernel launch with HIP events (mt_kernel_stats) */
 #define MT_TRACE 4u          /* record the per-unit schedule log (mt_schedule, mt_trace_dump) */
+/* Let the host AdamW of a step finish during the next step: mt_train_step
+ * returns once every gradient has landed in host memory, the remaining
+ * updates run in the order the next forward needs them (embedding, layers
+ * 0..L-1, head), and the next step loads a unit only after its update has
+ * landed. Results are identical to the synchronous mode. Accessors that read
+ * or write the host state (mt_params, mt_grads, mt_opt_state, mt_set_param)
+ * and mt_destroy wait for pending updates first; mt_sync waits explicitly. */
+#define MT_OVERLAP_OPT 8u
 
 typedef struct mt_model_cfg {
   int32_t n_layers;
@@ -75,7 +83,7 @@ typedef struct mt_model_cfg {
   int32_t compute_dtype;     /* MT_FP32 or MT_BF16 */
   int32_t n_layer_buffers;   /* 2 = streamed; >= n_layers + 1 = every layer resident */
   int32_t host_threads;      /* AdamW / gather pool size; 0 = online CPUs (at most 64) */
-  uint32_t flags;            /* MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE */
+  uint32_t flags;            /* MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE | MT_OVERLAP_OPT */
   float rms_eps;
   float rope_base;
   double lr, beta1, beta2, adam_eps, weight_decay;   /* AdamW hyperparameters */
@@ -135,6 +143,10 @@ int mt_set_param(mt_ctx* ctx, int32_t id, const float* src);
  * unchanged and the step count is not advanced. */
 int mt_train_step(mt_ctx* ctx, const int32_t* tokens, const int32_t* targets, int32_t B,
                   int32_t T, float* loss_out);
+
+/* Wait until every AdamW update submitted so far has landed in host memory
+ * (a no-op unless MT_OVERLAP_OPT left some running). */
+int mt_sync(mt_ctx* ctx);
 
 /* Per-token losses of the last step in (b, t) order: *n = B*T. Library-owned,
  * valid until the next mt_train_step or mt_destroy. */

@@ -264,6 +264,36 @@ def test_token_chunks_change_only_rounding():
         np.testing.assert_allclose(pb[ok], pa[ok], rtol=1e-5, atol=1e-9)
 
 
+@pytest.mark.parametrize("dtype,keep", [(mt.MT_FP32, True), (mt.MT_BF16, False), (mt.MT_BF16, True)])
+def test_overlapped_optimizer_is_bitwise_synchronous(dtype, keep):
+    """With MT_OVERLAP_OPT a step returns before its AdamW updates have all
+    landed; the next step loads each unit only after its update. Losses of
+    every step and the final state match the synchronous mode bit for bit."""
+    cfg = O.Config(5, 128, 2, 1, 64, 200, 300)
+    params = init_params(cfg, 29, 0.05)
+    base = mt.MT_KEEP_GRADS if keep else 0
+    out = []
+    for flags in (base, base | mt.MT_OVERLAP_OPT):
+        with make_ctx(cfg, 2, 40, params, dtype=dtype, flags=flags) as ctx:
+            losses = []
+            for s in range(4):
+                tokens, targets = synth.token_batch(29 + s, 2, 40, cfg.vocab)
+                losses.append(ctx.train_step(tokens, targets))
+                tl = ctx.token_losses().copy()
+            ctx.sync()
+            n = len(params)
+            state = [ctx.params(i).copy() for i in range(n)]
+            state += [ctx.opt_state(i)[0].copy() for i in range(n)] + [ctx.opt_state(i)[1].copy() for i in range(n)]
+            if keep:
+                state += [ctx.grads(i).copy() for i in range(n)]
+            out.append((losses, tl, state))
+    (l0, t0, s0), (l1, t1, s1) = out
+    assert l0 == l1
+    assert np.array_equal(t0, t1)
+    for a, b in zip(s0, s1):
+        assert np.array_equal(a, b)
+
+
 @pytest.mark.parametrize("dtype", [mt.MT_FP32, mt.MT_BF16])
 def test_streamed_equals_resident_bitwise(dtype):
     cfg = O.Config(5, 128, 2, 1, 64, 200, 300)
