@@ -168,7 +168,8 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
   typedef BCfg<HD> C;
   __shared__ __attribute__((aligned(16))) bf16 Qs[2][BS * C::P];
   __shared__ __attribute__((aligned(16))) bf16 Os[2][BS * C::P];
-  __shared__ float Ls[2][BS], Dsh[2][BS];
+  __shared__ __attribute__((aligned(16))) float Ls[2][BS];
+  __shared__ __attribute__((aligned(16))) float Dsh[2][BS];
 
   const int id = blockIdx.x;
   int kvh, kb;
@@ -261,16 +262,27 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ss], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, vf[ss], dp, 0, 0, 0);
       }
-      // rows are queries qs0 + (r/4)*8 + G*4 + r%4, the column is this lane's key
+      // rows are queries qs0 + (r/4)*8 + G*4 + r%4, the column is this lane's
+      // key; masking only where the sub-tile meets the diagonal or the end
+      const bool edge = qs0 < kw0 + 31 || qs0 + 31 >= Tn;
       bf16x8 pb0, pb1, db0, db1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr_ = 32 * u + (r >> 2) * 8 + G * 4 + (r & 3);
-        const int qi = q0 + qr_;
-        const float pv = (key <= qi && qi < Tn) ? exp2f(s[r] * sl2 - Ls[buf][qr_]) : 0.f;
-        const float dsv = pv * (dp[r] - Dsh[buf][qr_]);
-        if (r < 8) { pb0[r] = to_bf16(pv); db0[r] = to_bf16(dsv); }
-        else { pb1[r - 8] = to_bf16(pv); db1[r - 8] = to_bf16(dsv); }
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int qr4 = 32 * u + r4 * 8 + G * 4;
+        const floatx4 lq = *reinterpret_cast<const floatx4*>(&Ls[buf][qr4]);
+        const floatx4 dq4 = *reinterpret_cast<const floatx4*>(&Dsh[buf][qr4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = r4 * 4 + e;
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lq[e]));
+          if (edge) {
+            const int qi = q0 + qr4 + e;
+            if (!(key <= qi && qi < Tn)) pv = 0.f;
+          }
+          const float dsv = pv * (dp[r] - dq4[e]);
+          if (r < 8) { pb0[r] = to_bf16(pv); db0[r] = to_bf16(dsv); }
+          else { pb1[r - 8] = to_bf16(pv); db1[r - 8] = to_bf16(dsv); }
+        }
       }
 #pragma unroll
       for (int ht = 0; ht < C::NH; ++ht) {
@@ -386,12 +398,17 @@ __global__ __launch_bounds__(BT, 2) void attn_dq_bf16_kernel(const bf16* __restr
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ss], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, df[ss], dp, 0, 0, 0);
       }
-      // rows are keys kb0 + (r/4)*8 + G*4 + r%4, the column is this lane's query
+      // rows are keys kb0 + (r/4)*8 + G*4 + r%4, the column is this lane's
+      // query; masking only where the sub-tile meets the diagonal or the end
+      const bool edge = kb0 + 31 > wq0 || wq0 + 31 >= Tn;
       bf16x8 db0, db1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kk = kb0 + (r >> 2) * 8 + G * 4 + (r & 3);
-        const float pv = (kk <= q && q < Tn) ? exp2f(s[r] * sl2 - lse2) : 0.f;
+        float pv = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2));
+        if (edge) {
+          const int kk = kb0 + (r >> 2) * 8 + G * 4 + (r & 3);
+          if (!(kk <= q && q < Tn)) pv = 0.f;
+        }
         const float dsv = pv * (dp[r] - Dq);
         if (r < 8) db0[r] = to_bf16(dsv);
         else db1[r - 8] = to_bf16(dsv);

@@ -141,7 +141,10 @@ __global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __rest
     const bf16* Kb = Ks[buf];
     const bf16* Vb = Vs[buf];
 
-    // scores of the two 32-key sub-tiles (wave-uniform skip above the diagonal)
+    // raw scores of the two 32-key sub-tiles (wave-uniform skip above the
+    // diagonal; masking only on sub-tiles that cross it). The running maximum
+    // is taken on raw scores (the scale is positive, so it commutes with the
+    // maximum) and the scale is folded into the exponent's FMA.
     floatx16 s[2];
     bool live[2];
     float mx = -INFINITY;
@@ -158,31 +161,35 @@ __global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __rest
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + ss * 16);
           s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ss], s[st], 0, 0, 0);
         }
-        const bool full = kb + 31 <= wq0;   // every key visible to every query of the wave
+        if (kb + 31 > wq0) {   // crosses the diagonal of some query of the wave
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb + (r >> 2) * 8 + G * 4 + (r & 3);
-          const float v = (full || key <= q) ? s[st][r] * sl2 : -INFINITY;
-          s[st][r] = v;
-          mx = fmaxf(mx, v);
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb + (r >> 2) * 8 + G * 4 + (r & 3);
+            if (key > q) s[st][r] = -INFINITY;
+          }
         }
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[st][r], s[st][r + 1]));
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-    const float m_new = fmaxf(m, mx);
+    const float m_new = fmaxf(m, mx * sl2);
     const float alpha = exp2f(m - m_new);
+    const float nm = -m_new;
     float rs = 0.f;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = live[st] ? exp2f(s[st][r] - m_new) : 0.f;
+        const float p = live[st] ? __builtin_amdgcn_exp2f(fmaf(s[st][r], sl2, nm)) : 0.f;
         s[st][r] = p;
         rs += p;
       }
     rs += __shfl_xor(rs, 32, WAVE);
     l = l * alpha + rs;
     m = m_new;
+    // the output needs rescaling only when some row's maximum moved
+    const bool rescale = __any(alpha != 1.f);
     // P^T operands: 16-key step kk = 2*st + j takes accumulator slots 8j..8j+7
     bf16x8 pb0, pb1, pb2, pb3;
 #pragma unroll
@@ -196,8 +203,10 @@ __global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __rest
     // O^T += V^T P^T over four 16-key steps
 #pragma unroll
     for (int ht = 0; ht < C::NH; ++ht) {
+      if (rescale) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[ht][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[ht][r] *= alpha;
+      }
       const bf16* vcol = Vb + ht * 32 + 16 * (k16 & 1) + 4 * (i16 & 3) + (4 * G + (i16 >> 2)) * C::P;
       auto step = [&](int kk, const bf16x8& pb) {
         const bf16* p0 = vcol + 16 * kk * C::P;
