@@ -47,13 +47,22 @@ struct Tile64 {
   u32x4_b v[BCfg<HD>::NV];
   __device__ __forceinline__ void fetch(const bf16* __restrict__ src, int64_t ld, int r0, int Tn, int tid) {
     typedef BCfg<HD> C;
+    if (r0 + BS <= Tn) {
 #pragma unroll
-    for (int j = 0; j < C::NV; ++j) {
-      const int u = tid + BT * j;
-      const int row = u / C::VPR, col = (u % C::VPR) * 8;
-      const int rr = min(r0 + row, Tn - 1);
-      const u32x4_b x = *reinterpret_cast<const u32x4_b*>(src + (int64_t)rr * ld + col);
-      v[j] = r0 + row < Tn ? x : u32x4_b{0, 0, 0, 0};
+      for (int j = 0; j < C::NV; ++j) {
+        const int u = tid + BT * j;
+        const int row = u / C::VPR, col = (u % C::VPR) * 8;
+        v[j] = *reinterpret_cast<const u32x4_b*>(src + (int64_t)(r0 + row) * ld + col);
+      }
+    } else {   // the last tile: rows past the end read as zero
+#pragma unroll
+      for (int j = 0; j < C::NV; ++j) {
+        const int u = tid + BT * j;
+        const int row = u / C::VPR, col = (u % C::VPR) * 8;
+        const int rr = min(r0 + row, Tn - 1);
+        const u32x4_b x = *reinterpret_cast<const u32x4_b*>(src + (int64_t)rr * ld + col);
+        v[j] = r0 + row < Tn ? x : u32x4_b{0, 0, 0, 0};
+      }
     }
   }
   __device__ __forceinline__ void store(bf16* dst, int tid) const {
@@ -76,10 +85,7 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int pitch, int ro
   const bf16* p = tile + (row0 + 4 * G + (i16 >> 2)) * pitch + col0 + 16 * (k16 & 1) + 4 * (i16 & 3);
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_b*)p);
   const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_b*)(p + 8 * pitch));
-  bf16x8 a;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { a[e] = lo[e]; a[4 + e] = hi[e]; }
-  return a;
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 template <typename OutT>

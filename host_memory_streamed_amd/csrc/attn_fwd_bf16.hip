@@ -32,7 +32,10 @@ constexpr int FT = 256;   // threads
 
 template <int HD>
 struct F32Cfg {
-  static constexpr int P = HD + 8;          // LDS row pitch in elements (16-byte row skew)
+  static constexpr int P = HD + 8;          // K tile row pitch (elements): rows start 4 banks apart,
+                                            // conflict-free for 16-byte row reads
+  static constexpr int PV = HD + 16;        // V tile row pitch: rows start 8 banks apart, so the
+                                            // 4-row x 4-chunk transpose reads hit 32 distinct banks
   static constexpr int VPR = HD / 8;        // 16-byte vectors per row
   static constexpr int NV = FK * VPR / FT;  // vectors per thread per matrix per tile
   static constexpr int NS = HD / 16;        // 16-wide hd steps of Q K^T
@@ -43,28 +46,38 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // One 64-row tile of K or V: NV 16-byte vectors per thread, rows past the end
-// of the sequence read as zero.
+// of the sequence read as zero (only the last tile can have such rows).
 template <int HD>
 struct TileRegs {
   u32x4 v[F32Cfg<HD>::NV];
   __device__ __forceinline__ void fetch(const bf16* __restrict__ src, int64_t ld, int k0, int Tn, int tid) {
     typedef F32Cfg<HD> C;
+    if (k0 + FK <= Tn) {
 #pragma unroll
-    for (int j = 0; j < C::NV; ++j) {
-      const int u = tid + FT * j;
-      const int row = u / C::VPR, col = (u % C::VPR) * 8;
-      const int key = min(k0 + row, Tn - 1);
-      const u32x4 x = *reinterpret_cast<const u32x4*>(src + (int64_t)key * ld + col);
-      v[j] = k0 + row < Tn ? x : u32x4{0, 0, 0, 0};
+      for (int j = 0; j < C::NV; ++j) {
+        const int u = tid + FT * j;
+        const int row = u / C::VPR, col = (u % C::VPR) * 8;
+        v[j] = *reinterpret_cast<const u32x4*>(src + (int64_t)(k0 + row) * ld + col);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::NV; ++j) {
+        const int u = tid + FT * j;
+        const int row = u / C::VPR, col = (u % C::VPR) * 8;
+        const int key = min(k0 + row, Tn - 1);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(src + (int64_t)key * ld + col);
+        v[j] = k0 + row < Tn ? x : u32x4{0, 0, 0, 0};
+      }
     }
   }
+  template <int PITCH>
   __device__ __forceinline__ void store(bf16* dst, int tid) const {
     typedef F32Cfg<HD> C;
 #pragma unroll
     for (int j = 0; j < C::NV; ++j) {
       const int u = tid + FT * j;
       const int row = u / C::VPR, col = (u % C::VPR) * 8;
-      *reinterpret_cast<u32x4*>(dst + row * C::P + col) = v[j];
+      *reinterpret_cast<u32x4*>(dst + row * PITCH + col) = v[j];
     }
   }
 };
@@ -77,7 +90,7 @@ __global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __rest
                                                              int Hkv, int nq, int xcd_groups) {
   typedef F32Cfg<HD> C;
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][FK * C::P];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][FK * C::P];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][FK * C::PV];
 
   // work item: (head, query block), longest blocks first
   const int id = blockIdx.x;
@@ -126,8 +139,8 @@ __global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __rest
   TileRegs<HD> kr, vr;
   kr.fetch(Kg, ld, 0, Tn, tid);
   vr.fetch(Vg, ld, 0, Tn, tid);
-  kr.store(Ks[0], tid);
-  vr.store(Vs[0], tid);
+  kr.template store<C::P>(Ks[0], tid);
+  vr.template store<C::PV>(Vs[0], tid);
   __syncthreads();
 
   for (int kt = 0; kt < n_kt; ++kt) {
@@ -207,14 +220,12 @@ __global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __rest
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[ht][r] *= alpha;
       }
-      const bf16* vcol = Vb + ht * 32 + 16 * (k16 & 1) + 4 * (i16 & 3) + (4 * G + (i16 >> 2)) * C::P;
+      const bf16* vcol = Vb + ht * 32 + 16 * (k16 & 1) + 4 * (i16 & 3) + (4 * G + (i16 >> 2)) * C::PV;
       auto step = [&](int kk, const bf16x8& pb) {
-        const bf16* p0 = vcol + 16 * kk * C::P;
+        const bf16* p0 = vcol + 16 * kk * C::PV;
         const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 8 * C::P));
-        bf16x8 a;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { a[e] = lo[e]; a[4 + e] = hi[e]; }
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 8 * C::PV));
+        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[ht], 0, 0, 0);
       };
       if (live[0]) { step(0, pb0); step(1, pb1); }
@@ -222,8 +233,8 @@ __global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __rest
     }
 
     if (more) {
-      kr.store(Ks[buf ^ 1], tid);
-      vr.store(Vs[buf ^ 1], tid);
+      kr.template store<C::P>(Ks[buf ^ 1], tid);
+      vr.template store<C::PV>(Vs[buf ^ 1], tid);
     }
     __syncthreads();
   }
