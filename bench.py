@@ -34,10 +34,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_context(w, dtype, seed, flags, host_threads=0, chunk_rows=0, ckpt_host=0):
+def build_context(w, dtype, seed, flags, host_threads=0, chunk_rows=0, ckpt_host=0, resident=False):
     from host_memory_streamed_amd import mt, synth
     cfg = mt.make_config(w.n_layers, w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn_dim, w.vocab,
-                         w.batch, w.seq, dtype=dtype, n_layer_buffers=2, host_threads=host_threads,
+                         w.batch, w.seq, dtype=dtype, n_layer_buffers=(w.n_layers + 1 if resident else 2),
+                         host_threads=host_threads,
                          flags=flags, chunk_rows=chunk_rows, ckpt_host=ckpt_host)
     t0 = time.perf_counter()
     ctx = mt.Context(cfg)
@@ -145,6 +146,9 @@ def main():
     ap.add_argument("--trace", default=None, help="write the last step's schedule as Chrome JSON")
     ap.add_argument("--chunk-rows", type=int, default=0, help="token rows per projection/MLP chunk (0 = auto)")
     ap.add_argument("--ckpt-host", type=int, default=0, help="checkpoints parked in host memory (0 = auto)")
+    ap.add_argument("--resident", action="store_true",
+                    help="keep every layer in device memory (one buffer per unit) instead of streaming "
+                         "through two buffers")
     ap.add_argument("--sync-opt", action="store_true",
                     help="every AdamW update lands before its step returns (default: updates may finish "
                          "during the next step's forward, in the order it loads the units)")
@@ -169,7 +173,8 @@ def main():
         w = mt.Workload(**{**w.__dict__, "n_layers": args.layers})
     dtype = mt.MT_BF16 if args.dtype == "bf16" else mt.MT_FP32
     flags = mt.MT_KERNEL_TIMING | mt.MT_TRACE | (0 if args.sync_opt else mt.MT_OVERLAP_OPT)
-    ctx = build_context(w, dtype, args.seed, flags, chunk_rows=args.chunk_rows, ckpt_host=args.ckpt_host)
+    ctx = build_context(w, dtype, args.seed, flags, chunk_rows=args.chunk_rows, ckpt_host=args.ckpt_host,
+                        resident=args.resident)
     layout = ctx.layout_info()
     tokens, targets = synth.token_batch(args.seed, w.batch, w.seq, w.vocab)
     M = w.batch * w.seq
@@ -237,7 +242,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if dtype == mt.MT_BF16 else "fp32",
         "data": "synthetic",
-        "config": {"workload": w.name + "-shaped decoder, streamed through 2 layer buffers",
+        "config": {"workload": w.name + "-shaped decoder, " + ("every layer resident in device memory"
+                                                                if args.resident else "streamed through 2 layer buffers"),
                    "n_layers": w.n_layers, "d_model": w.d_model, "n_heads": w.n_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ffn_dim": w.ffn_dim,
                    "vocab": w.vocab, "global_batch": w.batch, "seq_len": w.seq,

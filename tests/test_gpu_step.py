@@ -387,6 +387,36 @@ def test_bad_token_is_rejected_before_any_work():
         assert ctx.opt_state(0)[2] == 0
         with pytest.raises(mt.MTError):
             ctx.train_step(np.zeros((B + 1, T), np.int32), np.zeros((B + 1, T), np.int32))
+        # empty batches and sequences are rejected, not run
+        for shp in ((0, T), (B, 0)):
+            with pytest.raises(mt.MTError) as e:
+                ctx.train_step(np.zeros(shp, np.int32), np.zeros(shp, np.int32))
+            assert e.value.code == mt.MT_EINVAL
+        assert ctx.opt_state(0)[2] == 0
+
+
+@pytest.mark.parametrize("mode", ["fp32", "bf16"])
+def test_step_smaller_than_allocated(mode):
+    """A context sized for 3 x 70 tokens runs a 2 x 45 step: every kernel
+    sees the actual, ragged sizes, not the allocated ones."""
+    cfg = O.Config(2, 128, 2, 1, 64, 200, 300)
+    params = init_params(cfg, 31, 0.05)
+    zeros = [np.zeros_like(p) for p in params]
+    dtype = mt.MT_BF16 if mode == "bf16" else mt.MT_FP32
+    c = mt.make_config(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn_dim,
+                       cfg.vocab, 3, 70, dtype=dtype, flags=mt.MT_KEEP_GRADS, host_threads=8)
+    with mt.Context(c, params) as ctx:
+        tokens, targets = synth.token_batch(31, 2, 45, cfg.vocab)
+        loss = ctx.train_step(tokens, targets)
+        res = O.train_step(params, zeros, zeros, 0, tokens, targets, cfg,
+                           "bf16-flash64" if mode == "bf16" else "fp32")
+        assert ctx.token_losses().shape == (2 * 45,)
+        if mode == "bf16":
+            assert abs(loss - res.loss) <= 2e-2 * abs(res.loss)
+        else:
+            assert abs(loss - res.loss) <= 1e-4 * abs(res.loss) + 1e-5
+        plain = O.train_step(params, zeros, zeros, 0, tokens, targets, cfg, "bf16") if mode == "bf16" else None
+        compare_step(ctx, res, cfg, mode, (params, zeros, zeros, 0), plain, tokens)
 
 
 def test_nonfinite_loss_applies_no_update():
