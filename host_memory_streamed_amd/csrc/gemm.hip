@@ -242,6 +242,9 @@ constexpr int BIG_STAGE = 2 * BIG_TILE_BYTES;     // A and B
 
 __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7) ^ ((row >> 3) & 7); }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
 template <typename T, bool KCONTIG>
 struct BigLoader {
   static constexpr int VE = 16 / sizeof(T);       // elements per chunk
@@ -292,6 +295,26 @@ struct BigLoader {
           }
         }
       }
+    }
+  }
+
+  // A K-contiguous stage straight from global memory into LDS, no register
+  // staging (full tiles, k0 + BK <= K). The tile is 32 blocks of 1 KB (8
+  // rows each); a global-to-LDS load writes lane l's 16 bytes at byte 16 l of
+  // its block, i.e. physical chunk l % 8 of row l / 8, so each lane fetches
+  // the logical chunk that the row's permutation puts there. Each wave fills
+  // four blocks; completion is awaited (vmcnt) before the stage's barrier.
+  __device__ __forceinline__ void direct(const T* __restrict__ base, int64_t ld, int r0, int k0, char* lds,
+                                         int tid) const {
+    static_assert(KCONTIG, "direct loads need K-contiguous rows");
+    const int w = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int j = 0; j < BIG / 8 / (BIG_THREADS / 64); ++j) {
+      const int blk = w * 4 + j;
+      const int r = blk * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ (r & 7) ^ ((r >> 3) & 7);
+      const T* p = base + (int64_t)(r0 + r) * ld + k0 + c * VE;
+      __builtin_amdgcn_global_load_lds((const glb_void_t*)p, (lds_void_t*)(lds + blk * 1024), 16, 0, 0);
     }
   }
 
@@ -387,24 +410,7 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
     for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
 
   const int nk = (K + BK - 1) / BK;
-  auto load_stage = [&](int k0) {
-    if (full && k0 + BK <= K) {
-      la.template load<false>(A, lda, m0, M, k0, K, tid);
-      lb.template load<false>(B, ldb, n0, N, k0, K, tid);
-    } else {
-      la.template load<true>(A, lda, m0, M, k0, K, tid);
-      lb.template load<true>(B, ldb, n0, N, k0, K, tid);
-    }
-  };
-  load_stage(0);
-  la.store(smem_big, tid);
-  lb.store(smem_big + BIG_TILE_BYTES, tid);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* cur = smem_big + (kt & 1) * BIG_STAGE;
-    const bool more = kt + 1 < nk;
-    if (more) load_stage((kt + 1) * BK);
+  auto mma_stage = [&](const char* cur) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int c = 2 * s + g;
@@ -427,12 +433,74 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
           }
         }
     }
-    if (more) {
-      char* nxt = smem_big + ((kt + 1) & 1) * BIG_STAGE;
-      la.store(nxt, tid);
-      lb.store(nxt + BIG_TILE_BYTES, tid);
+  };
+  // guarded stage through registers (edge tiles, the K tail)
+  auto reg_stage = [&](int k0, char* dst) {
+    la.template load<true>(A, lda, m0, M, k0, K, tid);
+    lb.template load<true>(B, ldb, n0, N, k0, K, tid);
+    la.store(dst, tid);
+    lb.store(dst + BIG_TILE_BYTES, tid);
+  };
+
+  bool done = false;
+  if constexpr (A_KC && B_KC) {
+    if (full) {
+      // full tile, both operands K-contiguous: every whole stage goes
+      // global -> LDS directly, one stage ahead; a K tail runs last
+      const int nkf = K / BK;
+      if (nkf > 0) {
+        la.direct(A, lda, m0, 0, smem_big, tid);
+        lb.direct(B, ldb, n0, 0, smem_big + BIG_TILE_BYTES, tid);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's LDS writes have landed
+        __syncthreads();
+      }
+      for (int kt = 0; kt < nkf; ++kt) {
+        const char* cur = smem_big + (kt & 1) * BIG_STAGE;
+        if (kt + 1 < nkf) {
+          char* nxt = smem_big + ((kt + 1) & 1) * BIG_STAGE;
+          la.direct(A, lda, m0, (kt + 1) * BK, nxt, tid);
+          lb.direct(B, ldb, n0, (kt + 1) * BK, nxt + BIG_TILE_BYTES, tid);
+        }
+        mma_stage(cur);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+      }
+      if (nkf < nk) {   // K tail (stage buffer nkf & 1 is free after the last barrier)
+        char* tb = smem_big + (nkf & 1) * BIG_STAGE;
+        reg_stage(nkf * BK, tb);
+        __syncthreads();
+        mma_stage(tb);
+      }
+      done = true;
     }
+  }
+  if (!done) {
+    auto load_stage = [&](int k0) {
+      if (full && k0 + BK <= K) {
+        la.template load<false>(A, lda, m0, M, k0, K, tid);
+        lb.template load<false>(B, ldb, n0, N, k0, K, tid);
+      } else {
+        la.template load<true>(A, lda, m0, M, k0, K, tid);
+        lb.template load<true>(B, ldb, n0, N, k0, K, tid);
+      }
+    };
+    load_stage(0);
+    la.store(smem_big, tid);
+    lb.store(smem_big + BIG_TILE_BYTES, tid);
     __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* cur = smem_big + (kt & 1) * BIG_STAGE;
+      const bool more = kt + 1 < nk;
+      if (more) load_stage((kt + 1) * BK);
+      mma_stage(cur);
+      if (more) {
+        char* nxt = smem_big + ((kt + 1) & 1) * BIG_STAGE;
+        la.store(nxt, tid);
+        lb.store(nxt + BIG_TILE_BYTES, tid);
+      }
+      __syncthreads();
+    }
   }
 
 #pragma unroll
