@@ -18,6 +18,8 @@
 // each slot holds. Workgroups are remapped so that consecutive tile ids land
 // on the same XCD (each of the 8 XCDs has its own L2) and walk the output in
 // groups of 8 tile rows.
+#include <type_traits>
+
 #include "dev_common.h"
 #include "kernels.h"
 
@@ -357,6 +359,75 @@ struct BigLoader {
   }
 };
 
+// bf16 operand whose rows run along M or N (A of TN, B of NN and TN): it stays
+// in its natural layout, one 512-byte LDS row per k (256 elements, 32 chunks
+// of 16 bytes), chunk c of row r stored at c ^ ((r & 3) << 1). A fragment for
+// 32 consecutive m (or n) and 8 consecutive k per lane group comes from two
+// LDS transpose reads of 4 k each, in the k-slot order of a K-contiguous
+// fragment; with the permutation each 16-lane transpose read (4 rows x 2
+// chunks) covers 32 distinct banks.
+struct BigNat {
+  static constexpr int VE = 8;
+  static constexpr int ROWB = 512;
+  static constexpr int NV = 64 * 32 / BIG_THREADS;   // chunks per thread per stage
+  Vec16 v[NV];
+  static __device__ __forceinline__ int pchunk(int row, int c) { return c ^ ((row & 3) << 1); }
+
+  template <bool CHECK>
+  __device__ __forceinline__ void load(const bf16* __restrict__ base, int64_t ld, int r0, int rows, int k0,
+                                       int K, int tid) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int q = tid + BIG_THREADS * j;
+      const int row = q >> 5, c = q & 31;
+      const int kk = k0 + row, gc = r0 + c * VE;
+      const bf16* p = base + (int64_t)kk * ld + gc;
+      if (!CHECK || (kk < K && gc + VE <= rows)) {
+        v[j] = *reinterpret_cast<const Vec16*>(p);
+      } else {
+        bf16 tmp[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) tmp[e] = (kk < K && gc + e < rows) ? p[e] : bf16(0.f);
+        __builtin_memcpy(&v[j], tmp, 16);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int q = tid + BIG_THREADS * j;
+      const int row = q >> 5, c = q & 31;
+      *reinterpret_cast<Vec16*>(lds + row * ROWB + (pchunk(row, c) << 4)) = v[j];
+    }
+  }
+  // Global -> LDS for a full stage: each wave fills four 1-KB blocks (two rows
+  // each); lane l lands on physical chunk l % 32 of row l / 32 of its block and
+  // fetches the logical chunk the permutation puts there.
+  __device__ __forceinline__ void direct(const bf16* __restrict__ base, int64_t ld, int r0, int k0, char* lds,
+                                         int tid) const {
+    const int w = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int blk = w * 4 + j;
+      const int row = 2 * blk + (lane >> 5);
+      const int c = pchunk(row, lane & 31);
+      const bf16* p = base + (int64_t)(k0 + row) * ld + r0 + c * VE;
+      __builtin_amdgcn_global_load_lds((const glb_void_t*)p, (lds_void_t*)(lds + blk * 1024), 16, 0, 0);
+    }
+  }
+  // MFMA fragment: 32 consecutive m (or n) from mn0, k-step s (16 k)
+  static __device__ __forceinline__ bf16x8 frag(const char* tile, int mn0, int s, int lane) {
+    typedef __attribute__((address_space(3))) bf16x4 lds4;
+    const int k16 = lane >> 4, i16 = lane & 15, G = lane >> 5, e = i16 >> 2, q = i16 & 3;
+    const int col = mn0 + 16 * (k16 & 1) + 4 * q;
+    const int row = 16 * s + 8 * G + e;                 // the second read is 4 rows on (same row & 3)
+    const int off = ((pchunk(row, col >> 3)) << 4) + (col & 7) * 2;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(tile + row * ROWB + off));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(tile + (row + 4) * ROWB + off));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
 template <typename T, int LAYOUT>
 __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __restrict__ A, int64_t lda,
                                                                   const T* __restrict__ B, int64_t ldb,
@@ -365,6 +436,10 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
                                                                   int tiles_m, int tiles_n) {
   constexpr bool A_KC = (LAYOUT != MT_GEMM_TN);
   constexpr bool B_KC = (LAYOUT == MT_GEMM_NT);
+  // bf16 M/N-contiguous operands stay in their natural layout (BigNat);
+  // fp32 ones are transposed into K-contiguous LDS rows on the way in
+  constexpr bool A_NAT = !A_KC && sizeof(T) == 2;
+  constexpr bool B_NAT = !B_KC && sizeof(T) == 2;
   typedef Mfma32<T> MF;
   constexpr int BK = BIG_ROW / sizeof(T);
   constexpr int NSUB = 16 / (MF::KL * (int)sizeof(T));   // instructions per 16-byte chunk
@@ -401,8 +476,8 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
     b_x[j] = (r & 7) ^ ((r >> 3) & 7);
   }
 
-  BigLoader<T, A_KC> la;
-  BigLoader<T, B_KC> lb;
+  typename std::conditional<A_NAT, BigNat, BigLoader<T, A_KC>>::type la;
+  typename std::conditional<B_NAT, BigNat, BigLoader<T, B_KC>>::type lb;
   floatx16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -411,6 +486,30 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
 
   const int nk = (K + BK - 1) / BK;
   auto mma_stage = [&](const char* cur) {
+    if constexpr (A_NAT || B_NAT) {
+      // bf16 with a natural-layout operand: one 16-k MFMA step per s
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int c = 2 * s + g;
+        bf16x8 af[4], bfr[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (A_NAT) af[i] = BigNat::frag(cur, wm * 128 + i * 32, s, lane);
+          else af[i] = *reinterpret_cast<const bf16x8*>(cur + a_base[i] + ((c ^ a_x[i]) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if constexpr (B_NAT) bfr[j] = BigNat::frag(cur + BIG_TILE_BYTES, wn * 64 + j * 32, s, lane);
+          else bfr[j] = *reinterpret_cast<const bf16x8*>(cur + b_base[j] + ((c ^ b_x[j]) << 4));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int c = 2 * s + g;
@@ -443,10 +542,10 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
   };
 
   bool done = false;
-  if constexpr (A_KC && B_KC) {
+  if constexpr ((A_KC || A_NAT) && (B_KC || B_NAT)) {
     if (full) {
-      // full tile, both operands K-contiguous: every whole stage goes
-      // global -> LDS directly, one stage ahead; a K tail runs last
+      // full tile with both operands loadable straight into LDS: every whole
+      // stage goes global -> LDS directly, one stage ahead; a K tail runs last
       const int nkf = K / BK;
       if (nkf > 0) {
         la.direct(A, lda, m0, 0, smem_big, tid);
