@@ -22,6 +22,8 @@
 #include "dev_common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace mt {
 namespace {
 
@@ -31,60 +33,99 @@ constexpr int BW = 128;   // keys (dK/dV) or queries (dQ) per workgroup
 constexpr int BS = 64;    // rows per streamed tile
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_b;
-typedef uint32_t u32x4_b __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_b;
+typedef __attribute__((address_space(1))) void glb_void_b;
 
+// A 64-row tile of HD bf16 columns in LDS, rows unpadded. The 16-byte chunks
+// of row r sit in the order chunk ^ perm(r), perm depending on r mod 16 only.
+// LDS serves 64 four-byte banks per cycle: a 16-byte row read takes 16 lanes
+// per cycle (16 rows, one chunk) and a transpose read 32 lanes (4 rows x 4
+// chunks), and the permutation gives each of those groups 16 distinct chunk
+// positions modulo 256 bytes, so neither read pattern has a bank conflict.
+// The tile is copied global -> LDS directly in 1 KB wave pieces whose lanes
+// fetch their source chunk through the same permutation.
 template <int HD>
-struct BCfg {
-  static constexpr int P = HD + 8;          // LDS row pitch (elements)
-  static constexpr int VPR = HD / 8;        // 16-byte vectors per row
-  static constexpr int NV = BS * VPR / BT;  // vectors per thread per tile
-  static constexpr int NS = HD / 16;        // 16-wide hd steps
-  static constexpr int NH = HD / 32;        // 32-row hd sub-tiles
-};
-
-template <int HD>
-struct Tile64 {
-  u32x4_b v[BCfg<HD>::NV];
-  __device__ __forceinline__ void fetch(const bf16* __restrict__ src, int64_t ld, int r0, int Tn, int tid) {
-    typedef BCfg<HD> C;
-    if (r0 + BS <= Tn) {
-#pragma unroll
-      for (int j = 0; j < C::NV; ++j) {
-        const int u = tid + BT * j;
-        const int row = u / C::VPR, col = (u % C::VPR) * 8;
-        v[j] = *reinterpret_cast<const u32x4_b*>(src + (int64_t)(r0 + row) * ld + col);
-      }
-    } else {   // the last tile: rows past the end read as zero
-#pragma unroll
-      for (int j = 0; j < C::NV; ++j) {
-        const int u = tid + BT * j;
-        const int row = u / C::VPR, col = (u % C::VPR) * 8;
-        const int rr = min(r0 + row, Tn - 1);
-        const u32x4_b x = *reinterpret_cast<const u32x4_b*>(src + (int64_t)rr * ld + col);
-        v[j] = r0 + row < Tn ? x : u32x4_b{0, 0, 0, 0};
-      }
-    }
+struct Swz {
+  static constexpr int NS = HD / 16;                  // 16-wide hd steps
+  static constexpr int NH = HD / 32;                  // 32-row hd sub-tiles
+  static constexpr int ELEMS = BS * HD;
+  static constexpr int WP = BS * HD * 2 / 1024 / (BT / 64);   // 1 KB pieces per wave
+  __device__ static __forceinline__ int perm(int r) {
+    if constexpr (HD == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
   }
-  __device__ __forceinline__ void store(bf16* dst, int tid) const {
-    typedef BCfg<HD> C;
-#pragma unroll
-    for (int j = 0; j < C::NV; ++j) {
-      const int u = tid + BT * j;
-      const int row = u / C::VPR, col = (u % C::VPR) * 8;
-      *reinterpret_cast<u32x4_b*>(dst + row * C::P + col) = v[j];
-    }
+  // element offset of column col (col % 8 < 8 stays in its chunk) of row r
+  __device__ static __forceinline__ int at(int r, int col) { return r * HD + 8 * ((col >> 3) ^ perm(r)) + (col & 7); }
+  // row and column of the chunk that lane lands in piece j of wave w
+  __device__ static __forceinline__ void piece(int w, int j, int lane, int& r, int& col) {
+    const int e = (w * WP + j) * 512 + lane * 8;
+    r = e / HD;
+    col = 8 * (((e % HD) >> 3) ^ perm(r));
   }
 };
 
-// A operand of a 16-row contraction step read transposed from a row-major
-// LDS tile: lane (column col0 + lane%32, slot group G) receives rows
-// row0 + 4G + 0..3 and row0 + 8 + 4G + 0..3 of its column, the slot order
-// of a 32x32 accumulator's rows.
-__device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int pitch, int row0, int col0, int lane) {
-  const int k16 = lane >> 4, i16 = lane & 15, G = lane >> 5;
-  const bf16* p = tile + (row0 + 4 * G + (i16 >> 2)) * pitch + col0 + 16 * (k16 & 1) + 4 * (i16 & 3);
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_b*)p);
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_b*)(p + 8 * pitch));
+// The per-lane source byte offsets of one tensor's tiles (row stride ld).
+template <int HD>
+struct TileCopy {
+  typedef Swz<HD> S;
+  uint32_t off[S::WP];
+  __device__ __forceinline__ void init(int64_t ld, int w, int lane) {
+#pragma unroll
+    for (int j = 0; j < S::WP; ++j) {
+      int r, col;
+      S::piece(w, j, lane, r, col);
+      off[j] = (uint32_t)(((int64_t)r * ld + col) * 2);
+    }
+  }
+  // rows r0 .. r0+63 of src; rows at or past n (r0 < n) repeat row n-1, whose
+  // products the callers mask. Completion: vmcnt(0), then a barrier.
+  __device__ __forceinline__ void copy(bf16* tile, const bf16* src, int64_t ld, int r0, int n, int w,
+                                       int lane) const {
+    const char* base = reinterpret_cast<const char*>(src + (int64_t)r0 * ld);
+    if (r0 + BS <= n) {
+#pragma unroll
+      for (int j = 0; j < S::WP; ++j)
+        __builtin_amdgcn_global_load_lds((glb_void_b*)(base + off[j]), (lds_void_b*)(tile + (w * S::WP + j) * 512),
+                                         16, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < S::WP; ++j) {
+        int r, col;
+        S::piece(w, j, lane, r, col);
+        const int64_t o = ((int64_t)min(r, n - 1 - r0) * ld + col) * 2;
+        __builtin_amdgcn_global_load_lds((glb_void_b*)(base + o), (lds_void_b*)(tile + (w * S::WP + j) * 512), 16, 0,
+                                         0);
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// Per-lane offsets of the two transpose reads of a 16-row contraction step
+// (rows 4G + 0..3 and 8 + 4G + 0..3 of a 16-row block, column block ht).
+template <int HD>
+struct TrOffsets {
+  int o[Swz<HD>::NH][2];
+  __device__ __forceinline__ void init(int lane) {
+    const int k16 = lane >> 4, i16 = lane & 15, G = lane >> 5;
+#pragma unroll
+    for (int ht = 0; ht < Swz<HD>::NH; ++ht)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        o[ht][h] = Swz<HD>::at(4 * G + (i16 >> 2) + 8 * h, ht * 32 + 16 * (k16 & 1) + 4 * (i16 & 3));
+  }
+};
+
+// A operand of a 16-row contraction step read transposed from a swizzled tile:
+// lane (column ht*32 + lane%32, slot group G) receives rows row0 + 4G + 0..3
+// and row0 + 8 + 4G + 0..3 of its column (row0 a multiple of 16), the slot
+// order of a 32x32 accumulator's rows.
+template <int HD>
+__device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int row0, int ht, const TrOffsets<HD>& t) {
+  const bf16* p = tile + row0 * HD;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_b*)(p + t.o[ht][0]));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_b*)(p + t.o[ht][1]));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -171,9 +212,11 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
                                                              const float* __restrict__ rcos,
                                                              const float* __restrict__ rsin, int Tn,
                                                              int H, int Hkv, int nkb, int xcd_groups) {
-  typedef BCfg<HD> C;
-  __shared__ __attribute__((aligned(16))) bf16 Qs[2][BS * C::P];
-  __shared__ __attribute__((aligned(16))) bf16 Os[2][BS * C::P];
+  typedef Swz<HD> C;
+  // one array per buffer: the compiler then sees that a copy in flight into
+  // one buffer does not alias reads of the other and does not wait for it
+  __shared__ __attribute__((aligned(1024))) bf16 Q0[C::ELEMS], Q1[C::ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 O0[C::ELEMS], O1[C::ELEMS];
   __shared__ __attribute__((aligned(16))) float Ls[2][BS];
   __shared__ __attribute__((aligned(16))) float Dsh[2][BS];
 
@@ -217,41 +260,43 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
     for (int r = 0; r < 16; ++r) dk[i][r] = dv[i][r] = 0.f;
   const float sl2 = B_LOG2E / sqrtf((float)HD);
 
+  TileCopy<HD> cq, co;
+  cq.init(ld, w, lane);
+  co.init(ldo, w, lane);
+  TrOffsets<HD> tro;
+  tro.init(lane);
+  int rro[C::NS];   // this lane's row-read offsets: row c, hd columns 16 ss + 8 G
+#pragma unroll
+  for (int ss = 0; ss < C::NS; ++ss) rro[ss] = C::at(c, 16 * ss + 8 * G);
+
   // query tiles at or after the block's first key, for every head of the group
   const int qt0 = (kb * BW) / BS;
   const int nqt = (Tn + BS - 1) / BS - qt0;
   const int n_it = grp * nqt;
 
-  Tile64<HD> qr, orr;
   float lv = 0.f;
-  auto fetch = [&](int it) {
+  auto issue = [&](int it, bf16* Qn, bf16* On) __attribute__((always_inline)) {
     const int h = kvh * grp + it / nqt;
     const int q0 = (qt0 + it % nqt) * BS;
-    qr.fetch(base + h * HD, ld, q0, Tn, tid);
-    orr.fetch(dbase + h * HD, ldo, q0, Tn, tid);
+    cq.copy(Qn, base + h * HD, ld, q0, Tn, w, lane);
+    co.copy(On, dbase + h * HD, ldo, q0, Tn, w, lane);
     if (tid < 2 * BS) {
       const int qi = min(q0 + (tid & (BS - 1)), Tn - 1);
       const int64_t idx = ((int64_t)b * H + h) * Tn + qi;
-      lv = tid < BS ? lse[idx] * B_LOG2E : Dv[idx];
+      lv = tid < BS ? lse[idx] : Dv[idx];
     }
   };
-  auto stash = [&](int buf) {
-    qr.store(Qs[buf], tid);
-    orr.store(Os[buf], tid);
-    if (tid < BS) Ls[buf][tid] = lv;
+  auto stash = [&](int buf) __attribute__((always_inline)) {
+    if (tid < BS) Ls[buf][tid] = lv * B_LOG2E;
     else if (tid < 2 * BS) Dsh[buf][tid - BS] = lv;
   };
-  fetch(0);
-  stash(0);
-  __syncthreads();
 
-  for (int it = 0; it < n_it; ++it) {
-    const int buf = it & 1;
+  // one query tile: Q and dO of tile it in (Qb, Ob), tile it+1 copied into (Qn, On)
+  auto tile = [&](int it, const bf16* Qb, const bf16* Ob, bf16* Qn, bf16* On, int buf)
+      __attribute__((always_inline)) {
     const int q0 = (qt0 + it % nqt) * BS;
     const bool more = it + 1 < n_it;
-    if (more) fetch(it + 1);
-    const bf16* Qb = Qs[buf];
-    const bf16* Ob = Os[buf];
+    if (more) issue(it + 1, Qn, On);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int qs0 = q0 + 32 * u;
@@ -259,47 +304,60 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
       floatx16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-      const bf16* qrow = Qb + (32 * u + c) * C::P + G * 8;
-      const bf16* orow = Ob + (32 * u + c) * C::P + G * 8;
 #pragma unroll
       for (int ss = 0; ss < C::NS; ++ss) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qrow + ss * 16);
-        const bf16x8 a2 = *reinterpret_cast<const bf16x8*>(orow + ss * 16);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Qb + 32 * u * HD + rro[ss]);
+        const bf16x8 a2 = *reinterpret_cast<const bf16x8*>(Ob + 32 * u * HD + rro[ss]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ss], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, vf[ss], dp, 0, 0, 0);
       }
       // rows are queries qs0 + (r/4)*8 + G*4 + r%4, the column is this lane's
       // key; masking only where the sub-tile meets the diagonal or the end
-      const bool edge = qs0 < kw0 + 31 || qs0 + 31 >= Tn;
       bf16x8 pb0, pb1, db0, db1;
+      auto grads = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int qr4 = 32 * u + r4 * 8 + G * 4;
-        const floatx4 lq = *reinterpret_cast<const floatx4*>(&Ls[buf][qr4]);
-        const floatx4 dq4 = *reinterpret_cast<const floatx4*>(&Dsh[buf][qr4]);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int qr4 = 32 * u + r4 * 8 + G * 4;
+          const floatx4 lq = *reinterpret_cast<const floatx4*>(&Ls[buf][qr4]);
+          const floatx4 dq4 = *reinterpret_cast<const floatx4*>(&Dsh[buf][qr4]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = r4 * 4 + e;
-          float pv = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lq[e]));
-          if (edge) {
-            const int qi = q0 + qr4 + e;
-            if (!(key <= qi && qi < Tn)) pv = 0.f;
+          for (int e = 0; e < 4; ++e) {
+            const int r = r4 * 4 + e;
+            float pv = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lq[e]));
+            if constexpr (decltype(masked)::value) {
+              const int qi = q0 + qr4 + e;
+              if (!(key <= qi && qi < Tn)) pv = 0.f;
+            }
+            const float dsv = pv * (dp[r] - dq4[e]);
+            if (r < 8) { pb0[r] = to_bf16(pv); db0[r] = to_bf16(dsv); }
+            else { pb1[r - 8] = to_bf16(pv); db1[r - 8] = to_bf16(dsv); }
           }
-          const float dsv = pv * (dp[r] - dq4[e]);
-          if (r < 8) { pb0[r] = to_bf16(pv); db0[r] = to_bf16(dsv); }
-          else { pb1[r - 8] = to_bf16(pv); db1[r - 8] = to_bf16(dsv); }
         }
-      }
+      };
+      if (qs0 < kw0 + 31 || qs0 + 31 >= Tn) grads(std::true_type{});
+      else grads(std::false_type{});
 #pragma unroll
       for (int ht = 0; ht < C::NH; ++ht) {
-        dv[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Ob, C::P, 32 * u, ht * 32, lane), pb0, dv[ht], 0, 0, 0);
-        dv[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Ob, C::P, 32 * u + 16, ht * 32, lane), pb1, dv[ht], 0, 0, 0);
-        dk[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Qb, C::P, 32 * u, ht * 32, lane), db0, dk[ht], 0, 0, 0);
-        dk[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Qb, C::P, 32 * u + 16, ht * 32, lane), db1, dk[ht], 0, 0, 0);
+        dv[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Ob, 32 * u, ht, tro), pb0, dv[ht], 0, 0, 0);
+        dv[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Ob, 32 * u + 16, ht, tro), pb1, dv[ht], 0, 0, 0);
+        dk[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Qb, 32 * u, ht, tro), db0, dk[ht], 0, 0, 0);
+        dk[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Qb, 32 * u + 16, ht, tro), db1, dk[ht], 0, 0, 0);
       }
     }
-    if (more) stash(buf ^ 1);
+    if (more) {
+      wait_copies();
+      stash(buf ^ 1);
+    }
     __syncthreads();
+  };
+
+  issue(0, Q0, O0);
+  wait_copies();
+  stash(0);
+  __syncthreads();
+  for (int it = 0; it < n_it; it += 2) {
+    tile(it, Q0, O0, Q1, O1, 0);
+    if (it + 1 < n_it) tile(it + 1, Q1, O1, Q0, O0, 1);
   }
 
   if (key < Tn) {
@@ -320,9 +378,10 @@ __global__ __launch_bounds__(BT, 2) void attn_dq_bf16_kernel(const bf16* __restr
                                                             const float* __restrict__ rcos,
                                                             const float* __restrict__ rsin, int Tn,
                                                             int H, int Hkv, int nq, int xcd_groups) {
-  typedef BCfg<HD> C;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BS * C::P];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][BS * C::P];
+  typedef Swz<HD> C;
+  // one array per buffer (see the dK/dV pass)
+  __shared__ __attribute__((aligned(1024))) bf16 K0[C::ELEMS], K1[C::ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 V0[C::ELEMS], V1[C::ELEMS];
 
   const int id = blockIdx.x;
   int h, qb;
@@ -369,25 +428,23 @@ __global__ __launch_bounds__(BT, 2) void attn_dq_bf16_kernel(const bf16* __restr
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[i][r] = 0.f;
 
+  TileCopy<HD> ck;   // K and V rows share the stride
+  ck.init(ld, w, lane);
+  TrOffsets<HD> tro;
+  tro.init(lane);
+  int rro[C::NS];
+#pragma unroll
+  for (int ss = 0; ss < C::NS; ++ss) rro[ss] = C::at(c, 16 * ss + 8 * G);
+
   const int q_hi = min(Tn, qb * BW + BW);
   const int n_kt = (q_hi - 1) / BS + 1;
-  Tile64<HD> kr, vr;
-  kr.fetch(Kg, ld, 0, Tn, tid);
-  vr.fetch(Vg, ld, 0, Tn, tid);
-  kr.store(Ks[0], tid);
-  vr.store(Vs[0], tid);
-  __syncthreads();
-
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
+  auto tile = [&](int kt, const bf16* Kb, const bf16* Vb, bf16* Kn, bf16* Vn) __attribute__((always_inline)) {
     const int k0 = kt * BS;
     const bool more = kt + 1 < n_kt;
     if (more) {
-      kr.fetch(Kg, ld, k0 + BS, Tn, tid);
-      vr.fetch(Vg, ld, k0 + BS, Tn, tid);
+      ck.copy(Kn, Kg, ld, k0 + BS, Tn, w, lane);
+      ck.copy(Vn, Vg, ld, k0 + BS, Tn, w, lane);
     }
-    const bf16* Kb = Ks[buf];
-    const bf16* Vb = Vs[buf];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int kb0 = k0 + 32 * st;
@@ -395,41 +452,48 @@ __global__ __launch_bounds__(BT, 2) void attn_dq_bf16_kernel(const bf16* __restr
       floatx16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-      const bf16* krow = Kb + (32 * st + c) * C::P + G * 8;
-      const bf16* vrow = Vb + (32 * st + c) * C::P + G * 8;
 #pragma unroll
       for (int ss = 0; ss < C::NS; ++ss) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + ss * 16);
-        const bf16x8 a2 = *reinterpret_cast<const bf16x8*>(vrow + ss * 16);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + 32 * st * HD + rro[ss]);
+        const bf16x8 a2 = *reinterpret_cast<const bf16x8*>(Vb + 32 * st * HD + rro[ss]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ss], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, df[ss], dp, 0, 0, 0);
       }
       // rows are keys kb0 + (r/4)*8 + G*4 + r%4, the column is this lane's
       // query; masking only where the sub-tile meets the diagonal or the end
-      const bool edge = kb0 + 31 > wq0 || wq0 + 31 >= Tn;
       bf16x8 db0, db1;
+      auto grads = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2));
-        if (edge) {
-          const int kk = kb0 + (r >> 2) * 8 + G * 4 + (r & 3);
-          if (!(kk <= q && q < Tn)) pv = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2));
+          if constexpr (decltype(masked)::value) {
+            const int kk = kb0 + (r >> 2) * 8 + G * 4 + (r & 3);
+            if (!(kk <= q && q < Tn)) pv = 0.f;
+          }
+          const float dsv = pv * (dp[r] - Dq);
+          if (r < 8) db0[r] = to_bf16(dsv);
+          else db1[r - 8] = to_bf16(dsv);
         }
-        const float dsv = pv * (dp[r] - Dq);
-        if (r < 8) db0[r] = to_bf16(dsv);
-        else db1[r - 8] = to_bf16(dsv);
-      }
+      };
+      if (kb0 + 31 > wq0 || wq0 + 31 >= Tn) grads(std::true_type{});
+      else grads(std::false_type{});
 #pragma unroll
       for (int ht = 0; ht < C::NH; ++ht) {
-        dq[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Kb, C::P, 32 * st, ht * 32, lane), db0, dq[ht], 0, 0, 0);
-        dq[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Kb, C::P, 32 * st + 16, ht * 32, lane), db1, dq[ht], 0, 0, 0);
+        dq[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Kb, 32 * st, ht, tro), db0, dq[ht], 0, 0, 0);
+        dq[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Kb, 32 * st + 16, ht, tro), db1, dq[ht], 0, 0, 0);
       }
     }
-    if (more) {
-      kr.store(Ks[buf ^ 1], tid);
-      vr.store(Vs[buf ^ 1], tid);
-    }
+    if (more) wait_copies();
     __syncthreads();
+  };
+
+  ck.copy(K0, Kg, ld, 0, Tn, w, lane);
+  ck.copy(V0, Vg, ld, 0, Tn, w, lane);
+  wait_copies();
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    tile(kt, K0, V0, K1, V1);
+    if (kt + 1 < n_kt) tile(kt + 1, K1, V1, K0, V0);
   }
 
   if (q < Tn) {
