@@ -7,13 +7,14 @@
 //
 //  - a workgroup owns 128 queries of one head (4 waves x 32 queries), so each
 //    K/V tile brought on chip serves 128 queries;
-//  - 64-key K and V tiles are double buffered in LDS: the global loads of
-//    tile k+1 are in flight while tile k is consumed, one barrier per tile;
+//  - 64-key K and V tiles are double buffered in LDS and copied there
+//    straight from global memory: tile k+1 is in flight while tile k is
+//    consumed, one barrier per tile;
 //  - S^T = K Q^T runs with K rows from LDS as the A operand and the wave's 32
 //    queries held in registers as B; O^T += V^T P^T takes P^T straight from
 //    the S^T accumulator (the k-slots of each 16-key step are ordered as the
-//    accumulator holds them) and V^T from the row-major V tile through the
-//    LDS transpose read, two 4-key reads per step;
+//    accumulator holds them) and V^T from the V tile through the LDS
+//    transpose read, two 4-key reads per step;
 //  - key sub-tiles that lie wholly above a wave's last query are skipped;
 //  - work items are numbered so that the query blocks of one head run on the
 //    same XCD (workgroup i goes to XCD i % 8) and share its L2, longest
@@ -32,52 +33,64 @@ constexpr int FT = 256;   // threads
 
 template <int HD>
 struct F32Cfg {
-  static constexpr int P = HD + 8;          // K tile row pitch (elements): rows start 4 banks apart,
-                                            // conflict-free for 16-byte row reads
-  static constexpr int PV = HD + 16;        // V tile row pitch: rows start 8 banks apart, so the
-                                            // 4-row x 4-chunk transpose reads hit 32 distinct banks
-  static constexpr int VPR = HD / 8;        // 16-byte vectors per row
-  static constexpr int NV = FK * VPR / FT;  // vectors per thread per matrix per tile
   static constexpr int NS = HD / 16;        // 16-wide hd steps of Q K^T
   static constexpr int NH = HD / 32;        // 32-row hd sub-tiles of O^T
+  static constexpr int ELEMS = FK * HD;
+  static constexpr int WP = FK * HD * 2 / 1024 / (FT / 64);   // 1 KB copy pieces per wave
+  // K and V tiles are stored without padding, the 16-byte chunks of row r in
+  // the order chunk ^ perm(r) (perm depends on r mod 16). LDS serves 64
+  // four-byte banks per cycle: 16 lanes of a 16-byte row read (16 rows, one
+  // chunk) and 32 lanes of a transpose read (4 rows x 4 chunks) then fall on
+  // 16 distinct chunk positions modulo 256 bytes, free of bank conflicts.
+  __device__ static __forceinline__ int perm(int r) {
+    if constexpr (HD == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+  __device__ static __forceinline__ int at(int r, int col) { return r * HD + 8 * ((col >> 3) ^ perm(r)); }
 };
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_f;
+typedef __attribute__((address_space(1))) void glb_void_f;
 
-// One 64-row tile of K or V: NV 16-byte vectors per thread, rows past the end
-// of the sequence read as zero (only the last tile can have such rows).
+// Direct global -> LDS copy of a 64-row K or V tile: wave w fills 1 KB pieces
+// w*WP .. w*WP+WP-1, lane i landing 16 bytes at piece + 16 i; each lane
+// fetches the chunk that the permuted layout puts there. Rows at or past the
+// end of the sequence repeat the last row (those keys are masked).
 template <int HD>
-struct TileRegs {
-  u32x4 v[F32Cfg<HD>::NV];
-  __device__ __forceinline__ void fetch(const bf16* __restrict__ src, int64_t ld, int k0, int Tn, int tid) {
-    typedef F32Cfg<HD> C;
-    if (k0 + FK <= Tn) {
+struct TileCopyF {
+  typedef F32Cfg<HD> C;
+  uint32_t off[C::WP];
+  __device__ __forceinline__ static void piece(int w, int j, int lane, int& r, int& col) {
+    const int e = (w * C::WP + j) * 512 + lane * 8;
+    r = e / HD;
+    col = 8 * (((e % HD) >> 3) ^ C::perm(r));
+  }
+  __device__ __forceinline__ void init(int64_t ld, int w, int lane) {
 #pragma unroll
-      for (int j = 0; j < C::NV; ++j) {
-        const int u = tid + FT * j;
-        const int row = u / C::VPR, col = (u % C::VPR) * 8;
-        v[j] = *reinterpret_cast<const u32x4*>(src + (int64_t)(k0 + row) * ld + col);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < C::NV; ++j) {
-        const int u = tid + FT * j;
-        const int row = u / C::VPR, col = (u % C::VPR) * 8;
-        const int key = min(k0 + row, Tn - 1);
-        const u32x4 x = *reinterpret_cast<const u32x4*>(src + (int64_t)key * ld + col);
-        v[j] = k0 + row < Tn ? x : u32x4{0, 0, 0, 0};
-      }
+    for (int j = 0; j < C::WP; ++j) {
+      int r, col;
+      piece(w, j, lane, r, col);
+      off[j] = (uint32_t)(((int64_t)r * ld + col) * 2);
     }
   }
-  template <int PITCH>
-  __device__ __forceinline__ void store(bf16* dst, int tid) const {
-    typedef F32Cfg<HD> C;
+  __device__ __forceinline__ void copy(bf16* tile, const bf16* src, int64_t ld, int k0, int Tn, int w,
+                                       int lane) const {
+    const char* base = reinterpret_cast<const char*>(src + (int64_t)k0 * ld);
+    if (k0 + FK <= Tn) {
 #pragma unroll
-    for (int j = 0; j < C::NV; ++j) {
-      const int u = tid + FT * j;
-      const int row = u / C::VPR, col = (u % C::VPR) * 8;
-      *reinterpret_cast<u32x4*>(dst + row * PITCH + col) = v[j];
+      for (int j = 0; j < C::WP; ++j)
+        __builtin_amdgcn_global_load_lds((glb_void_f*)(base + off[j]), (lds_void_f*)(tile + (w * C::WP + j) * 512),
+                                         16, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::WP; ++j) {
+        int r, col;
+        piece(w, j, lane, r, col);
+        const int64_t o = ((int64_t)min(r, Tn - 1 - k0) * ld + col) * 2;
+        __builtin_amdgcn_global_load_lds((glb_void_f*)(base + o), (lds_void_f*)(tile + (w * C::WP + j) * 512), 16,
+                                         0, 0);
+      }
     }
   }
 };
@@ -89,8 +102,10 @@ __global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __rest
                                                              float* __restrict__ lse, int Tn, int H,
                                                              int Hkv, int nq, int xcd_groups) {
   typedef F32Cfg<HD> C;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][FK * C::P];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][FK * C::PV];
+  // one array per buffer: the compiler then sees that the copy in flight into
+  // one buffer does not alias the reads of the other and does not wait for it
+  __shared__ __attribute__((aligned(1024))) bf16 K0[C::ELEMS], K1[C::ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 V0[C::ELEMS], V1[C::ELEMS];
 
   // work item: (head, query block), longest blocks first
   const int id = blockIdx.x;
@@ -136,28 +151,32 @@ __global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __rest
   const int q_hi = min(Tn, qb * FQ + FQ);   // end of the block's valid queries
   const int n_kt = (q_hi - 1) / FK + 1;
 
-  TileRegs<HD> kr, vr;
-  kr.fetch(Kg, ld, 0, Tn, tid);
-  vr.fetch(Vg, ld, 0, Tn, tid);
-  kr.template store<C::P>(Ks[0], tid);
-  vr.template store<C::PV>(Vs[0], tid);
-  __syncthreads();
+  TileCopyF<HD> cp;   // K and V rows share the stride
+  cp.init(ld, w, lane);
+  int rro[C::NS];     // K row reads: row c, hd columns 16 ss + 8 G
+#pragma unroll
+  for (int ss = 0; ss < C::NS; ++ss) rro[ss] = C::at(c, 16 * ss + 8 * G);
+  int tro[C::NH][2];  // V transpose reads: rows 4G + i16/4 (+8), columns ht*32 + 16 (k16&1) + 4 (i16&3)
+#pragma unroll
+  for (int ht = 0; ht < C::NH; ++ht)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int col = ht * 32 + 16 * (k16 & 1) + 4 * (i16 & 3);
+      tro[ht][hh] = C::at(4 * G + (i16 >> 2) + 8 * hh, col) + (col & 7);
+    }
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
+  auto tile = [&](int kt, const bf16* Kb, const bf16* Vb, bf16* Kn, bf16* Vn) __attribute__((always_inline)) {
     const int k0 = kt * FK;
     const bool more = kt + 1 < n_kt;
     if (more) {
-      kr.fetch(Kg, ld, k0 + FK, Tn, tid);
-      vr.fetch(Vg, ld, k0 + FK, Tn, tid);
+      cp.copy(Kn, Kg, ld, k0 + FK, Tn, w, lane);
+      cp.copy(Vn, Vg, ld, k0 + FK, Tn, w, lane);
     }
-    const bf16* Kb = Ks[buf];
-    const bf16* Vb = Vs[buf];
 
     // raw scores of the two 32-key sub-tiles (wave-uniform skip above the
-    // diagonal; masking only on sub-tiles that cross it). The running maximum
-    // is taken on raw scores (the scale is positive, so it commutes with the
-    // maximum) and the scale is folded into the exponent's FMA.
+    // diagonal; masking only on sub-tiles that cross it or the end). The
+    // running maximum is taken on raw scores (the scale is positive, so it
+    // commutes with the maximum) and the scale is folded into the exponent's FMA.
     floatx16 s[2];
     bool live[2];
     float mx = -INFINITY;
@@ -168,13 +187,12 @@ __global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __rest
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[st][r] = 0.f;
       if (live[st]) {
-        const bf16* arow = Kb + (32 * st + c) * C::P + G * 8;
 #pragma unroll
         for (int ss = 0; ss < C::NS; ++ss) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + ss * 16);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + 32 * st * HD + rro[ss]);
           s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ss], s[st], 0, 0, 0);
         }
-        if (kb + 31 > wq0) {   // crosses the diagonal of some query of the wave
+        if (kb + 31 > wq0) {   // crosses the diagonal of some query of the wave (keys past the end too)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kb + (r >> 2) * 8 + G * 4 + (r & 3);
@@ -220,11 +238,10 @@ __global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __rest
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[ht][r] *= alpha;
       }
-      const bf16* vcol = Vb + ht * 32 + 16 * (k16 & 1) + 4 * (i16 & 3) + (4 * G + (i16 >> 2)) * C::PV;
-      auto step = [&](int kk, const bf16x8& pb) {
-        const bf16* p0 = vcol + 16 * kk * C::PV;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 8 * C::PV));
+      auto step = [&](int kk, const bf16x8& pb) __attribute__((always_inline)) {
+        const bf16* p0 = Vb + 16 * kk * HD;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + tro[ht][0]));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + tro[ht][1]));
         const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[ht], 0, 0, 0);
       };
@@ -232,11 +249,17 @@ __global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __rest
       if (live[1]) { step(2, pb2); step(3, pb3); }
     }
 
-    if (more) {
-      kr.template store<C::P>(Ks[buf ^ 1], tid);
-      vr.template store<C::PV>(Vs[buf ^ 1], tid);
-    }
+    if (more) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the next tile has landed
     __syncthreads();
+  };
+
+  cp.copy(K0, Kg, ld, 0, Tn, w, lane);
+  cp.copy(V0, Vg, ld, 0, Tn, w, lane);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    tile(kt, K0, V0, K1, V1);
+    if (kt + 1 < n_kt) tile(kt + 1, K1, V1, K0, V0);
   }
 
   if (q < Tn) {
