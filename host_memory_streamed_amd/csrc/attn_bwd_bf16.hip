@@ -297,11 +297,9 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
     const int q0 = (qt0 + it % nqt) * BS;
     const bool more = it + 1 < n_it;
     if (more) issue(it + 1, Qn, On);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int qs0 = q0 + 32 * u;
-      if (qs0 + 31 < kw0) continue;   // every query of the sub-tile precedes the wave's keys
-      floatx16 s, dp;
+
+    // S = Q K^T and dP = dO V^T of sub-tile u (queries q0 + 32u ..)
+    auto sdp = [&](int u, floatx16& s, floatx16& dp) __attribute__((always_inline)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
@@ -311,37 +309,136 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ss], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, vf[ss], dp, 0, 0, 0);
       }
-      // rows are queries qs0 + (r/4)*8 + G*4 + r%4, the column is this lane's
-      // key; masking only where the sub-tile meets the diagonal or the end
-      bf16x8 pb0, pb1, db0, db1;
-      auto grads = [&](auto masked) __attribute__((always_inline)) {
+    };
+    // P and dS = P (dP - D) as bf16 operands; rows are queries
+    // q0 + 32u + (r/4)*8 + G*4 + r%4, the column is this lane's key
+    auto grads = [&](auto masked, int u, const floatx16& s, const floatx16& dp, bf16x8& pb0, bf16x8& pb1,
+                     bf16x8& db0, bf16x8& db1) __attribute__((always_inline)) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int qr4 = 32 * u + r4 * 8 + G * 4;
-          const floatx4 lq = *reinterpret_cast<const floatx4*>(&Ls[buf][qr4]);
-          const floatx4 dq4 = *reinterpret_cast<const floatx4*>(&Dsh[buf][qr4]);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int qr4 = 32 * u + r4 * 8 + G * 4;
+        const floatx4 lq = *reinterpret_cast<const floatx4*>(&Ls[buf][qr4]);
+        const floatx4 dq4 = *reinterpret_cast<const floatx4*>(&Dsh[buf][qr4]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = r4 * 4 + e;
-            float pv = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lq[e]));
-            if constexpr (decltype(masked)::value) {
-              const int qi = q0 + qr4 + e;
-              if (!(key <= qi && qi < Tn)) pv = 0.f;
-            }
-            const float dsv = pv * (dp[r] - dq4[e]);
-            if (r < 8) { pb0[r] = to_bf16(pv); db0[r] = to_bf16(dsv); }
-            else { pb1[r - 8] = to_bf16(pv); db1[r - 8] = to_bf16(dsv); }
+        for (int e = 0; e < 4; ++e) {
+          const int r = r4 * 4 + e;
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lq[e]));
+          if constexpr (decltype(masked)::value) {
+            const int qi = q0 + qr4 + e;
+            if (!(key <= qi && qi < Tn)) pv = 0.f;
           }
+          const float dsv = pv * (dp[r] - dq4[e]);
+          if (r < 8) { pb0[r] = to_bf16(pv); db0[r] = to_bf16(dsv); }
+          else { pb1[r - 8] = to_bf16(pv); db1[r - 8] = to_bf16(dsv); }
         }
-      };
-      if (qs0 < kw0 + 31 || qs0 + 31 >= Tn) grads(std::true_type{});
-      else grads(std::false_type{});
+      }
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS over the sub-tile's 32 queries
+    auto accum = [&](int u, const bf16x8& pb0, const bf16x8& pb1, const bf16x8& db0, const bf16x8& db1)
+        __attribute__((always_inline)) {
 #pragma unroll
       for (int ht = 0; ht < C::NH; ++ht) {
         dv[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Ob, 32 * u, ht, tro), pb0, dv[ht], 0, 0, 0);
         dv[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Ob, 32 * u + 16, ht, tro), pb1, dv[ht], 0, 0, 0);
         dk[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Qb, 32 * u, ht, tro), db0, dk[ht], 0, 0, 0);
         dk[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Qb, 32 * u + 16, ht, tro), db1, dk[ht], 0, 0, 0);
+      }
+    };
+
+    if (q0 >= kw0 + 31 && q0 + BS <= Tn) {
+      // Interior tile: both sub-tiles whole and unmasked, software-pipelined so
+      // that the softmax arithmetic of one sub-tile runs while the matrix cores
+      // work on the other:
+      //   S0,dP0 | S1,dP1 + softmax 0 | dV,dK += (sub-tile 0) + softmax 1 | dV,dK += (sub-tile 1)
+      // Operands are read from LDS one phase ahead; each step of a phase is
+      // fenced so the compiler keeps the interleaving.
+      floatx16 s0, dp0, s1, dp1;
+      bf16x8 qa[C::NS], oa[C::NS];       // sub-tile 1 row operands
+      floatx4 lq[4], dq[4];               // softmax statistics of the sub-tile in flight
+      bf16x8 p00, p01, d00, d01, p10, p11, d10, d11;
+      bf16x8 ta[16];                      // transpose operands of the next accumulation
+      auto stats = [&](int u) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          lq[r4] = *reinterpret_cast<const floatx4*>(&Ls[buf][32 * u + r4 * 8 + G * 4]);
+          dq[r4] = *reinterpret_cast<const floatx4*>(&Dsh[buf][32 * u + r4 * 8 + G * 4]);
+        }
+      };
+      auto gelem = [&](int r, const floatx16& sv, const floatx16& dpv, bf16x8& pb0, bf16x8& pb1, bf16x8& db0,
+                       bf16x8& db1) __attribute__((always_inline)) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sv[r], sl2, -lq[r >> 2][r & 3]));
+        const float dsv = pv * (dpv[r] - dq[r >> 2][r & 3]);
+        if (r < 8) { pb0[r] = to_bf16(pv); db0[r] = to_bf16(dsv); }
+        else { pb1[r - 8] = to_bf16(pv); db1[r - 8] = to_bf16(dsv); }
+      };
+      // accumulation product t of a sub-tile: hd block t/4; dV with P rows
+      // 0..15 / 16..31, then dK with dS rows 0..15 / 16..31
+      auto tread = [&](int u, int t) __attribute__((always_inline)) {
+        ta[t] = tr_operand<HD>((t & 3) < 2 ? Ob : Qb, 32 * u + 16 * (t & 1), t >> 2, tro);
+      };
+      auto amma = [&](int t, const bf16x8& pb0, const bf16x8& pb1, const bf16x8& db0, const bf16x8& db1)
+          __attribute__((always_inline)) {
+        const int ht = t >> 2;
+        switch (t & 3) {
+          case 0: dv[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[t], pb0, dv[ht], 0, 0, 0); break;
+          case 1: dv[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[t], pb1, dv[ht], 0, 0, 0); break;
+          case 2: dk[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[t], db0, dk[ht], 0, 0, 0); break;
+          default: dk[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[t], db1, dk[ht], 0, 0, 0); break;
+        }
+      };
+      constexpr int NA = 4 * C::NH;       // accumulation products per sub-tile
+
+      // phase 1: S0, dP0; read sub-tile 1's operands and sub-tile 0's statistics
+      sdp(0, s0, dp0);
+#pragma unroll
+      for (int ss = 0; ss < C::NS; ++ss) {
+        qa[ss] = *reinterpret_cast<const bf16x8*>(Qb + 32 * HD + rro[ss]);
+        oa[ss] = *reinterpret_cast<const bf16x8*>(Ob + 32 * HD + rro[ss]);
+      }
+      stats(0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s1[r] = dp1[r] = 0.f;
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 2: S1, dP1 with softmax 0; read the sub-tile 0 transpose operands
+#pragma unroll
+      for (int ss = 0; ss < C::NS; ++ss) {
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ss], kf[ss], s1, 0, 0, 0);
+        dp1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[ss], vf[ss], dp1, 0, 0, 0);
+#pragma unroll
+        for (int r = 16 * ss / C::NS; r < 16 * (ss + 1) / C::NS; ++r) gelem(r, s0, dp0, p00, p01, d00, d01);
+#pragma unroll
+        for (int t = NA * ss / C::NS; t < NA * (ss + 1) / C::NS; ++t) tread(0, t);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      stats(1);
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 3: accumulate sub-tile 0 with softmax 1; read the sub-tile 1 operands
+      bf16x8 tb[16];
+#pragma unroll
+      for (int j = 0; j < NA; ++j) {
+        amma(j, p00, p01, d00, d01);
+#pragma unroll
+        for (int r = 16 * j / NA; r < 16 * (j + 1) / NA; ++r) gelem(r, s1, dp1, p10, p11, d10, d11);
+        tb[j] = tr_operand<HD>((j & 3) < 2 ? Ob : Qb, 32 + 16 * (j & 1), j >> 2, tro);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // phase 4: accumulate sub-tile 1
+#pragma unroll
+      for (int j = 0; j < NA; ++j) ta[j] = tb[j];
+#pragma unroll
+      for (int j = 0; j < NA; ++j) amma(j, p10, p11, d10, d11);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int qs0 = q0 + 32 * u;
+        if (qs0 + 31 < kw0) continue;   // every query of the sub-tile precedes the wave's keys
+        floatx16 s, dp;
+        sdp(u, s, dp);
+        bf16x8 pb0, pb1, db0, db1;
+        // masking only where the sub-tile meets the diagonal or the end
+        if (qs0 < kw0 + 31 || qs0 + 31 >= Tn) grads(std::true_type{}, u, s, dp, pb0, pb1, db0, db1);
+        else grads(std::false_type{}, u, s, dp, pb0, pb1, db0, db1);
+        accum(u, pb0, pb1, db0, db1);
       }
     }
     if (more) {
