@@ -31,10 +31,17 @@ constexpr float B_LOG2E = 1.4426950408889634f;
 constexpr int BT = 256;   // threads
 constexpr int BW = 128;   // keys (dK/dV) or queries (dQ) per workgroup
 constexpr int BS = 64;    // rows per streamed tile
+#ifndef FENCE2
+#define FENCE2 2          // steps per scheduling region in the pipelined phases
+#endif
+#ifndef FENCE3
+#define FENCE3 4
+#endif
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_b;
 typedef __attribute__((address_space(3))) void lds_void_b;
 typedef __attribute__((address_space(1))) void glb_void_b;
+typedef uint32_t u32x4_b __attribute__((ext_vector_type(4)));
 
 // A 64-row tile of HD bf16 columns in LDS, rows unpadded. The 16-byte chunks
 // of row r sit in the order chunk ^ perm(r), perm depending on r mod 16 only.
@@ -97,6 +104,40 @@ struct TileCopy {
                                          0);
       }
     }
+  }
+};
+
+// Register-staged copy of a 64-row tile into the same permuted layout: the
+// lane's 16-byte chunks of the wave's 1 KB pieces are loaded into registers
+// ahead of time and written to LDS later. Unlike the direct copy, no write
+// into LDS is then in flight while the other buffer is read, which keeps the
+// compiler's LDS wait counts exact.
+template <int HD>
+struct StageCopy {
+  typedef Swz<HD> S;
+  static constexpr int RPP = 512 / HD;   // tile rows per 1 KB piece
+  uint32_t off[S::WP];                   // source byte offset of the lane's chunk of piece j (whole tile)
+  int row0;                              // tile row of the lane's chunk in piece 0 (piece j: + j*RPP)
+  u32x4_b v[S::WP];
+  __device__ __forceinline__ void init(int64_t ld, int w, int lane) {
+    int r, col;
+#pragma unroll
+    for (int j = 0; j < S::WP; ++j) {
+      S::piece(w, j, lane, r, col);
+      off[j] = (uint32_t)(((int64_t)r * ld + col) * 2);
+    }
+    S::piece(w, 0, lane, r, col);
+    row0 = r;
+  }
+  // piece j of rows r0 .. r0+63 of src (row stride ld); rows at or past n
+  // (r0 < n) repeat row n-1, whose products the callers mask
+  __device__ __forceinline__ void load(int j, const bf16* src, int64_t ld, int r0, int n) {
+    const int ex = max(0, row0 + j * RPP - (n - 1 - r0));
+    const char* p = reinterpret_cast<const char*>(src + (int64_t)r0 * ld);
+    v[j] = *reinterpret_cast<const u32x4_b*>(p + (off[j] - (uint32_t)ex * (uint32_t)(ld * 2)));
+  }
+  __device__ __forceinline__ void store(int j, bf16* tile, int w, int lane) const {
+    *reinterpret_cast<u32x4_b*>(tile + (w * S::WP + j) * 512 + lane * 8) = v[j];
   }
 };
 
@@ -233,7 +274,8 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
   }
   const int b = blockIdx.z;
   const int grp = H / Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = tid >> 6;
   const int c = lane & 31, G = lane >> 5;
   const int64_t ld = (int64_t)(H + 2 * Hkv) * HD, ldo = (int64_t)H * HD;
   const bf16* base = qkv + (int64_t)b * Tn * ld;
@@ -260,7 +302,7 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
     for (int r = 0; r < 16; ++r) dk[i][r] = dv[i][r] = 0.f;
   const float sl2 = B_LOG2E / sqrtf((float)HD);
 
-  TileCopy<HD> cq, co;
+  StageCopy<HD> cq, co;   // Q and dO tiles
   cq.init(ld, w, lane);
   co.init(ldo, w, lane);
   TrOffsets<HD> tro;
@@ -274,29 +316,64 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
   const int nqt = (Tn + BS - 1) / BS - qt0;
   const int n_it = grp * nqt;
 
+  // tiles run over heads kvh*grp .. kvh*grp+grp-1, each over query tiles
+  // qt0 .. qt0+nqt-1; (nx_h, nx_qt) is the next tile to stage, cu_qt the
+  // current tile's query tile. (sh, sq0) is what the current tile stages:
+  // the next tile, or itself again when there is none (into the free buffer,
+  // never read).
+  int nx_h = kvh * grp, nx_qt = qt0, cu_qt = qt0;
+  int sh = nx_h, sq0 = nx_qt * BS;
   float lv = 0.f;
-  auto issue = [&](int it, bf16* Qn, bf16* On) __attribute__((always_inline)) {
-    const int h = kvh * grp + it / nqt;
-    const int q0 = (qt0 + it % nqt) * BS;
-    cq.copy(Qn, base + h * HD, ld, q0, Tn, w, lane);
-    co.copy(On, dbase + h * HD, ldo, q0, Tn, w, lane);
+  auto pick_next = [&](bool more) __attribute__((always_inline)) {
+    if (more) {
+      sh = nx_h;
+      sq0 = nx_qt * BS;
+      if (++nx_qt == qt0 + nqt) {
+        nx_qt = qt0;
+        ++nx_h;
+      }
+    }
+  };
+  auto load_q = [&](int j) __attribute__((always_inline)) { cq.load(j, base + sh * HD, ld, sq0, Tn); };
+  auto load_o = [&](int j) __attribute__((always_inline)) { co.load(j, dbase + sh * HD, ldo, sq0, Tn); };
+  auto load_lv = [&]() __attribute__((always_inline)) {
     if (tid < 2 * BS) {
-      const int qi = min(q0 + (tid & (BS - 1)), Tn - 1);
-      const int64_t idx = ((int64_t)b * H + h) * Tn + qi;
+      const int qi = min(sq0 + (tid & (BS - 1)), Tn - 1);
+      const int64_t idx = ((int64_t)b * H + sh) * Tn + qi;
       lv = tid < BS ? lse[idx] : Dv[idx];
     }
+  };
+  auto put = [&](int j, bf16* Qn, bf16* On) __attribute__((always_inline)) {
+    cq.store(j, Qn, w, lane);
+    co.store(j, On, w, lane);
   };
   auto stash = [&](int buf) __attribute__((always_inline)) {
     if (tid < BS) Ls[buf][tid] = lv * B_LOG2E;
     else if (tid < 2 * BS) Dsh[buf][tid - BS] = lv;
   };
 
-  // one query tile: Q and dO of tile it in (Qb, Ob), tile it+1 copied into (Qn, On)
-  auto tile = [&](int it, const bf16* Qb, const bf16* Ob, bf16* Qn, bf16* On, int buf)
+  constexpr int NA = 4 * C::NH;   // accumulation products per 32-query sub-tile
+  // accumulation product t of a sub-tile: hd block t/4; dV with P rows
+  // 0..15 / 16..31, then dK with dS rows 0..15 / 16..31
+  auto amma = [&](int t, const bf16x8& a, const bf16x8& pb0, const bf16x8& pb1, const bf16x8& db0,
+                  const bf16x8& db1) __attribute__((always_inline)) {
+    const int ht = t >> 2;
+    switch (t & 3) {
+      case 0: dv[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb0, dv[ht], 0, 0, 0); break;
+      case 1: dv[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb1, dv[ht], 0, 0, 0); break;
+      case 2: dk[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, db0, dk[ht], 0, 0, 0); break;
+      default: dk[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, db1, dk[ht], 0, 0, 0); break;
+    }
+  };
+  // the transpose operand of product t for the sub-tile at row u*32 of a tile
+  auto toper = [&](const bf16* Qb, const bf16* Ob, int u, int t) __attribute__((always_inline)) {
+    return tr_operand<HD>((t & 3) < 2 ? Ob : Qb, 32 * u + 16 * (t & 1), t >> 2, tro);
+  };
+  // one query tile: Q and dO in (Qb, Ob), the next tile copied into (Qn, On)
+  auto tile = [&](bool more, const bf16* Qb, const bf16* Ob, bf16* Qn, bf16* On, int buf)
       __attribute__((always_inline)) {
-    const int q0 = (qt0 + it % nqt) * BS;
-    const bool more = it + 1 < n_it;
-    if (more) issue(it + 1, Qn, On);
+    const int q0 = cu_qt * BS;
+    pick_next(more);
 
     // S = Q K^T and dP = dO V^T of sub-tile u (queries q0 + 32u ..)
     auto sdp = [&](int u, floatx16& s, floatx16& dp) __attribute__((always_inline)) {
@@ -333,30 +410,18 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
         }
       }
     };
-    // dV^T += dO^T P and dK^T += Q^T dS over the sub-tile's 32 queries
-    auto accum = [&](int u, const bf16x8& pb0, const bf16x8& pb1, const bf16x8& db0, const bf16x8& db1)
-        __attribute__((always_inline)) {
-#pragma unroll
-      for (int ht = 0; ht < C::NH; ++ht) {
-        dv[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Ob, 32 * u, ht, tro), pb0, dv[ht], 0, 0, 0);
-        dv[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Ob, 32 * u + 16, ht, tro), pb1, dv[ht], 0, 0, 0);
-        dk[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Qb, 32 * u, ht, tro), db0, dk[ht], 0, 0, 0);
-        dk[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Qb, 32 * u + 16, ht, tro), db1, dk[ht], 0, 0, 0);
-      }
-    };
 
     if (q0 >= kw0 + 31 && q0 + BS <= Tn) {
       // Interior tile: both sub-tiles whole and unmasked, software-pipelined so
       // that the softmax arithmetic of one sub-tile runs while the matrix cores
       // work on the other:
-      //   S0,dP0 | S1,dP1 + softmax 0 | dV,dK += (sub-tile 0) + softmax 1 | dV,dK += (sub-tile 1)
-      // Operands are read from LDS one phase ahead; each step of a phase is
+      //   S0,dP0 | S1,dP1 + softmax 0 | accumulate sub-tile 0 + softmax 1 |
+      //   accumulate sub-tile 1
+      // Operands are read from LDS ahead of use; the steps of a phase are
       // fenced so the compiler keeps the interleaving.
       floatx16 s0, dp0, s1, dp1;
-      bf16x8 qa[C::NS], oa[C::NS];       // sub-tile 1 row operands
       floatx4 lq[4], dq[4];               // softmax statistics of the sub-tile in flight
-      bf16x8 p00, p01, d00, d01, p10, p11, d10, d11;
-      bf16x8 ta[16];                      // transpose operands of the next accumulation
+      bf16x8 p00, p01, d00, d01;
       auto stats = [&](int u) __attribute__((always_inline)) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
@@ -371,63 +436,84 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
         if (r < 8) { pb0[r] = to_bf16(pv); db0[r] = to_bf16(dsv); }
         else { pb1[r - 8] = to_bf16(pv); db1[r - 8] = to_bf16(dsv); }
       };
-      // accumulation product t of a sub-tile: hd block t/4; dV with P rows
-      // 0..15 / 16..31, then dK with dS rows 0..15 / 16..31
-      auto tread = [&](int u, int t) __attribute__((always_inline)) {
-        ta[t] = tr_operand<HD>((t & 3) < 2 ? Ob : Qb, 32 * u + 16 * (t & 1), t >> 2, tro);
-      };
-      auto amma = [&](int t, const bf16x8& pb0, const bf16x8& pb1, const bf16x8& db0, const bf16x8& db1)
-          __attribute__((always_inline)) {
-        const int ht = t >> 2;
-        switch (t & 3) {
-          case 0: dv[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[t], pb0, dv[ht], 0, 0, 0); break;
-          case 1: dv[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[t], pb1, dv[ht], 0, 0, 0); break;
-          case 2: dk[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[t], db0, dk[ht], 0, 0, 0); break;
-          default: dk[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[t], db1, dk[ht], 0, 0, 0); break;
-        }
-      };
-      constexpr int NA = 4 * C::NH;       // accumulation products per sub-tile
 
-      // phase 1: S0, dP0; read sub-tile 1's operands and sub-tile 0's statistics
-      sdp(0, s0, dp0);
+      // phase 1: S0, dP0; rows read two steps ahead
+      bf16x8 ra[C::NS], rb[C::NS];
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        ra[ss] = *reinterpret_cast<const bf16x8*>(Qb + rro[ss]);
+        rb[ss] = *reinterpret_cast<const bf16x8*>(Ob + rro[ss]);
+      }
+      stats(0);
+      load_lv();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s0[r] = dp0[r] = 0.f;
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ss = 0; ss < C::NS; ++ss) {
+#pragma unroll
+        for (int j = C::WP * ss / C::NS; j < C::WP * (ss + 1) / C::NS; ++j) load_q(j);
+        if (ss + 2 < C::NS) {
+          ra[ss + 2] = *reinterpret_cast<const bf16x8*>(Qb + rro[ss + 2]);
+          rb[ss + 2] = *reinterpret_cast<const bf16x8*>(Ob + rro[ss + 2]);
+        }
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ss], kf[ss], s0, 0, 0, 0);
+        dp0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[ss], vf[ss], dp0, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      bf16x8 qa[C::NS], oa[C::NS];        // sub-tile 1 rows, read two steps ahead
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
         qa[ss] = *reinterpret_cast<const bf16x8*>(Qb + 32 * HD + rro[ss]);
         oa[ss] = *reinterpret_cast<const bf16x8*>(Ob + 32 * HD + rro[ss]);
       }
-      stats(0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s1[r] = dp1[r] = 0.f;
       __builtin_amdgcn_sched_barrier(0);
       // phase 2: S1, dP1 with softmax 0; read the sub-tile 0 transpose operands
+      bf16x8 ta[NA];
 #pragma unroll
       for (int ss = 0; ss < C::NS; ++ss) {
+#pragma unroll
+        for (int j = C::WP * ss / C::NS; j < C::WP * (ss + 1) / C::NS; ++j) load_o(j);
+        if (ss + 2 < C::NS) {
+          qa[ss + 2] = *reinterpret_cast<const bf16x8*>(Qb + 32 * HD + rro[ss + 2]);
+          oa[ss + 2] = *reinterpret_cast<const bf16x8*>(Ob + 32 * HD + rro[ss + 2]);
+        }
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ss], kf[ss], s1, 0, 0, 0);
         dp1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[ss], vf[ss], dp1, 0, 0, 0);
 #pragma unroll
         for (int r = 16 * ss / C::NS; r < 16 * (ss + 1) / C::NS; ++r) gelem(r, s0, dp0, p00, p01, d00, d01);
 #pragma unroll
-        for (int t = NA * ss / C::NS; t < NA * (ss + 1) / C::NS; ++t) tread(0, t);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int t = NA * ss / C::NS; t < NA * (ss + 1) / C::NS; ++t) ta[t] = toper(Qb, Ob, 0, t);
+        if ((ss + 1) % FENCE2 == 0) __builtin_amdgcn_sched_barrier(0);
       }
       stats(1);
       __builtin_amdgcn_sched_barrier(0);
       // phase 3: accumulate sub-tile 0 with softmax 1; read the sub-tile 1 operands
-      bf16x8 tb[16];
+      bf16x8 tb[NA], p10, p11, d10, d11;
 #pragma unroll
       for (int j = 0; j < NA; ++j) {
-        amma(j, p00, p01, d00, d01);
+        amma(j, ta[j], p00, p01, d00, d01);
 #pragma unroll
         for (int r = 16 * j / NA; r < 16 * (j + 1) / NA; ++r) gelem(r, s1, dp1, p10, p11, d10, d11);
-        tb[j] = tr_operand<HD>((j & 3) < 2 ? Ob : Qb, 32 + 16 * (j & 1), j >> 2, tro);
-        __builtin_amdgcn_sched_barrier(0);
+        tb[j] = toper(Qb, Ob, 1, j);
+        if ((j + 1) % FENCE3 == 0) __builtin_amdgcn_sched_barrier(0);
       }
-      // phase 4: accumulate sub-tile 1
+      // phase 4: accumulate sub-tile 1; write the staged tile to the free buffer
 #pragma unroll
-      for (int j = 0; j < NA; ++j) ta[j] = tb[j];
-#pragma unroll
-      for (int j = 0; j < NA; ++j) amma(j, p10, p11, d10, d11);
+      for (int j = 0; j < NA; ++j) {
+        amma(j, tb[j], p10, p11, d10, d11);
+        if (j % 2 == 0 && j < 2 * C::WP) put(j / 2, Qn, On);
+      }
+      stash(buf ^ 1);
     } else {
+#pragma unroll
+      for (int j = 0; j < C::WP; ++j) {
+        load_q(j);
+        load_o(j);
+      }
+      load_lv();
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int qs0 = q0 + 32 * u;
@@ -438,23 +524,31 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
         // masking only where the sub-tile meets the diagonal or the end
         if (qs0 < kw0 + 31 || qs0 + 31 >= Tn) grads(std::true_type{}, u, s, dp, pb0, pb1, db0, db1);
         else grads(std::false_type{}, u, s, dp, pb0, pb1, db0, db1);
-        accum(u, pb0, pb1, db0, db1);
+#pragma unroll
+        for (int t = 0; t < NA; ++t) amma(t, toper(Qb, Ob, u, t), pb0, pb1, db0, db1);
       }
-    }
-    if (more) {
-      wait_copies();
+#pragma unroll
+      for (int j = 0; j < C::WP; ++j) put(j, Qn, On);
       stash(buf ^ 1);
     }
+    if (++cu_qt == qt0 + nqt) cu_qt = qt0;
     __syncthreads();
   };
 
-  issue(0, Q0, O0);
-  wait_copies();
+  pick_next(true);
+#pragma unroll
+  for (int j = 0; j < C::WP; ++j) {
+    load_q(j);
+    load_o(j);
+  }
+  load_lv();
+#pragma unroll
+  for (int j = 0; j < C::WP; ++j) put(j, Q0, O0);
   stash(0);
   __syncthreads();
   for (int it = 0; it < n_it; it += 2) {
-    tile(it, Q0, O0, Q1, O1, 0);
-    if (it + 1 < n_it) tile(it + 1, Q1, O1, Q0, O0, 1);
+    tile(it + 1 < n_it, Q0, O0, Q1, O1, 0);
+    if (it + 1 < n_it) tile(it + 2 < n_it, Q1, O1, Q0, O0, 1);
   }
 
   if (key < Tn) {
