@@ -306,18 +306,20 @@ struct BigLoader {
   // its block, i.e. physical chunk l % 8 of row l / 8, so each lane fetches
   // the logical chunk that the row's permutation puts there. Each wave fills
   // four blocks; completion is awaited (vmcnt) before the stage's barrier.
-  __device__ __forceinline__ void direct(const T* __restrict__ base, int64_t ld, int r0, int k0, char* lds,
-                                         int tid) const {
+  __device__ __forceinline__ void direct_piece(int j, const T* __restrict__ base, int64_t ld, int r0, int k0,
+                                               char* lds, int tid) const {
     static_assert(KCONTIG, "direct loads need K-contiguous rows");
     const int w = tid >> 6, lane = tid & 63;
+    const int blk = w * 4 + j;
+    const int r = blk * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ (r & 7) ^ ((r >> 3) & 7);
+    const T* p = base + (int64_t)(r0 + r) * ld + k0 + c * VE;
+    __builtin_amdgcn_global_load_lds((const glb_void_t*)p, (lds_void_t*)(lds + blk * 1024), 16, 0, 0);
+  }
+  __device__ __forceinline__ void direct(const T* __restrict__ base, int64_t ld, int r0, int k0, char* lds,
+                                         int tid) const {
 #pragma unroll
-    for (int j = 0; j < BIG / 8 / (BIG_THREADS / 64); ++j) {
-      const int blk = w * 4 + j;
-      const int r = blk * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ (r & 7) ^ ((r >> 3) & 7);
-      const T* p = base + (int64_t)(r0 + r) * ld + k0 + c * VE;
-      __builtin_amdgcn_global_load_lds((const glb_void_t*)p, (lds_void_t*)(lds + blk * 1024), 16, 0, 0);
-    }
+    for (int j = 0; j < BIG / 8 / (BIG_THREADS / 64); ++j) direct_piece(j, base, ld, r0, k0, lds, tid);
   }
 
   __device__ __forceinline__ void store(char* lds, int tid) const {
@@ -403,17 +405,19 @@ struct BigNat {
   // Global -> LDS for a full stage: each wave fills four 1-KB blocks (two rows
   // each); lane l lands on physical chunk l % 32 of row l / 32 of its block and
   // fetches the logical chunk the permutation puts there.
+  __device__ __forceinline__ void direct_piece(int j, const bf16* __restrict__ base, int64_t ld, int r0, int k0,
+                                               char* lds, int tid) const {
+    const int w = tid >> 6, lane = tid & 63;
+    const int blk = w * 4 + j;
+    const int row = 2 * blk + (lane >> 5);
+    const int c = pchunk(row, lane & 31);
+    const bf16* p = base + (int64_t)(k0 + row) * ld + r0 + c * VE;
+    __builtin_amdgcn_global_load_lds((const glb_void_t*)p, (lds_void_t*)(lds + blk * 1024), 16, 0, 0);
+  }
   __device__ __forceinline__ void direct(const bf16* __restrict__ base, int64_t ld, int r0, int k0, char* lds,
                                          int tid) const {
-    const int w = tid >> 6, lane = tid & 63;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int blk = w * 4 + j;
-      const int row = 2 * blk + (lane >> 5);
-      const int c = pchunk(row, lane & 31);
-      const bf16* p = base + (int64_t)(k0 + row) * ld + r0 + c * VE;
-      __builtin_amdgcn_global_load_lds((const glb_void_t*)p, (lds_void_t*)(lds + blk * 1024), 16, 0, 0);
-    }
+    for (int j = 0; j < 4; ++j) direct_piece(j, base, ld, r0, k0, lds, tid);
   }
   // MFMA fragment: 32 consecutive m (or n) from mn0, k-step s (16 k)
   static __device__ __forceinline__ bf16x8 frag(const char* tile, int mn0, int s, int lane) {
@@ -485,7 +489,10 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
     for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
 
   const int nk = (K + BK - 1) / BK;
-  auto mma_stage = [&](const char* cur) {
+  // one stage of products from LDS; after the products of k-step s, hook(s)
+  // issues part of the next stage's copies, so the copy instructions spread
+  // over the stage instead of stalling every wave at its start
+  auto mma_stage = [&](const char* cur, auto hook) {
     if constexpr (A_NAT || B_NAT) {
       // bf16 with a natural-layout operand: one 16-k MFMA step per s
 #pragma unroll
@@ -507,6 +514,7 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        hook(s);
       }
       return;
     }
@@ -531,8 +539,10 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
             acc[i][j] = MF::mma(fa, fb, acc[i][j]);
           }
         }
+      hook(s);
     }
   };
+  auto no_hook = [](int) {};
   // guarded stage through registers (edge tiles, the K tail)
   auto reg_stage = [&](int k0, char* dst) {
     la.template load<true>(A, lda, m0, M, k0, K, tid);
@@ -555,12 +565,17 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
       }
       for (int kt = 0; kt < nkf; ++kt) {
         const char* cur = smem_big + (kt & 1) * BIG_STAGE;
-        if (kt + 1 < nkf) {
-          char* nxt = smem_big + ((kt + 1) & 1) * BIG_STAGE;
-          la.direct(A, lda, m0, (kt + 1) * BK, nxt, tid);
-          lb.direct(B, ldb, n0, (kt + 1) * BK, nxt + BIG_TILE_BYTES, tid);
-        }
-        mma_stage(cur);
+        char* nxt = smem_big + ((kt + 1) & 1) * BIG_STAGE;
+        const bool more = kt + 1 < nkf;
+        mma_stage(cur, [&](int s) {
+          if (more && s < 2) {   // early in the stage, so the copies land before its end
+#pragma unroll
+            for (int j = 2 * s; j < 2 * s + 2; ++j) {
+              la.direct_piece(j, A, lda, m0, (kt + 1) * BK, nxt, tid);
+              lb.direct_piece(j, B, ldb, n0, (kt + 1) * BK, nxt + BIG_TILE_BYTES, tid);
+            }
+          }
+        });
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
       }
@@ -568,7 +583,7 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
         char* tb = smem_big + (nkf & 1) * BIG_STAGE;
         reg_stage(nkf * BK, tb);
         __syncthreads();
-        mma_stage(tb);
+        mma_stage(tb, no_hook);
       }
       done = true;
     }
@@ -592,7 +607,7 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
       const char* cur = smem_big + (kt & 1) * BIG_STAGE;
       const bool more = kt + 1 < nk;
       if (more) load_stage((kt + 1) * BK);
-      mma_stage(cur);
+      mma_stage(cur, no_hook);
       if (more) {
         char* nxt = smem_big + ((kt + 1) & 1) * BIG_STAGE;
         la.store(nxt, tid);
