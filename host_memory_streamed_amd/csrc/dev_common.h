@@ -72,3 +72,28 @@ template <> struct Mfma32<float> {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
 };
+
+// Global -> LDS copy of 16 bytes per lane in the buffer (MUBUF) form: lane i's
+// bytes, read at base + voffset_i, land at lds + 16 i (lds wave-uniform).
+// The compiler tracks this form as a plain vector-memory load, so LDS reads
+// issued while it is in flight keep exact wait counts; the global (FLAT) form
+// of the same copy is treated as a possible LDS access and turns every later
+// LDS wait into a wait for all outstanding LDS operations.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+extern "C" __device__ void mt_raw_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3))) void* lds,
+                                                  int size, int voffset, int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+// descriptor of the bytes from base on: no stride, no range limit, the gfx9
+// data-format word
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base) {
+  const uint64_t a = (uint64_t)base;
+  i32x4_t r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)(uint32_t)(a >> 32);
+  r[2] = -1;
+  r[3] = 0x00020000;
+  return r;
+}
+__device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t voffset, void* lds) {
+  mt_raw_buffer_load_lds(buffer_rsrc(base), (__attribute__((address_space(3))) void*)lds, 16, (int)voffset, 0, 0, 0);
+}

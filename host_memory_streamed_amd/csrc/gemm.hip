@@ -313,8 +313,8 @@ struct BigLoader {
     const int blk = w * 4 + j;
     const int r = blk * 8 + (lane >> 3);
     const int c = (lane & 7) ^ (r & 7) ^ ((r >> 3) & 7);
-    const T* p = base + (int64_t)(r0 + r) * ld + k0 + c * VE;
-    __builtin_amdgcn_global_load_lds((const glb_void_t*)p, (lds_void_t*)(lds + blk * 1024), 16, 0, 0);
+    copy16_to_lds(base + (int64_t)r0 * ld + k0, (uint32_t)(((int64_t)r * ld + c * VE) * (int64_t)sizeof(T)),
+                  lds + blk * 1024);
   }
   __device__ __forceinline__ void direct(const T* __restrict__ base, int64_t ld, int r0, int k0, char* lds,
                                          int tid) const {
@@ -411,8 +411,7 @@ struct BigNat {
     const int blk = w * 4 + j;
     const int row = 2 * blk + (lane >> 5);
     const int c = pchunk(row, lane & 31);
-    const bf16* p = base + (int64_t)(k0 + row) * ld + r0 + c * VE;
-    __builtin_amdgcn_global_load_lds((const glb_void_t*)p, (lds_void_t*)(lds + blk * 1024), 16, 0, 0);
+    copy16_to_lds(base + (int64_t)k0 * ld + r0, (uint32_t)(((int64_t)row * ld + c * VE) * 2), lds + blk * 1024);
   }
   __device__ __forceinline__ void direct(const bf16* __restrict__ base, int64_t ld, int r0, int k0, char* lds,
                                          int tid) const {
@@ -448,7 +447,9 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
   constexpr int BK = BIG_ROW / sizeof(T);
   constexpr int NSUB = 16 / (MF::KL * (int)sizeof(T));   // instructions per 16-byte chunk
 
-  extern __shared__ __attribute__((aligned(16))) char smem_big[];
+  // one array per stage buffer: the compiler then sees that the copies in
+  // flight into one stage do not alias the reads of the other
+  __shared__ __attribute__((aligned(1024))) char st0[BIG_STAGE], st1[BIG_STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -558,14 +559,12 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
       // stage goes global -> LDS directly, one stage ahead; a K tail runs last
       const int nkf = K / BK;
       if (nkf > 0) {
-        la.direct(A, lda, m0, 0, smem_big, tid);
-        lb.direct(B, ldb, n0, 0, smem_big + BIG_TILE_BYTES, tid);
+        la.direct(A, lda, m0, 0, st0, tid);
+        lb.direct(B, ldb, n0, 0, st0 + BIG_TILE_BYTES, tid);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's LDS writes have landed
         __syncthreads();
       }
-      for (int kt = 0; kt < nkf; ++kt) {
-        const char* cur = smem_big + (kt & 1) * BIG_STAGE;
-        char* nxt = smem_big + ((kt + 1) & 1) * BIG_STAGE;
+      auto fstage = [&](int kt, const char* cur, char* nxt) __attribute__((always_inline)) {
         const bool more = kt + 1 < nkf;
         mma_stage(cur, [&](int s) {
           if (more && s < 2) {   // early in the stage, so the copies land before its end
@@ -578,9 +577,13 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
         });
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
+      };
+      for (int kt = 0; kt < nkf; kt += 2) {   // buffers fixed at compile time
+        fstage(kt, st0, st1);
+        if (kt + 1 < nkf) fstage(kt + 1, st1, st0);
       }
       if (nkf < nk) {   // K tail (stage buffer nkf & 1 is free after the last barrier)
-        char* tb = smem_big + (nkf & 1) * BIG_STAGE;
+        char* tb = (nkf & 1) ? st1 : st0;
         reg_stage(nkf * BK, tb);
         __syncthreads();
         mma_stage(tb, no_hook);
@@ -599,17 +602,17 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
       }
     };
     load_stage(0);
-    la.store(smem_big, tid);
-    lb.store(smem_big + BIG_TILE_BYTES, tid);
+    la.store(st0, tid);
+    lb.store(st0 + BIG_TILE_BYTES, tid);
     __syncthreads();
 
     for (int kt = 0; kt < nk; ++kt) {
-      const char* cur = smem_big + (kt & 1) * BIG_STAGE;
+      const char* cur = (kt & 1) ? st1 : st0;
       const bool more = kt + 1 < nk;
       if (more) load_stage((kt + 1) * BK);
       mma_stage(cur, no_hook);
       if (more) {
-        char* nxt = smem_big + ((kt + 1) & 1) * BIG_STAGE;
+        char* nxt = (kt & 1) ? st0 : st1;
         la.store(nxt, tid);
         lb.store(nxt + BIG_TILE_BYTES, tid);
       }
@@ -660,10 +663,7 @@ template <typename T, int LAYOUT>
 hipError_t launch_big(const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc,
                       const float* R, int64_t ldr, int M, int N, int K, hipStream_t s) {
   const int tm = (M + BIG - 1) / BIG, tn = (N + BIG - 1) / BIG;
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)gemm_big_kernel<T, LAYOUT>, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * BIG_STAGE);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemm_big_kernel<T, LAYOUT>), dim3(tm * tn), dim3(BIG_THREADS), 2 * BIG_STAGE, s,
+  hipLaunchKernelGGL((gemm_big_kernel<T, LAYOUT>), dim3(tm * tn), dim3(BIG_THREADS), 0, s,
                      (const T*)A, lda, (const T*)B, ldb, C, ldc, R, ldr, M, N, K, tm, tn);
   return hipGetLastError();
 }
