@@ -566,13 +566,31 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
       }
       auto fstage = [&](int kt, const char* cur, char* nxt) __attribute__((always_inline)) {
         const bool more = kt + 1 < nkf;
+        // the last stage copies itself again into the free buffer (valid
+        // memory, landed before the barrier, overwritten by any K tail): the
+        // stage then has no branch and its LDS reads can move ahead of products
+        const int kn = (more ? kt + 1 : kt) * BK;
         mma_stage(cur, [&](int s) {
-          if (more && s < 2) {   // early in the stage, so the copies land before its end
+          if (s < 2) {   // early in the stage, so the copies land before its end
 #pragma unroll
             for (int j = 2 * s; j < 2 * s + 2; ++j) {
-              la.direct_piece(j, A, lda, m0, (kt + 1) * BK, nxt, tid);
-              lb.direct_piece(j, B, ldb, n0, (kt + 1) * BK, nxt + BIG_TILE_BYTES, tid);
+              la.direct_piece(j, A, lda, m0, kn, nxt, tid);
+              lb.direct_piece(j, B, ldb, n0, kn, nxt + BIG_TILE_BYTES, tid);
             }
+          }
+          if (s == 3) {
+            // order for the stage: each k-step's LDS reads one step ahead of
+            // its products, the copies after the first two reads
+            constexpr int NDS = (A_NAT ? 8 : 4) + (B_NAT ? 4 : 2);   // LDS reads per k-step
+            __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
           }
         });
         __builtin_amdgcn_s_waitcnt(0x0F70);
