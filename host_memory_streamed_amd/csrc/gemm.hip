@@ -570,23 +570,27 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
         // memory, landed before the barrier, overwritten by any K tail): the
         // stage then has no branch and its LDS reads can move ahead of products
         const int kn = (more ? kt + 1 : kt) * BK;
+        // copies early in the stage so that they land before its end: over the
+        // first two k-steps, or all in the first where only one k-step's
+        // fragments fit in registers (both operands K-contiguous)
+        constexpr int CSTEPS = (A_NAT || B_NAT) ? 2 : 1;
         mma_stage(cur, [&](int s) {
-          if (s < 2) {   // early in the stage, so the copies land before its end
+          if (s < CSTEPS) {
 #pragma unroll
-            for (int j = 2 * s; j < 2 * s + 2; ++j) {
+            for (int j = 4 * s / CSTEPS; j < 4 * (s + 1) / CSTEPS; ++j) {
               la.direct_piece(j, A, lda, m0, kn, nxt, tid);
               lb.direct_piece(j, B, ldb, n0, kn, nxt + BIG_TILE_BYTES, tid);
             }
           }
           if (s == 3) {
             // order for the stage: each k-step's LDS reads one step ahead of
-            // its products, the copies after the first two reads
+            // its products, the copies after the first reads
             constexpr int NDS = (A_NAT ? 8 : 4) + (B_NAT ? 4 : 2);   // LDS reads per k-step
             __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 8 / CSTEPS, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+            if constexpr (CSTEPS == 2) __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
