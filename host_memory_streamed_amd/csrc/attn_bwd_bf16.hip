@@ -39,8 +39,6 @@ constexpr int BS = 64;    // rows per streamed tile
 #endif
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_b;
-typedef __attribute__((address_space(3))) void lds_void_b;
-typedef __attribute__((address_space(1))) void glb_void_b;
 typedef uint32_t u32x4_b __attribute__((ext_vector_type(4)));
 
 // A 64-row tile of HD bf16 columns in LDS, rows unpadded. The 16-byte chunks
@@ -91,17 +89,14 @@ struct TileCopy {
     const char* base = reinterpret_cast<const char*>(src + (int64_t)r0 * ld);
     if (r0 + BS <= n) {
 #pragma unroll
-      for (int j = 0; j < S::WP; ++j)
-        __builtin_amdgcn_global_load_lds((glb_void_b*)(base + off[j]), (lds_void_b*)(tile + (w * S::WP + j) * 512),
-                                         16, 0, 0);
+      for (int j = 0; j < S::WP; ++j) copy16_to_lds(base, off[j], tile + (w * S::WP + j) * 512);
     } else {
 #pragma unroll
       for (int j = 0; j < S::WP; ++j) {
         int r, col;
         S::piece(w, j, lane, r, col);
         const int64_t o = ((int64_t)min(r, n - 1 - r0) * ld + col) * 2;
-        __builtin_amdgcn_global_load_lds((glb_void_b*)(base + o), (lds_void_b*)(tile + (w * S::WP + j) * 512), 16, 0,
-                                         0);
+        copy16_to_lds(base, (uint32_t)o, tile + (w * S::WP + j) * 512);
       }
     }
   }

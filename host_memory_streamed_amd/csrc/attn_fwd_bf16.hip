@@ -50,10 +50,8 @@ struct F32Cfg {
 };
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) void lds_void_f;
-typedef __attribute__((address_space(1))) void glb_void_f;
 
-// Direct global -> LDS copy of a 64-row K or V tile: wave w fills 1 KB pieces
+// Direct global -> LDS copy (buffer form) of a 64-row K or V tile: wave w fills 1 KB pieces
 // w*WP .. w*WP+WP-1, lane i landing 16 bytes at piece + 16 i; each lane
 // fetches the chunk that the permuted layout puts there. Rows at or past the
 // end of the sequence repeat the last row (those keys are masked).
@@ -79,17 +77,14 @@ struct TileCopyF {
     const char* base = reinterpret_cast<const char*>(src + (int64_t)k0 * ld);
     if (k0 + FK <= Tn) {
 #pragma unroll
-      for (int j = 0; j < C::WP; ++j)
-        __builtin_amdgcn_global_load_lds((glb_void_f*)(base + off[j]), (lds_void_f*)(tile + (w * C::WP + j) * 512),
-                                         16, 0, 0);
+      for (int j = 0; j < C::WP; ++j) copy16_to_lds(base, off[j], tile + (w * C::WP + j) * 512);
     } else {
 #pragma unroll
       for (int j = 0; j < C::WP; ++j) {
         int r, col;
         piece(w, j, lane, r, col);
         const int64_t o = ((int64_t)min(r, Tn - 1 - k0) * ld + col) * 2;
-        __builtin_amdgcn_global_load_lds((glb_void_f*)(base + o), (lds_void_f*)(tile + (w * C::WP + j) * 512), 16,
-                                         0, 0);
+        copy16_to_lds(base, (uint32_t)o, tile + (w * C::WP + j) * 512);
       }
     }
   }
