@@ -168,6 +168,76 @@ __global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __rest
       cp.copy(Vn, Vg, ld, k0 + FK, Tn, w, lane);
     }
 
+    // P^T V step kk (16 keys) of hd block ht
+    auto pv_step = [&](int ht, int kk, const bf16x8& pb) __attribute__((always_inline)) {
+      const bf16* p0 = Vb + 16 * kk * HD;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + tro[ht][0]));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + tro[ht][1]));
+      const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      oacc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[ht], 0, 0, 0);
+    };
+
+    if (k0 + FK - 1 <= wq0) {
+      // interior tile: every key precedes every query of the wave (so none is
+      // past the end): no masks, no selects; the output is rescaled before the
+      // exponentials so that they share one region with the P^T V products.
+      // Same arithmetic and order as the general path below.
+      floatx16 s0, s1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
+#pragma unroll
+      for (int ss = 0; ss < C::NS; ++ss) {
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(Kb + rro[ss]);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(Kb + 32 * HD + rro[ss]);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ss], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ss], s1, 0, 0, 0);
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s0[r], s0[r + 1]));
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s1[r], s1[r + 1]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+      const float m_new = fmaxf(m, mx * sl2);
+      const float alpha = exp2f(m - m_new);
+      const float nm = -m_new;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int ht = 0; ht < C::NH; ++ht)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[ht][r] *= alpha;
+      }
+      float rs = 0.f;
+      bf16x8 pb0, pb1, pb2, pb3;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s0[r], sl2, nm));
+        rs += p;
+        if (r < 8) pb0[r] = to_bf16(p);
+        else pb1[r - 8] = to_bf16(p);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s1[r], sl2, nm));
+        rs += p;
+        if (r < 8) pb2[r] = to_bf16(p);
+        else pb3[r - 8] = to_bf16(p);
+      }
+#pragma unroll
+      for (int ht = 0; ht < C::NH; ++ht) {
+        pv_step(ht, 0, pb0);
+        pv_step(ht, 1, pb1);
+        pv_step(ht, 2, pb2);
+        pv_step(ht, 3, pb3);
+      }
+      rs += __shfl_xor(rs, 32, WAVE);
+      l = l * alpha + rs;
+      m = m_new;
+      if (more) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the next tile has landed
+      __syncthreads();
+      return;
+    }
+
     // raw scores of the two 32-key sub-tiles (wave-uniform skip above the
     // diagonal; masking only on sub-tiles that cross it or the end). The
     // running maximum is taken on raw scores (the scale is positive, so it
@@ -233,15 +303,8 @@ __global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __rest
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[ht][r] *= alpha;
       }
-      auto step = [&](int kk, const bf16x8& pb) __attribute__((always_inline)) {
-        const bf16* p0 = Vb + 16 * kk * HD;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + tro[ht][0]));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + tro[ht][1]));
-        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[ht], 0, 0, 0);
-      };
-      if (live[0]) { step(0, pb0); step(1, pb1); }
-      if (live[1]) { step(2, pb2); step(3, pb3); }
+      if (live[0]) { pv_step(ht, 0, pb0); pv_step(ht, 1, pb1); }
+      if (live[1]) { pv_step(ht, 2, pb2); pv_step(ht, 3, pb3); }
     }
 
     if (more) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the next tile has landed
