@@ -631,6 +631,51 @@ __global__ __launch_bounds__(BT, 2) void attn_dq_bf16_kernel(const bf16* __restr
       ck.copy(Kn, Kg, ld, k0 + BS, Tn, w, lane);
       ck.copy(Vn, Vg, ld, k0 + BS, Tn, w, lane);
     }
+    if (k0 + BS - 1 <= wq0 && wq0 + 31 < Tn) {
+      // interior tile: every key precedes every (valid) query of the wave; one
+      // straight-line block, so that the softmax of one 32-key sub-tile can
+      // overlap the other's products. Same arithmetic and order as below.
+      floatx16 s0, dp0, s1, dp1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s0[r] = dp0[r] = s1[r] = dp1[r] = 0.f;
+#pragma unroll
+      for (int ss = 0; ss < C::NS; ++ss) {
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(Kb + rro[ss]), qf[ss], s0, 0, 0, 0);
+        dp0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(Vb + rro[ss]), df[ss], dp0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ss = 0; ss < C::NS; ++ss) {
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(Kb + 32 * HD + rro[ss]), qf[ss], s1,
+                                                     0, 0, 0);
+        dp1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(Vb + 32 * HD + rro[ss]), df[ss],
+                                                      dp1, 0, 0, 0);
+      }
+      auto grads = [&](const floatx16& sv, const floatx16& dpv, bf16x8& db0, bf16x8& db1) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sv[r], sl2, -lse2));
+          const float dsv = pv * (dpv[r] - Dq);
+          if (r < 8) db0[r] = to_bf16(dsv);
+          else db1[r - 8] = to_bf16(dsv);
+        }
+      };
+      bf16x8 e0, e1, f0, f1;
+      grads(s0, dp0, e0, e1);
+#pragma unroll
+      for (int ht = 0; ht < C::NH; ++ht) {
+        dq[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Kb, 0, ht, tro), e0, dq[ht], 0, 0, 0);
+        dq[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Kb, 16, ht, tro), e1, dq[ht], 0, 0, 0);
+      }
+      grads(s1, dp1, f0, f1);
+#pragma unroll
+      for (int ht = 0; ht < C::NH; ++ht) {
+        dq[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Kb, 32, ht, tro), f0, dq[ht], 0, 0, 0);
+        dq[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<HD>(Kb, 48, ht, tro), f1, dq[ht], 0, 0, 0);
+      }
+      if (more) wait_copies();
+      __syncthreads();
+      return;
+    }
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int kb0 = k0 + 32 * st;
