@@ -9,7 +9,7 @@
 //    the wave's K and V stay in registers as the B operands of
 //    S = Q K^T and dP = dO V^T (its keys are the columns); 64-query Q and dO
 //    tiles of every query head of the group stream through double-buffered
-//    LDS; dV^T += dO^T P and dK^T += Q^T dS take P and dS from the
+//    LDS (copied in pieces spread over the previous tile's work); dV^T += dO^T P and dK^T += Q^T dS take P and dS from the
 //    accumulators and dO^T, Q^T through the LDS transpose read.
 //  dQ pass: a workgroup owns 128 queries of one head (4 waves x 32); the
 //    wave's Q and dO stay in registers as the B operands of S^T = K Q^T and
@@ -39,7 +39,6 @@ constexpr int BS = 64;    // rows per streamed tile
 #endif
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_b;
-typedef uint32_t u32x4_b __attribute__((ext_vector_type(4)));
 
 // A 64-row tile of HD bf16 columns in LDS, rows unpadded. The 16-byte chunks
 // of row r sit in the order chunk ^ perm(r), perm depending on r mod 16 only.
@@ -102,18 +101,16 @@ struct TileCopy {
   }
 };
 
-// Register-staged copy of a 64-row tile into the same permuted layout: the
-// lane's 16-byte chunks of the wave's 1 KB pieces are loaded into registers
-// ahead of time and written to LDS later. Unlike the direct copy, no write
-// into LDS is then in flight while the other buffer is read, which keeps the
-// compiler's LDS wait counts exact.
+// Piecewise direct copy of a 64-row tile into the permuted layout (buffer
+// form): piece j of wave w can be issued at any point of a tile's work, so
+// the copy instructions spread over it. Rows at or past the end repeat the
+// last row without a branch (the offset is pulled back by the excess rows).
 template <int HD>
-struct StageCopy {
+struct PieceCopy {
   typedef Swz<HD> S;
   static constexpr int RPP = 512 / HD;   // tile rows per 1 KB piece
   uint32_t off[S::WP];                   // source byte offset of the lane's chunk of piece j (whole tile)
   int row0;                              // tile row of the lane's chunk in piece 0 (piece j: + j*RPP)
-  u32x4_b v[S::WP];
   __device__ __forceinline__ void init(int64_t ld, int w, int lane) {
     int r, col;
 #pragma unroll
@@ -124,15 +121,11 @@ struct StageCopy {
     S::piece(w, 0, lane, r, col);
     row0 = r;
   }
-  // piece j of rows r0 .. r0+63 of src (row stride ld); rows at or past n
-  // (r0 < n) repeat row n-1, whose products the callers mask
-  __device__ __forceinline__ void load(int j, const bf16* src, int64_t ld, int r0, int n) {
+  // piece j of rows r0 .. r0+63 of src (row stride ld) into tile; rows at or
+  // past n (r0 < n) repeat row n-1, whose products the callers mask
+  __device__ __forceinline__ void copy(int j, bf16* tile, const bf16* src, int64_t ld, int r0, int n, int w) const {
     const int ex = max(0, row0 + j * RPP - (n - 1 - r0));
-    const char* p = reinterpret_cast<const char*>(src + (int64_t)r0 * ld);
-    v[j] = *reinterpret_cast<const u32x4_b*>(p + (off[j] - (uint32_t)ex * (uint32_t)(ld * 2)));
-  }
-  __device__ __forceinline__ void store(int j, bf16* tile, int w, int lane) const {
-    *reinterpret_cast<u32x4_b*>(tile + (w * S::WP + j) * 512 + lane * 8) = v[j];
+    copy16_to_lds(src + (int64_t)r0 * ld, off[j] - (uint32_t)ex * (uint32_t)(ld * 2), tile + (w * S::WP + j) * 512);
   }
 };
 
@@ -297,7 +290,7 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
     for (int r = 0; r < 16; ++r) dk[i][r] = dv[i][r] = 0.f;
   const float sl2 = B_LOG2E / sqrtf((float)HD);
 
-  StageCopy<HD> cq, co;   // Q and dO tiles
+  PieceCopy<HD> cq, co;   // Q and dO tiles
   cq.init(ld, w, lane);
   co.init(ldo, w, lane);
   TrOffsets<HD> tro;
@@ -329,18 +322,14 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
       }
     }
   };
-  auto load_q = [&](int j) __attribute__((always_inline)) { cq.load(j, base + sh * HD, ld, sq0, Tn); };
-  auto load_o = [&](int j) __attribute__((always_inline)) { co.load(j, dbase + sh * HD, ldo, sq0, Tn); };
+  auto copy_q = [&](int j, bf16* Qn) __attribute__((always_inline)) { cq.copy(j, Qn, base + sh * HD, ld, sq0, Tn, w); };
+  auto copy_o = [&](int j, bf16* On) __attribute__((always_inline)) { co.copy(j, On, dbase + sh * HD, ldo, sq0, Tn, w); };
   auto load_lv = [&]() __attribute__((always_inline)) {
     if (tid < 2 * BS) {
       const int qi = min(sq0 + (tid & (BS - 1)), Tn - 1);
       const int64_t idx = ((int64_t)b * H + sh) * Tn + qi;
       lv = tid < BS ? lse[idx] : Dv[idx];
     }
-  };
-  auto put = [&](int j, bf16* Qn, bf16* On) __attribute__((always_inline)) {
-    cq.store(j, Qn, w, lane);
-    co.store(j, On, w, lane);
   };
   auto stash = [&](int buf) __attribute__((always_inline)) {
     if (tid < BS) Ls[buf][tid] = lv * B_LOG2E;
@@ -447,7 +436,7 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
 #pragma unroll
       for (int ss = 0; ss < C::NS; ++ss) {
 #pragma unroll
-        for (int j = C::WP * ss / C::NS; j < C::WP * (ss + 1) / C::NS; ++j) load_q(j);
+        for (int j = C::WP * ss / C::NS; j < C::WP * (ss + 1) / C::NS; ++j) copy_q(j, Qn);
         if (ss + 2 < C::NS) {
           ra[ss + 2] = *reinterpret_cast<const bf16x8*>(Qb + rro[ss + 2]);
           rb[ss + 2] = *reinterpret_cast<const bf16x8*>(Ob + rro[ss + 2]);
@@ -470,7 +459,7 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
 #pragma unroll
       for (int ss = 0; ss < C::NS; ++ss) {
 #pragma unroll
-        for (int j = C::WP * ss / C::NS; j < C::WP * (ss + 1) / C::NS; ++j) load_o(j);
+        for (int j = C::WP * ss / C::NS; j < C::WP * (ss + 1) / C::NS; ++j) copy_o(j, On);
         if (ss + 2 < C::NS) {
           qa[ss + 2] = *reinterpret_cast<const bf16x8*>(Qb + 32 * HD + rro[ss + 2]);
           oa[ss + 2] = *reinterpret_cast<const bf16x8*>(Ob + 32 * HD + rro[ss + 2]);
@@ -495,18 +484,16 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
         tb[j] = toper(Qb, Ob, 1, j);
         if ((j + 1) % FENCE3 == 0) __builtin_amdgcn_sched_barrier(0);
       }
-      // phase 4: accumulate sub-tile 1; write the staged tile to the free buffer
+      // phase 4: accumulate sub-tile 1
 #pragma unroll
-      for (int j = 0; j < NA; ++j) {
-        amma(j, tb[j], p10, p11, d10, d11);
-        if (j % 2 == 0 && j < 2 * C::WP) put(j / 2, Qn, On);
-      }
+      for (int j = 0; j < NA; ++j) amma(j, tb[j], p10, p11, d10, d11);
+      wait_copies();
       stash(buf ^ 1);
     } else {
 #pragma unroll
       for (int j = 0; j < C::WP; ++j) {
-        load_q(j);
-        load_o(j);
+        copy_q(j, Qn);
+        copy_o(j, On);
       }
       load_lv();
 #pragma unroll
@@ -522,8 +509,7 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
 #pragma unroll
         for (int t = 0; t < NA; ++t) amma(t, toper(Qb, Ob, u, t), pb0, pb1, db0, db1);
       }
-#pragma unroll
-      for (int j = 0; j < C::WP; ++j) put(j, Qn, On);
+      wait_copies();
       stash(buf ^ 1);
     }
     if (++cu_qt == qt0 + nqt) cu_qt = qt0;
@@ -533,12 +519,11 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
   pick_next(true);
 #pragma unroll
   for (int j = 0; j < C::WP; ++j) {
-    load_q(j);
-    load_o(j);
+    copy_q(j, Q0);
+    copy_o(j, O0);
   }
   load_lv();
-#pragma unroll
-  for (int j = 0; j < C::WP; ++j) put(j, Q0, O0);
+  wait_copies();
   stash(0);
   __syncthreads();
   for (int it = 0; it < n_it; it += 2) {
