@@ -52,6 +52,8 @@ int mt_op_rmsnorm_bwd(const float* x, const float* w, const float* rstd, const f
                       int32_t accumulate, float* dw, float* ws, int64_t rows, int32_t d, void* stream) {
   if (rows < 0 || d < 4 || d % 4 || d > 16384 || !w || !dw || !ws) return MT_EINVAL;
   if (rows > 0 && (!x || !rstd || !dy || !dx)) return MT_EINVAL;
+  auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  if (!a16(w) || !a16(ws) || (rows > 0 && (!a16(x) || !a16(dy) || !a16(dx)))) return MT_EINVAL;
   return hip_rc(rmsnorm_bwd(x, w, rstd, dy, dx, accumulate, dw, ws, rows, d, st(stream)));
 }
 

@@ -10,7 +10,7 @@ namespace mt {
 namespace {
 
 constexpr int RMS_MAX_D = 16384;
-constexpr int RMS_BWD_MAX_PARTIALS = 256;
+constexpr int RMS_BWD_MAX_PARTIALS = 1024;   // four row groups per CU
 
 template <typename T>
 __device__ __forceinline__ void store4(T* p, floatx4 v);
@@ -122,13 +122,27 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restric
 }
 
 // dw[c] = sum over partial rows in order.
-__global__ void reduce_rows_kernel(const float* __restrict__ ws, float* __restrict__ dw, int nparts,
-                                   int d) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= d) return;
-  float s = 0.f;
-  for (int p = 0; p < nparts; ++p) s += ws[(int64_t)p * d + c];
-  dw[c] = s;
+// dw[c] = sum over the partial rows, in a fixed order: a block owns 64
+// columns (16 float4 groups); its 16 lanes per group sum the partials
+// p = lane, lane + 16, ... in order, and the 16 lane sums are added in lane
+// order. Reads are 256-byte coalesced rows; d % 4 == 0.
+__global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restrict__ ws, float* __restrict__ dw,
+                                                          int nparts, int d) {
+  __shared__ floatx4 part[16][16];
+  const int cg = threadIdx.x & 15, pl = threadIdx.x >> 4;
+  const int c = blockIdx.x * 64 + cg * 4;
+  floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (c < d)
+    for (int p = pl; p < nparts; p += 16) s += *reinterpret_cast<const floatx4*>(ws + (int64_t)p * d + c);
+  part[pl][cg] = s;
+  __syncthreads();
+  if (pl == 0 && c < d) {
+    floatx4 t = part[0][cg];
+#pragma unroll
+    for (int q = 1; q < 16; ++q) t += part[q][cg];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dw[c + e] = t[e];   // dw needs no alignment
+  }
 }
 
 // ------------------------------------------------------------------- RoPE ---
@@ -289,7 +303,7 @@ hipError_t rmsnorm_bwd(const float* x, const float* w, const float* rstd, const 
   }
   // with no rows the reduction over zero partials writes dw = 0
   const int used = rows > 0 ? (int)((rows + rpb - 1) / rpb) : 0;
-  hipLaunchKernelGGL(reduce_rows_kernel, dim3((d + 255) / 256), dim3(256), 0, s, ws, dw, used, d);
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3((d + 63) / 64), dim3(256), 0, s, ws, dw, used, d);
   return hipGetLastError();
 }
 

@@ -49,7 +49,8 @@ int mt_op_rmsnorm_fwd(int32_t out_dtype, const float* x, const float* w, void* y
 /* RMSNorm backward given dy [rows, d] (fp32): dx = r (dy w - x r^2 mean(dy w x)),
  * written to dx (accumulate != 0: dx += ...), and dw[d] = sum over rows of
  * dy x r, summed in a fixed order. ws: mt_op_rmsnorm_bwd_ws_floats(rows, d)
- * floats of scratch. */
+ * floats of scratch. x, w, dy, dx and ws are read and written 16 bytes at a
+ * time and must be 16-byte aligned (MT_EINVAL otherwise). */
 int64_t mt_op_rmsnorm_bwd_ws_floats(int64_t rows, int32_t d);
 int mt_op_rmsnorm_bwd(const float* x, const float* w, const float* rstd, const float* dy,
                       float* dx, int32_t accumulate, float* dw, float* ws, int64_t rows,

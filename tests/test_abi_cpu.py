@@ -116,3 +116,19 @@ def test_rope_table_matches_oracle():
     c, s = mt.rope_table(524288, 2, 10000.0)
     t = 524287
     assert abs(c[t, 0] - math.cos(t)) < 1e-7 and abs(s[t, 0] - math.sin(t)) < 1e-7
+
+
+def test_rmsnorm_bwd_rejects_misaligned_operands():
+    # host-side argument checks run before any device call (addresses only)
+    L = mt.lib()
+    good, odd = ctypes.c_void_p(4096), ctypes.c_void_p(4100)
+    args = [good] * 5 + [1, good, good, 8, 64, None]
+    for i in (1, 7):   # w, ws
+        a = list(args)
+        a[i] = odd
+        assert L.mt_op_rmsnorm_bwd(*a) == mt.MT_EINVAL
+    for i in (0, 3, 4):   # x, dy, dx
+        a = list(args)
+        a[i] = odd
+        assert L.mt_op_rmsnorm_bwd(*a) == mt.MT_EINVAL
+    assert mt.rmsnorm_bwd_ws_floats(4096, 5120) == 1024 * 5120
