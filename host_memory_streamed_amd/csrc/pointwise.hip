@@ -180,6 +180,46 @@ __global__ __launch_bounds__(256) void rope_kernel(const float* __restrict__ in,
   }
 }
 
+// The same rotation four pairs per thread with 16-byte loads (hd % 8 == 0,
+// rows and tables 16-byte aligned).
+template <typename OutT>
+__global__ __launch_bounds__(256) void rope4_kernel(const float* __restrict__ in, OutT* __restrict__ out,
+                                                    const float* __restrict__ cosv,
+                                                    const float* __restrict__ sinv, int64_t row0,
+                                                    int Tn, int H, int Hkv, int hd, int backward) {
+  const int64_t m = blockIdx.x;
+  const int t = (int)((row0 + m) % Tn);
+  const int half = hd / 2, q4 = half / 4;
+  const int rot = (H + Hkv) * q4;         // rotated quads
+  const int width = (H + 2 * Hkv) * hd;
+  const float* ir = in + m * width;
+  OutT* orow = out + m * width;
+  const float* cr = cosv + (int64_t)t * half;
+  const float* sr = sinv + (int64_t)t * half;
+  const int total = rot + Hkv * hd / 4;
+  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+    if (idx < rot) {
+      const int head = idx / q4, i = (idx % q4) * 4;
+      const int c1 = head * hd + i, c2 = c1 + half;
+      const floatx4 x1 = *reinterpret_cast<const floatx4*>(ir + c1);
+      const floatx4 x2 = *reinterpret_cast<const floatx4*>(ir + c2);
+      const floatx4 cs = *reinterpret_cast<const floatx4*>(cr + i);
+      const floatx4 sn = *reinterpret_cast<const floatx4*>(sr + i);
+      floatx4 o1, o2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (backward) { o1[e] = x1[e] * cs[e] + x2[e] * sn[e]; o2[e] = x2[e] * cs[e] - x1[e] * sn[e]; }
+        else          { o1[e] = x1[e] * cs[e] - x2[e] * sn[e]; o2[e] = x2[e] * cs[e] + x1[e] * sn[e]; }
+      }
+      store4<OutT>(orow + c1, o1);
+      store4<OutT>(orow + c2, o2);
+    } else {
+      const int c = (H + Hkv) * hd + (idx - rot) * 4;
+      store4<OutT>(orow + c, *reinterpret_cast<const floatx4*>(ir + c));
+    }
+  }
+}
+
 // ----------------------------------------------------------------- SwiGLU ---
 
 __device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + expf(-x)); }
@@ -311,10 +351,18 @@ hipError_t rope(int out_dtype, int backward, const float* in, void* out, const f
                 const float* sinv, int64_t row0, int64_t rows, int Tn, int H, int Hkv, int hd,
                 hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  if (out_dtype == 1)
+  auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  const bool vec = hd % 8 == 0 && a16(in) && a16(cosv) && a16(sinv) && (out_dtype == 1 ? ((uintptr_t)out & 7) == 0 : a16(out));
+  if (vec) {
+    if (out_dtype == 1)
+      hipLaunchKernelGGL(rope4_kernel<bf16>, dim3((unsigned)rows), dim3(256), 0, s, in, (bf16*)out, cosv, sinv, row0, Tn, H, Hkv, hd, backward);
+    else
+      hipLaunchKernelGGL(rope4_kernel<float>, dim3((unsigned)rows), dim3(256), 0, s, in, (float*)out, cosv, sinv, row0, Tn, H, Hkv, hd, backward);
+  } else if (out_dtype == 1) {
     hipLaunchKernelGGL(rope_kernel<bf16>, dim3((unsigned)rows), dim3(256), 0, s, in, (bf16*)out, cosv, sinv, row0, Tn, H, Hkv, hd, backward);
-  else
+  } else {
     hipLaunchKernelGGL(rope_kernel<float>, dim3((unsigned)rows), dim3(256), 0, s, in, (float*)out, cosv, sinv, row0, Tn, H, Hkv, hd, backward);
+  }
   return hipGetLastError();
 }
 
