@@ -136,7 +136,7 @@ def cpu_baseline(w, budget_tokens=512):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="14b", help="tiny | 1.3b | 14b | 120b (120b: --layers)")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
