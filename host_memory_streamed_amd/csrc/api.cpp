@@ -354,6 +354,7 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
   ok &= dalloc(M * D.qkvd * es, &w.dqkv_s);
   ok &= dalloc((size_t)mt_op_attn_bwd_ws_bytes(S, cfg->max_batch, cfg->max_seq, D.H, D.hd), &w.attn_ws);
   ok &= dalloc((size_t)rmsnorm_bwd_partials(M) * d * 4, (void**)&w.rms_ws);
+  ok &= dalloc((size_t)GEMM_WS_BYTES, &w.gemm_ws);
   w.hf = w.h;   // the head runs between the last forward and the first recompute
   ok &= dalloc(M * 4, (void**)&w.rstdf);
   // logits in token chunks of at most ~4 GiB (multiples of 128 rows)

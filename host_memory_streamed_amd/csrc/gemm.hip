@@ -431,12 +431,28 @@ struct BigNat {
   }
 };
 
+// Tile id -> (tile row, tile column): groups of 8 tile rows, column-major
+// inside a group, so that concurrent workgroups share A rows and B columns.
+__device__ __forceinline__ void big_tile(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int group = 8 * tiles_n;
+  const int first_m = (pid / group) * 8;
+  const int gsize = min(tiles_m - first_m, 8);
+  tm = first_m + (pid % group) % gsize;
+  tn = (pid % group) / gsize;
+}
+
+// C = A B (+R) over 256x256 tiles. Workgroups [0, full_wgs) each own a tile
+// over the whole K range. With ks > 1, the remaining tiles are split along K:
+// workgroup full_wgs + j works on tile full_wgs + j / ks, K block j % ks (kc_k
+// values each); block 0 writes C (+R), block s > 0 writes its 256x256 partial
+// to ws slab (tile - full_wgs) * (ks - 1) + s - 1, for gemm_big_fixup.
 template <typename T, int LAYOUT>
-__global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __restrict__ A, int64_t lda,
-                                                                  const T* __restrict__ B, int64_t ldb,
-                                                                  float* C, int64_t ldc, const float* R,
-                                                                  int64_t ldr, int M, int N, int K,
-                                                                  int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __restrict__ A_, int64_t lda,
+                                                                  const T* __restrict__ B_, int64_t ldb,
+                                                                  float* C_, int64_t ldc_, const float* R_,
+                                                                  int64_t ldr, int M, int N, int K_,
+                                                                  int tiles_m, int tiles_n, int full_wgs, int ks,
+                                                                  int kc_k, float* ws) {
   constexpr bool A_KC = (LAYOUT != MT_GEMM_TN);
   constexpr bool B_KC = (LAYOUT == MT_GEMM_NT);
   // bf16 M/N-contiguous operands stay in their natural layout (BigNat);
@@ -456,15 +472,34 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
   const int wm = wave >> 2, wn = wave & 3;       // 2 x 4 waves
   const int g = lane >> 5, l32 = lane & 31;
 
-  const int nwg = tiles_m * tiles_n;
-  const int pid = remap_tile(blockIdx.x, nwg);
-  const int group = 8 * tiles_n;
-  const int first_m = (pid / group) * 8;
-  const int gsize = min(tiles_m - first_m, 8);
-  const int tm = first_m + (pid % group) % gsize;
-  const int tn = (pid % group) / gsize;
+  int pid, split = 0;
+  if ((int)blockIdx.x < full_wgs) {
+    pid = remap_tile(blockIdx.x, full_wgs);
+  } else {
+    const int j = blockIdx.x - full_wgs;
+    pid = full_wgs + j / ks;
+    split = j % ks;
+  }
+  int tm, tn;
+  big_tile(pid, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BIG, n0 = tn * BIG;
   const bool full = (m0 + BIG <= M) && (n0 + BIG <= N);
+  // this workgroup's K range, operands and output
+  const int k_begin = split * kc_k;
+  const int K = (int)blockIdx.x < full_wgs ? K_ : min(K_ - k_begin, kc_k);
+  const T* __restrict__ A = A_ + (A_KC ? (int64_t)k_begin : (int64_t)k_begin * lda);
+  const T* __restrict__ B = B_ + (B_KC ? (int64_t)k_begin : (int64_t)k_begin * ldb);
+  float* C = C_;
+  int64_t ldc = ldc_;
+  const float* R = R_;
+  int ro = 0, co = 0;   // output origin (partials are tile-local)
+  if (split > 0) {
+    C = ws + ((int64_t)(pid - full_wgs) * (ks - 1) + split - 1) * BIG * BIG;
+    ldc = BIG;
+    R = nullptr;
+    ro = m0;
+    co = n0;
+  }
 
   // LDS read offsets of this lane's rows (chunk added per k-step)
   int a_base[4], a_x[4], b_base[2], b_x[2];
@@ -654,10 +689,30 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
         if (row < M) {
           float val = acc[i][j][r];
           if (R) val += R[(int64_t)row * ldr + col];
-          C[(int64_t)row * ldc + col] = val;
+          C[(int64_t)(row - ro) * ldc + (col - co)] = val;
         }
       }
     }
+}
+
+// C += the K-block partials of the split tiles, blocks 1 .. ks-1 in order.
+// Block (t, y): tile full_wgs + t, 1024 of its elements (4 per thread).
+__global__ __launch_bounds__(256) void gemm_big_fixup(float* C, int64_t ldc, const float* __restrict__ ws, int M,
+                                                      int N, int tiles_m, int tiles_n, int full_wgs, int ks) {
+  const int t = blockIdx.x;
+  int tm, tn;
+  big_tile(full_wgs + t, tiles_m, tiles_n, tm, tn);
+  const int e = (blockIdx.y * 256 + threadIdx.x) * 4;   // element of the tile, row-major
+  const int r = e / BIG, c = e % BIG;
+  const float* p = ws + (int64_t)t * (ks - 1) * BIG * BIG + e;
+  floatx4 v = *reinterpret_cast<const floatx4*>(p);
+  for (int s = 1; s < ks - 1; ++s) v += *reinterpret_cast<const floatx4*>(p + (int64_t)s * BIG * BIG);
+  const int row = tm * BIG + r, col = tn * BIG + c;
+  if (row >= M) return;
+  float* dst = C + (int64_t)row * ldc + col;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (col + q < N) dst[q] += v[q];
 }
 
 // C = R (or 0) for K = 0
@@ -681,12 +736,50 @@ hipError_t launch(const void* A, int64_t lda, const void* B, int64_t ldb, float*
   return hipGetLastError();
 }
 
+// compute units of the current device (one workgroup of 512 threads each)
+int gemm_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
 template <typename T, int LAYOUT>
 hipError_t launch_big(const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc,
-                      const float* R, int64_t ldr, int M, int N, int K, hipStream_t s) {
+                      const float* R, int64_t ldr, int M, int N, int K, float* ws, int64_t ws_bytes,
+                      hipStream_t s) {
   const int tm = (M + BIG - 1) / BIG, tn = (N + BIG - 1) / BIG;
-  hipLaunchKernelGGL((gemm_big_kernel<T, LAYOUT>), dim3(tm * tn), dim3(BIG_THREADS), 0, s,
-                     (const T*)A, lda, (const T*)B, ldb, C, ldc, R, ldr, M, N, K, tm, tn);
+  const int tiles = tm * tn;
+  constexpr int BK = BIG_ROW / sizeof(T);
+  // the tiles of a last, at most half-full wave of workgroups (or of a grid
+  // of at most half a wave) are split along K so that they fill it
+  const int wave = gemm_cus();
+  const int q = tiles / wave, r = tiles % wave;
+  int full_wgs = tiles, ks = 1, kc_k = K;
+  if (ws && r > 0 && 2 * r <= wave && (q * wave) % 8 == 0) {
+    const int nk = (K + BK - 1) / BK;
+    const int want = std::min(wave / r, nk / 4);       // at least 4 K stages per block
+    if (want >= 2) {
+      const int kb = (nk + want - 1) / want;           // K stages per block
+      const int n = (nk + kb - 1) / kb;                 // non-empty blocks
+      if (n >= 2 && (int64_t)r * (n - 1) * BIG * BIG * 4 <= ws_bytes) {
+        full_wgs = q * wave;
+        ks = n;
+        kc_k = kb * BK;
+      }
+    }
+  }
+  hipLaunchKernelGGL((gemm_big_kernel<T, LAYOUT>), dim3(full_wgs + (tiles - full_wgs) * ks), dim3(BIG_THREADS), 0,
+                     s, (const T*)A, lda, (const T*)B, ldb, C, ldc, R, ldr, M, N, K, tm, tn, full_wgs, ks, kc_k, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ks == 1) return e;
+  hipLaunchKernelGGL(gemm_big_fixup, dim3(tiles - full_wgs, BIG * BIG / 1024), dim3(256), 0, s, C, ldc,
+                     (const float*)ws, M, N, tm, tn, full_wgs, ks);
   return hipGetLastError();
 }
 
@@ -698,34 +791,54 @@ bool big_ok(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, i
 
 }  // namespace
 
+hipError_t gemm_impl(int dtype, int layout, const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
+                     int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N, int64_t K, int variant,
+                     void* ws, int64_t ws_bytes, hipStream_t s);
+
 hipError_t gemm(int dtype, int layout, const void* A, int64_t lda, const void* B, int64_t ldb,
                 float* C, int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N,
                 int64_t K, hipStream_t s) {
-  return gemm_variant(dtype, layout, A, lda, B, ldb, C, ldc, R, ldr, M, N, K, 0, s);
+  return gemm_impl(dtype, layout, A, lda, B, ldb, C, ldc, R, ldr, M, N, K, 0, nullptr, 0, s);
 }
 
 hipError_t gemm_variant(int dtype, int layout, const void* A, int64_t lda, const void* B, int64_t ldb,
                         float* C, int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N,
                         int64_t K, int variant, hipStream_t s) {
+  return gemm_impl(dtype, layout, A, lda, B, ldb, C, ldc, R, ldr, M, N, K, variant, nullptr, 0, s);
+}
+
+hipError_t gemm_ws(int dtype, int layout, const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
+                   int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N, int64_t K, void* ws,
+                   int64_t ws_bytes, hipStream_t s) {
+  return gemm_impl(dtype, layout, A, lda, B, ldb, C, ldc, R, ldr, M, N, K, 0, ws, ws_bytes, s);
+}
+
+hipError_t gemm_impl(int dtype, int layout, const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
+                     int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N, int64_t K, int variant,
+                     void* ws, int64_t ws_bytes, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
   if (K > 0) {
     // 256x256 tiles when operands are 16-byte aligned and the grid still has
-    // at least about half a wave of workgroups per CU; else 128x128 tiles
+    // at least about half a wave of workgroups per CU, counting the K splits
+    // of a small grid when a workspace allows them; else 128x128 tiles
     const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    const bool use_big = variant == 2 || (variant == 0 && big_tiles >= 128);
+    const int64_t nk = (K + 63) / 64;
+    const int64_t splits = ws && big_tiles < gemm_cus() ? std::min<int64_t>(gemm_cus() / big_tiles, nk / 4) : 1;
+    const bool use_big = variant == 2 || (variant == 0 && big_tiles * std::max<int64_t>(splits, 1) >= 128);
+    float* wsf = ws_bytes > 0 ? static_cast<float*>(ws) : nullptr;
     if (use_big && big_ok(dtype, A, lda, B, ldb, M, N)) {
       const int m = (int)M, n = (int)N, k = (int)K;
       if (dtype == 1) {
         switch (layout) {
-          case MT_GEMM_NT: return launch_big<bf16, MT_GEMM_NT>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
-          case MT_GEMM_NN: return launch_big<bf16, MT_GEMM_NN>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
-          default: return launch_big<bf16, MT_GEMM_TN>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
+          case MT_GEMM_NT: return launch_big<bf16, MT_GEMM_NT>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, wsf, ws_bytes, s);
+          case MT_GEMM_NN: return launch_big<bf16, MT_GEMM_NN>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, wsf, ws_bytes, s);
+          default: return launch_big<bf16, MT_GEMM_TN>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, wsf, ws_bytes, s);
         }
       }
       switch (layout) {
-        case MT_GEMM_NT: return launch_big<float, MT_GEMM_NT>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
-        case MT_GEMM_NN: return launch_big<float, MT_GEMM_NN>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
-        default: return launch_big<float, MT_GEMM_TN>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, s);
+        case MT_GEMM_NT: return launch_big<float, MT_GEMM_NT>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, wsf, ws_bytes, s);
+        case MT_GEMM_NN: return launch_big<float, MT_GEMM_NN>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, wsf, ws_bytes, s);
+        default: return launch_big<float, MT_GEMM_TN>(A, lda, B, ldb, C, ldc, R, ldr, m, n, k, wsf, ws_bytes, s);
       }
     }
   }

@@ -17,6 +17,14 @@ hipError_t gemm(int dtype, int layout, const void* A, int64_t lda, const void* B
 hipError_t gemm_variant(int dtype, int layout, const void* A, int64_t lda, const void* B, int64_t ldb,
                         float* C, int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N,
                         int64_t K, int variant, hipStream_t s);
+// As gemm; with a device workspace of ws_bytes (GEMM_WS_BYTES enables every
+// split), the tiles of a last, at most half-full wave of 256x256 workgroups
+// are split along K and their partials added in a fixed order. Calls that
+// share a workspace must be ordered (one stream).
+constexpr int64_t GEMM_WS_BYTES = 64ll << 20;
+hipError_t gemm_ws(int dtype, int layout, const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
+                   int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N, int64_t K, void* ws,
+                   int64_t ws_bytes, hipStream_t s);
 
 bool attn_supported(int dtype, int hd);
 // bf16 forward on 32x32 matrix-core tiles (hd 64 or 128), attn_fwd_bf16.hip

@@ -83,7 +83,7 @@ static int qkv_forward(Ctx& c, const LayerPtrs& W, int64_t M, int T) {
     const void* h = static_cast<const char*>(w.h) + r0 * d * esz(S);
     void* qs = static_cast<char*>(w.qkv_s) + r0 * D.qkvd * esz(S);
     RUN(K_GEMM_NT, 2.0 * mc * D.qkvd * d, gemm_bytes(mc, D.qkvd, d, S, false),
-        gemm(S, MT_GEMM_NT, h, d, W.wqkv, d, w.qkv_f, D.qkvd, nullptr, 0, mc, D.qkvd, d, c.s_comp));
+        gemm_ws(S, MT_GEMM_NT, h, d, W.wqkv, d, w.qkv_f, D.qkvd, nullptr, 0, mc, D.qkvd, d, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
     RUN(K_ROPE, 0, (double)mc * D.qkvd * (4 + esz(S)),
         rope(S, 0, w.qkv_f, qs, w.rope_cos, w.rope_sin, r0, mc, T, D.H, D.Hkv, D.hd, c.s_comp));
   }
@@ -100,7 +100,7 @@ static int mlp_front(Ctx& c, const LayerPtrs& W, int64_t r0, int64_t mc) {
   RUN(K_RMS_FWD, 0, (double)mc * d * (4 + esz(S)),
       rmsnorm_fwd(S, w.x1 + r0 * d, W.mlp_norm, w.h2, w.rstd2 + r0, mc, D.d, c.cfg.rms_eps, c.s_comp));
   RUN(K_GEMM_NT, 2.0 * mc * 2 * F * d, gemm_bytes(mc, 2 * F, d, S, false),
-      gemm(S, MT_GEMM_NT, w.h2, d, W.wgu, d, w.gu_f, 2 * F, nullptr, 0, mc, 2 * F, d, c.s_comp));
+      gemm_ws(S, MT_GEMM_NT, w.h2, d, W.wgu, d, w.gu_f, 2 * F, nullptr, 0, mc, 2 * F, d, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
   RUN(K_SWIGLU, 0, (double)mc * F * (8 + esz(S)), swiglu_fwd(S, w.gu_f, w.act, mc, D.F, c.s_comp));
   return MT_OK;
 }
@@ -120,7 +120,7 @@ int layer_forward(Ctx& c, const LayerPtrs& W, int l, int B, int T, bool recomput
   RUN(K_ATTN_FWD, attn_fl, (double)M * D.qkvd * esz(S) + (double)M * D.qd * (4 + (S ? 2 : 0)),
       attn_fwd(S, w.qkv_s, w.o_f, S ? w.o_s : nullptr, w.lse, B, T, D.H, D.Hkv, D.hd, c.s_comp));
   RUN(K_GEMM_NT, 2.0 * M * d * D.qd, gemm_bytes(M, d, D.qd, S, true),
-      gemm(S, MT_GEMM_NT, w.o_s, D.qd, W.wo, D.qd, w.x1, d, x, d, M, d, D.qd, c.s_comp));
+      gemm_ws(S, MT_GEMM_NT, w.o_s, D.qd, W.wo, D.qd, w.x1, d, x, d, M, d, D.qd, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
   // the recompute stops here: the backward rebuilds the MLP chunk by chunk
   if (recompute) return MT_OK;
   float* xn = c.ckpt_dev(l + 1);
@@ -128,7 +128,7 @@ int layer_forward(Ctx& c, const LayerPtrs& W, int l, int B, int T, bool recomput
     const int64_t mc = std::min(w.chunk, M - r0);
     if ((rc = mlp_front(c, W, r0, mc))) return rc;
     RUN(K_GEMM_NT, 2.0 * mc * d * F, gemm_bytes(mc, d, F, S, true),
-        gemm(S, MT_GEMM_NT, w.act, F, W.wdown, F, xn + r0 * d, d, w.x1 + r0 * d, d, mc, d, F, c.s_comp));
+        gemm_ws(S, MT_GEMM_NT, w.act, F, W.wdown, F, xn + r0 * d, d, w.x1 + r0 * d, d, mc, d, F, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
   }
   return MT_OK;
 }
@@ -156,34 +156,34 @@ int layer_backward(Ctx& c, const LayerPtrs& W, int l, int B, int T, float* gu) {
     const void* gs = static_cast<const char*>(w.g_s) + r0 * d * esz(S);
     if ((rc = mlp_front(c, W, r0, mc))) return rc;
     RUN(K_GEMM_NN, 2.0 * mc * F * d, gemm_bytes(mc, F, d, S, false),
-        gemm(S, MT_GEMM_NN, gs, d, W.wdown, F, w.dact_f, F, nullptr, 0, mc, F, d, c.s_comp));
+        gemm_ws(S, MT_GEMM_NN, gs, d, W.wdown, F, w.dact_f, F, nullptr, 0, mc, F, d, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
     RUN(K_GEMM_TN, 2.0 * d * F * mc, gemm_bytes(d, F, mc, S, acc),
-        gemm(S, MT_GEMM_TN, gs, d, w.act, F, gu + U.off[5], F, acc ? gu + U.off[5] : nullptr, F, d, F, mc,
-             c.s_comp));
+        gemm_ws(S, MT_GEMM_TN, gs, d, w.act, F, gu + U.off[5], F, acc ? gu + U.off[5] : nullptr, F, d, F, mc,
+                w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
     RUN(K_SWIGLU, 0, (double)mc * F * (12 + 2 * esz(S)), swiglu_bwd(S, w.gu_f, w.dact_f, w.dgu_s, mc, D.F, c.s_comp));
     RUN(K_GEMM_NN, 2.0 * mc * d * 2 * F, gemm_bytes(mc, d, 2 * F, S, false),
-        gemm(S, MT_GEMM_NN, w.dgu_s, 2 * F, W.wgu, d, w.dh_f + r0 * d, d, nullptr, 0, mc, d, 2 * F, c.s_comp));
+        gemm_ws(S, MT_GEMM_NN, w.dgu_s, 2 * F, W.wgu, d, w.dh_f + r0 * d, d, nullptr, 0, mc, d, 2 * F, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
     RUN(K_GEMM_TN, 2.0 * 2 * F * d * mc, gemm_bytes(2 * F, d, mc, S, acc),
-        gemm(S, MT_GEMM_TN, w.dgu_s, 2 * F, w.h2, d, gu + U.off[4], d, acc ? gu + U.off[4] : nullptr, d, 2 * F,
-             d, mc, c.s_comp));
+        gemm_ws(S, MT_GEMM_TN, w.dgu_s, 2 * F, w.h2, d, gu + U.off[4], d, acc ? gu + U.off[4] : nullptr, d, 2 * F,
+                d, mc, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
   }
   RUN(K_RMS_BWD, 0, (double)M * d * 20,
       rmsnorm_bwd(w.x1, W.mlp_norm, w.rstd2, w.dh_f, w.g_f, 1, gu + U.off[1], w.rms_ws, M, D.d, c.s_comp));
   // out projection: x1 = x + o Wo^T
   if (S) RUN(K_CAST, 0, (double)M * d * 6, cast(S, w.g_f, w.g_s, M * d, c.s_comp));
   RUN(K_GEMM_NN, 2.0 * M * qd * d, gemm_bytes(M, qd, d, S, false),
-      gemm(S, MT_GEMM_NN, w.g_s, d, W.wo, qd, w.do_f, qd, nullptr, 0, M, qd, d, c.s_comp));
+      gemm_ws(S, MT_GEMM_NN, w.g_s, d, W.wo, qd, w.do_f, qd, nullptr, 0, M, qd, d, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
   RUN(K_GEMM_TN, 2.0 * d * qd * M, gemm_bytes(d, qd, M, S, false),
-      gemm(S, MT_GEMM_TN, w.g_s, d, w.o_s, qd, gu + U.off[3], qd, nullptr, 0, d, qd, M, c.s_comp));
+      gemm_ws(S, MT_GEMM_TN, w.g_s, d, w.o_s, qd, gu + U.off[3], qd, nullptr, 0, d, qd, M, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
   // attention, with the rotation's backward applied as the gradients are written
   RUN(K_ATTN_BWD, 2.5 * attn_fl, (double)M * qkvd * 2 * esz(S) + (double)M * qd * 8,
       attn_bwd(S, w.qkv_s, w.o_f, w.do_f, w.lse, w.dqkv_s, S, w.rope_cos, w.rope_sin, w.attn_ws, B, T, D.H,
                D.Hkv, D.hd, c.s_comp));
   // qkv projection
   RUN(K_GEMM_NN, 2.0 * M * d * qkvd, gemm_bytes(M, d, qkvd, S, false),
-      gemm(S, MT_GEMM_NN, w.dqkv_s, qkvd, W.wqkv, d, w.dh_f, d, nullptr, 0, M, d, qkvd, c.s_comp));
+      gemm_ws(S, MT_GEMM_NN, w.dqkv_s, qkvd, W.wqkv, d, w.dh_f, d, nullptr, 0, M, d, qkvd, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
   RUN(K_GEMM_TN, 2.0 * qkvd * d * M, gemm_bytes(qkvd, d, M, S, false),
-      gemm(S, MT_GEMM_TN, w.dqkv_s, qkvd, w.h, d, gu + U.off[2], d, nullptr, 0, qkvd, d, M, c.s_comp));
+      gemm_ws(S, MT_GEMM_TN, w.dqkv_s, qkvd, w.h, d, gu + U.off[2], d, nullptr, 0, qkvd, d, M, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
   RUN(K_RMS_BWD, 0, (double)M * d * 20,
       rmsnorm_bwd(x, W.attn_norm, w.rstd1, w.dh_f, w.g_f, 1, gu + U.off[0], w.rms_ws, M, D.d, c.s_comp));
   return MT_OK;
@@ -207,13 +207,13 @@ int head_forward_backward(Ctx& c, const void* image, int B, int T, float* gu) {
     const int64_t mc = std::min(w.head_chunk, M - r0);
     const void* hf = static_cast<const char*>(w.hf) + r0 * d * esz(S);
     RUN(K_GEMM_NT, 2.0 * mc * V * d, gemm_bytes(mc, V, d, S, false),
-        gemm(S, MT_GEMM_NT, hf, d, w_head, d, w.logits, V, nullptr, 0, mc, V, d, c.s_comp));
+        gemm_ws(S, MT_GEMM_NT, hf, d, w_head, d, w.logits, V, nullptr, 0, mc, V, d, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
     RUN(K_XENT, 0, (double)mc * V * (4 + esz(S)),
         xent(S, w.logits, w.targets + r0, w.tok_loss + r0, w.dz_s, mc, (int)V, scale, c.s_comp));
     RUN(K_GEMM_TN, 2.0 * V * d * mc, gemm_bytes(V, d, mc, S, r0 > 0),
-        gemm(S, MT_GEMM_TN, w.dz_s, V, hf, d, d_head, d, r0 > 0 ? d_head : nullptr, d, V, d, mc, c.s_comp));
+        gemm_ws(S, MT_GEMM_TN, w.dz_s, V, hf, d, d_head, d, r0 > 0 ? d_head : nullptr, d, V, d, mc, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
     RUN(K_GEMM_NN, 2.0 * mc * d * V, gemm_bytes(mc, d, V, S, false),
-        gemm(S, MT_GEMM_NN, w.dz_s, V, w_head, d, w.dh_f + r0 * d, d, nullptr, 0, mc, d, V, c.s_comp));
+        gemm_ws(S, MT_GEMM_NN, w.dz_s, V, w_head, d, w.dh_f + r0 * d, d, nullptr, 0, mc, d, V, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
   }
   RUN(K_RMS_BWD, 0, (double)M * d * 20,
       rmsnorm_bwd(x, w_norm, w.rstdf, w.dh_f, w.g_f, 0, gu + U.off[0], w.rms_ws, M, D.d, c.s_comp));

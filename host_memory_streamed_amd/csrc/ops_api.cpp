@@ -36,6 +36,23 @@ int mt_op_gemm_variant(int32_t dtype, int32_t layout, const void* A, int64_t lda
   return hip_rc(gemm_variant(dtype, layout, A, lda, B, ldb, C, ldc, R, ldr, M, N, K, variant, st(stream)));
 }
 
+int64_t mt_op_gemm_ws_bytes(void) { return GEMM_WS_BYTES; }
+
+int mt_op_gemm_ws(int32_t dtype, int32_t layout, const void* A, int64_t lda, const void* B, int64_t ldb,
+                  float* C, int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N, int64_t K,
+                  void* ws, int64_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || layout < MT_GEMM_NT || layout > MT_GEMM_TN) return MT_EINVAL;
+  if (M < 0 || N < 0 || K < 0 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || ws_bytes < 0) return MT_EINVAL;
+  if (ws_bytes > 0 && (!ws || ((uintptr_t)ws & 15))) return MT_EINVAL;
+  if (M == 0 || N == 0) return MT_OK;
+  if (!C || (K > 0 && (!A || !B))) return MT_EINVAL;
+  const int64_t a_cols = layout == MT_GEMM_TN ? M : K;
+  const int64_t b_cols = layout == MT_GEMM_NT ? K : N;
+  if (lda < a_cols || ldb < b_cols || ldc < N || (R && ldr < N)) return MT_EINVAL;
+  return hip_rc(gemm_ws(dtype, layout, A, lda, B, ldb, C, ldc, R, ldr, M, N, K, ws_bytes > 0 ? ws : nullptr,
+                        ws_bytes, st(stream)));
+}
+
 int mt_op_rmsnorm_fwd(int32_t out_dtype, const float* x, const float* w, void* y, float* rstd, int64_t rows,
                       int32_t d, float eps, void* stream) {
   if (!dtype_ok(out_dtype) || rows < 0 || d < 4 || d % 4 || d > 16384) return MT_EINVAL;

@@ -146,6 +146,7 @@ struct Workspace {
   void* dqkv_s = nullptr;   // gradient of the unrotated projection output
   void* attn_ws = nullptr;
   float* rms_ws = nullptr;
+  void* gemm_ws = nullptr;  // K-split partials of the GEMMs (GEMM_WS_BYTES)
   // head
   void* hf = nullptr;       // shares h's memory
   float* rstdf = nullptr;

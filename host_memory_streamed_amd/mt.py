@@ -88,6 +88,9 @@ _SIGS = {
     "mt_op_gemm": (ctypes.c_int, [_I32, _I32, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _P]),
     "mt_op_gemm_variant": (ctypes.c_int, [_I32, _I32, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64,
                                           _I32, _P]),
+    "mt_op_gemm_ws_bytes": (_I64, []),
+    "mt_op_gemm_ws": (ctypes.c_int, [_I32, _I32, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _I64,
+                                     _P]),
     "mt_op_rmsnorm_fwd": (ctypes.c_int, [_I32, _P, _P, _P, _P, _I64, _I32, _F, _P]),
     "mt_op_rmsnorm_bwd_ws_floats": (_I64, [_I64, _I32]),
     "mt_op_rmsnorm_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _P, _P, _I64, _I32, _P]),
@@ -292,6 +295,15 @@ def _stream(stream):
 def gemm(dtype, layout, A, lda, B, ldb, C, ldc, M, N, K, R=None, ldr=0, stream=None, variant=0):
     _check(lib().mt_op_gemm_variant(dtype, layout, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(R), ldr, M, N,
                                     K, variant, _stream(stream)))
+
+
+def gemm_ws_bytes():
+    return lib().mt_op_gemm_ws_bytes()
+
+
+def gemm_ws(dtype, layout, A, lda, B, ldb, C, ldc, M, N, K, ws, ws_bytes, R=None, ldr=0, stream=None):
+    _check(lib().mt_op_gemm_ws(dtype, layout, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(R), ldr, M, N, K,
+                               _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def rmsnorm_fwd(out_dtype, x, w, y, rstd, rows, d, eps, stream=None):

@@ -41,6 +41,19 @@ int mt_op_gemm_variant(int32_t dtype, int32_t layout, const void* A, int64_t lda
                        int64_t ldb, float* C, int64_t ldc, const float* R, int64_t ldr, int64_t M,
                        int64_t N, int64_t K, int32_t variant, void* stream);
 
+/* mt_op_gemm with a device workspace ws of ws_bytes (16-byte aligned; NULL or
+ * 0 bytes: no split, as mt_op_gemm). When the 256x256 tiles of the product
+ * leave the last wave of workgroups at most half full (or fill at most half
+ * of one), those tiles are split along K: the split blocks write partials to
+ * ws, and a second kernel adds them to C in a fixed order (deterministic;
+ * the rounding differs from the unsplit product by the summation order).
+ * mt_op_gemm_ws_bytes() is the size that allows every split. Calls sharing
+ * a workspace must be ordered on one stream. */
+int64_t mt_op_gemm_ws_bytes(void);
+int mt_op_gemm_ws(int32_t dtype, int32_t layout, const void* A, int64_t lda, const void* B, int64_t ldb,
+                  float* C, int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N, int64_t K,
+                  void* ws, int64_t ws_bytes, void* stream);
+
 /* RMSNorm forward over rows of x [rows, d] (fp32): y = x r w with
  * r = (mean(x^2) + eps)^(-1/2), written as out_dtype; rstd[rows] = r. */
 int mt_op_rmsnorm_fwd(int32_t out_dtype, const float* x, const float* w, void* y, float* rstd,

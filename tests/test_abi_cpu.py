@@ -118,6 +118,17 @@ def test_rope_table_matches_oracle():
     assert abs(c[t, 0] - math.cos(t)) < 1e-7 and abs(s[t, 0] - math.sin(t)) < 1e-7
 
 
+def test_gemm_ws_rejects_bad_workspace():
+    # host-side argument checks run before any device call (addresses only)
+    L = mt.lib()
+    good, odd = ctypes.c_void_p(4096), ctypes.c_void_p(4100)
+    base = [mt.MT_BF16, mt.MT_GEMM_NT, good, 64, good, 64, good, 64, None, 0, 64, 64, 64]
+    assert L.mt_op_gemm_ws(*base, odd, 1 << 20, None) == mt.MT_EINVAL
+    assert L.mt_op_gemm_ws(*base, None, 1 << 20, None) == mt.MT_EINVAL
+    assert L.mt_op_gemm_ws(*base, good, -1, None) == mt.MT_EINVAL
+    assert mt.gemm_ws_bytes() >= 16 * 15 * 256 * 256 * 4
+
+
 def test_rmsnorm_bwd_rejects_misaligned_operands():
     # host-side argument checks run before any device call (addresses only)
     L = mt.lib()

@@ -49,7 +49,7 @@ def fp32_close(gpu, ref, absterm, ulps=64):
 
 # -------------------------------------------------------------------- GEMM ---
 
-def _gemm_case(dtype, layout, M, N, K, residual=False, sample=None, variant=0):
+def _gemm_case(dtype, layout, M, N, K, residual=False, sample=None, variant=0, ws=None, alias=False):
     # logical operands: X [M, K], Y [K, N]; stored per layout
     X = RNG.standard_normal((M, K)).astype(np.float32)
     Y = RNG.standard_normal((K, N)).astype(np.float32)
@@ -65,8 +65,19 @@ def _gemm_case(dtype, layout, M, N, K, residual=False, sample=None, variant=0):
     R = RNG.standard_normal((M, N)).astype(np.float32) if residual else None
     C = torch.full((M, N), float("nan"), device=DEV)
     Rd = dev(R) if residual else None
-    mt.gemm(dtype, layout, A, lda, B, ldb, C, N, M, N, K, R=Rd, ldr=N, variant=variant)
+    if alias:   # C = C + A B: the residual is the output itself
+        C.copy_(Rd)
+        Rd = C
+    if ws is None:
+        mt.gemm(dtype, layout, A, lda, B, ldb, C, N, M, N, K, R=Rd, ldr=N, variant=variant)
+    else:
+        mt.gemm_ws(dtype, layout, A, lda, B, ldb, C, N, M, N, K, ws, ws.numel() * 4, R=Rd, ldr=N)
     got = host(C)
+    if ws is not None and not alias:
+        # fixed-order sums: a second call gives the same bits
+        C2 = torch.full((M, N), float("nan"), device=DEV)
+        mt.gemm_ws(dtype, layout, A, lda, B, ldb, C2, N, M, N, K, ws, ws.numel() * 4, R=Rd, ldr=N)
+        np.testing.assert_array_equal(host(C2), got)
     X64, Y64 = X.astype(np.float64), Y.astype(np.float64)
     if sample is None:
         ref = X64 @ Y64 + (R if residual else 0)
@@ -75,8 +86,8 @@ def _gemm_case(dtype, layout, M, N, K, residual=False, sample=None, variant=0):
     else:
         ii = RNG.integers(0, M, sample)
         jj = RNG.integers(0, N, sample)
-        ref = np.einsum("sk,ks->s", X64[ii], Y64[:, jj])
-        absterm = np.einsum("sk,ks->s", np.abs(X64[ii]), np.abs(Y64[:, jj]))
+        ref = np.einsum("sk,ks->s", X64[ii], Y64[:, jj]) + (R[ii, jj] if residual else 0)
+        absterm = np.einsum("sk,ks->s", np.abs(X64[ii]), np.abs(Y64[:, jj])) + (np.abs(R[ii, jj]) if residual else 0)
         fp32_close(got[ii, jj], ref, absterm)
 
 
@@ -100,6 +111,32 @@ def test_gemm_tile_variants(variant, dtype, layout, M, N, K):
                                           (mt.MT_GEMM_TN, 27648, 5120, 4096)])
 def test_gemm_full_14b_shapes_sampled(layout, M, N, K):
     _gemm_case(mt.MT_BF16, layout, M, N, K, sample=512)
+
+
+@pytest.fixture(scope="module")
+def gemm_ws_buf():
+    return torch.empty(mt.gemm_ws_bytes() // 4, dtype=torch.float32, device=DEV)
+
+
+# With a workspace, a grid of at most half a wave of 256x256 tiles (16 here)
+# and the tiles of a part-filled last wave (64 of 320) are split along K; the
+# ragged case puts a K tail in the last block of each split tile.
+@pytest.mark.parametrize("dtype", [mt.MT_FP32, mt.MT_BF16])
+@pytest.mark.parametrize("layout", [mt.MT_GEMM_NT, mt.MT_GEMM_NN, mt.MT_GEMM_TN])
+@pytest.mark.parametrize("M,N,K", [(1024, 1024, 4096), (1000, 904, 3000)])
+def test_gemm_split_k(gemm_ws_buf, dtype, layout, M, N, K):
+    _gemm_case(dtype, layout, M, N, K, residual=True, ws=gemm_ws_buf)
+
+
+@pytest.mark.parametrize("layout", [mt.MT_GEMM_NT, mt.MT_GEMM_NN, mt.MT_GEMM_TN])
+def test_gemm_split_k_accumulates_into_output(gemm_ws_buf, layout):
+    _gemm_case(mt.MT_BF16, layout, 1000, 904, 3000, residual=True, ws=gemm_ws_buf, alias=True)
+
+
+@pytest.mark.parametrize("layout,M,N,K", [(mt.MT_GEMM_NT, 4096, 5120, 5120), (mt.MT_GEMM_NN, 4096, 5120, 13824),
+                                          (mt.MT_GEMM_TN, 5120, 5120, 4096), (mt.MT_GEMM_TN, 2048, 2048, 16384)])
+def test_gemm_split_k_full_shapes_sampled(gemm_ws_buf, layout, M, N, K):
+    _gemm_case(mt.MT_BF16, layout, M, N, K, residual=True, sample=4096, ws=gemm_ws_buf)
 
 
 def test_gemm_k_zero_gives_residual():
