@@ -77,6 +77,56 @@ def recorded_traffic(kernel_class):
     return None
 
 
+def link_probe(mib=1024, reps=3):
+    """Plain pinned-host <-> device copies of `mib` MiB, each direction alone
+    (HIP events on a side stream): the host link's per-direction rate on this
+    box, the bandwidth the step's link bound is priced at."""
+    import torch
+    n = mib << 18   # fp32 elements
+    dev = torch.empty(n, device="cuda")
+    host = torch.empty(n, pin_memory=True)
+    s = torch.cuda.Stream()
+    out = {}
+    for name, dst, src in (("h2d", dev, host), ("d2h", host, dev)):
+        best = 0.0
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(s):
+                e0.record(s)
+                dst.copy_(src, non_blocking=True)
+                e1.record(s)
+            e1.synchronize()
+            best = max(best, n * 4 / (e0.elapsed_time(e1) * 1e-3))
+        out[name] = best
+    del dev, host
+    torch.cuda.synchronize()
+    return out
+
+
+def link_roofline(w, stats, step_s, bw, wbytes):
+    """The step's host-link bound from the bytes the step moves in each phase.
+    Forward phase: every unit image in, plus x0 and the targets. Backward
+    phase: L-1 layer images in (layer L-1 is still resident at the turn)
+    against every gradient, x0's gradient and the losses out. Phase-aware:
+    the phases run one after the other (no gradient exists before the turn);
+    duplex: both directions busy the whole step."""
+    d, L, M = w.d_model, w.n_layers, w.batch * w.seq
+    qkv = (w.n_heads + 2 * w.n_kv_heads) * w.head_dim
+    layer_img = 2 * d * 4 + (qkv * d + d * w.n_heads * w.head_dim + 3 * d * w.ffn_dim) * wbytes
+    h2d, d2h = stats["h2d_bytes"], stats["d2h_bytes"]
+    b_in = (L - 1) * layer_img
+    f = h2d - b_in
+    t_phase = f / bw["h2d"] + max(b_in / bw["h2d"], d2h / bw["d2h"])
+    t_dup = max(h2d / bw["h2d"], d2h / bw["d2h"])
+    return {
+        "bw_h2d_GBps": round(bw["h2d"] / 1e9, 2), "bw_d2h_GBps": round(bw["d2h"] / 1e9, 2),
+        "fwd_h2d_bytes": f, "bwd_h2d_bytes": b_in, "d2h_bytes": d2h,
+        "t_link_phase_s": round(t_phase, 4), "t_link_duplex_s": round(t_dup, 4),
+        "tokens_s_phase": round(M / t_phase, 1),
+        "frac_phase": round(t_phase / step_s, 4), "frac_duplex": round(t_dup / step_s, 4),
+    }
+
+
 def cpu_baseline(w, budget_tokens=512):
     """The CPU oracle (plain float64 NumPy) timed on a bounded sample of the
     same workload: one decoder layer of the real shape and the real head on
@@ -152,6 +202,8 @@ def main():
     ap.add_argument("--sync-opt", action="store_true",
                     help="every AdamW update lands before its step returns (default: updates may finish "
                          "during the next step's forward, in the order it loads the units)")
+    ap.add_argument("--no-link-probe", action="store_true",
+                    help="skip the plain pinned-copy measurement of the host link after the run")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="after the run, one plain device copy of this many MiB (a known-size reference "
                          "dispatch for hardware byte counters)")
@@ -283,6 +335,13 @@ def main():
         "cpu_baseline": None,
     }
     ctx.close()
+    if not args.no_link_probe:
+        bw = link_probe()
+        log(f"link probe: H2D {bw['h2d'] / 1e9:.1f} GB/s, D2H {bw['d2h'] / 1e9:.1f} GB/s")
+        if not args.resident and not layout["ckpt_host"]:
+            out["link_roofline"] = link_roofline(w, stats[-1], ms * 1e-3, bw, 2 if dtype == mt.MT_BF16 else 4)
+        else:
+            out["link_roofline"] = {"bw_h2d_GBps": round(bw["h2d"] / 1e9, 2), "bw_d2h_GBps": round(bw["d2h"] / 1e9, 2)}
     if args.copy_probe:
         n = args.copy_probe << 18   # fp32 elements
         src = torch.ones(n, device="cuda")
