@@ -34,10 +34,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_context(w, dtype, seed, flags, host_threads=0, chunk_rows=0, ckpt_host=0, resident=False):
+def build_context(w, dtype, seed, flags, host_threads=0, chunk_rows=0, ckpt_host=0, buffers=2):
     from host_memory_streamed_amd import mt, synth
     cfg = mt.make_config(w.n_layers, w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn_dim, w.vocab,
-                         w.batch, w.seq, dtype=dtype, n_layer_buffers=(w.n_layers + 1 if resident else 2),
+                         w.batch, w.seq, dtype=dtype, n_layer_buffers=buffers,
                          host_threads=host_threads,
                          flags=flags, chunk_rows=chunk_rows, ckpt_host=ckpt_host)
     t0 = time.perf_counter()
@@ -197,8 +197,11 @@ def main():
     ap.add_argument("--chunk-rows", type=int, default=0, help="token rows per projection/MLP chunk (0 = auto)")
     ap.add_argument("--ckpt-host", type=int, default=0, help="checkpoints parked in host memory (0 = auto)")
     ap.add_argument("--resident", action="store_true",
-                    help="keep every layer in device memory (one buffer per unit) instead of streaming "
-                         "through two buffers")
+                    help="device cache of every unit (one buffer per layer and the head) instead of streaming "
+                         "through two buffers: same as --layer-buffers n_layers+1")
+    ap.add_argument("--layer-buffers", type=int, default=2,
+                    help="device layer buffers: 2 streams every unit; k > 2 keeps the head and the top k-3 "
+                         "layers in a device cache, refreshed with each update as it lands")
     ap.add_argument("--sync-opt", action="store_true",
                     help="every AdamW update lands before its step returns (default: updates may finish "
                          "during the next step's forward, in the order it loads the units)")
@@ -225,8 +228,9 @@ def main():
         w = mt.Workload(**{**w.__dict__, "n_layers": args.layers})
     dtype = mt.MT_BF16 if args.dtype == "bf16" else mt.MT_FP32
     flags = mt.MT_KERNEL_TIMING | mt.MT_TRACE | (0 if args.sync_opt else mt.MT_OVERLAP_OPT)
+    buffers = w.n_layers + 1 if args.resident else min(max(2, args.layer_buffers), w.n_layers + 1)
     ctx = build_context(w, dtype, args.seed, flags, chunk_rows=args.chunk_rows, ckpt_host=args.ckpt_host,
-                        resident=args.resident)
+                        buffers=buffers)
     layout = ctx.layout_info()
     tokens, targets = synth.token_batch(args.seed, w.batch, w.seq, w.vocab)
     M = w.batch * w.seq
@@ -267,7 +271,7 @@ def main():
     mfu = mean("model_flops") / (ms * 1e-3) / peak
     h2d, d2h = mean("h2d_bytes"), mean("d2h_bytes")
     # copy engine rates over the last step's copies
-    loads = [e for e in sched if e["phase"] == "load" and e["stream"] == 0]
+    loads = [e for e in sched if e["phase"] in ("load", "refresh") and e["stream"] == 0]
     grads = [e for e in sched if e["phase"] == "grad" and e["stream"] == 2]
     h2d_busy = sum(e["t1"] - e["t0"] for e in loads) * 1e-3
     d2h_busy = sum(e["t1"] - e["t0"] for e in grads) * 1e-3
@@ -294,8 +298,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if dtype == mt.MT_BF16 else "fp32",
         "data": "synthetic",
-        "config": {"workload": w.name + "-shaped decoder, " + ("every layer resident in device memory"
-                                                                if args.resident else "streamed through 2 layer buffers"),
+        "config": {"workload": w.name + "-shaped decoder, " + (
+                       "streamed through 2 layer buffers" if buffers == 2 else
+                       "every unit in a device cache refreshed by each update" if buffers == w.n_layers + 1 else
+                       f"head and top {buffers - 3} layers in a device cache, the rest streamed through 2 buffers"),
+                   "layer_buffers": buffers,
                    "n_layers": w.n_layers, "d_model": w.d_model, "n_heads": w.n_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ffn_dim": w.ffn_dim,
                    "vocab": w.vocab, "global_batch": w.batch, "seq_len": w.seq,
@@ -338,10 +345,14 @@ def main():
     if not args.no_link_probe:
         bw = link_probe()
         log(f"link probe: H2D {bw['h2d'] / 1e9:.1f} GB/s, D2H {bw['d2h'] / 1e9:.1f} GB/s")
-        if not args.resident and not layout["ckpt_host"]:
+        if buffers == 2 and not layout["ckpt_host"]:
             out["link_roofline"] = link_roofline(w, stats[-1], ms * 1e-3, bw, 2 if dtype == mt.MT_BF16 else 4)
         else:
-            out["link_roofline"] = {"bw_h2d_GBps": round(bw["h2d"] / 1e9, 2), "bw_d2h_GBps": round(bw["d2h"] / 1e9, 2)}
+            # a device cache moves its refreshes into the backward: only the
+            # duplex bound applies
+            t_dup = max(h2d / bw["h2d"], d2h / bw["d2h"])
+            out["link_roofline"] = {"bw_h2d_GBps": round(bw["h2d"] / 1e9, 2), "bw_d2h_GBps": round(bw["d2h"] / 1e9, 2),
+                                    "t_link_duplex_s": round(t_dup, 4), "frac_duplex": round(t_dup / (ms * 1e-3), 4)}
     if args.copy_probe:
         n = args.copy_probe << 18   # fp32 elements
         src = torch.ones(n, device="cuda")

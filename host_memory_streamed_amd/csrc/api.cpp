@@ -119,8 +119,7 @@ static int validate(const mt_model_cfg* c, std::string& why) {
   if (c->ffn_dim < 1 || c->vocab < 2) return bad("ffn_dim and vocab must be positive");
   if (c->max_batch < 1 || c->max_seq < 1) return bad("max_batch and max_seq must be >= 1");
   if ((int64_t)c->max_batch * c->max_seq > (1LL << 31) - 1) return bad("max_batch * max_seq too large");
-  if (c->n_layer_buffers != 2 && c->n_layer_buffers < c->n_layers + 1)
-    return bad("n_layer_buffers must be 2 (streamed) or >= n_layers + 1 (resident)");
+  if (c->n_layer_buffers < 2) return bad("n_layer_buffers must be >= 2");
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f) || !(c->lr >= 0.0) || !(c->beta1 >= 0.0 && c->beta1 < 1.0) ||
       !(c->beta2 >= 0.0 && c->beta2 < 1.0) || !(c->adam_eps >= 0.0))
     return bad("invalid eps / rope_base / AdamW hyperparameters");
@@ -225,8 +224,13 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
   c.cfg = *cfg;
   c.D = make_dims(*cfg);
   c.dtype = cfg->compute_dtype;
-  c.resident = cfg->n_layer_buffers != 2;
-  c.nbuf = c.resident ? c.D.L + 1 : 2;
+  if (cfg->n_layer_buffers >= c.D.L + 1) {
+    c.nbuf = c.ncache = c.D.L + 1;
+  } else {
+    c.nbuf = cfg->n_layer_buffers;
+    c.ncache = c.nbuf - 2;
+  }
+  c.dev_current.assign(c.D.L + 1, 0);
   c.M_max = (int64_t)cfg->max_batch * cfg->max_seq;
   c.tensors = tensor_table(c.D);
   c.pool = new Pool(default_threads(cfg->host_threads));
@@ -314,9 +318,15 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
     return true;
   };
   bool ok = true;
-  const size_t img = std::max(c.units[0].lay.image_bytes(S), c.units[D.L].lay.image_bytes(S));
+  // streaming buffers fit any unit that streams through them; a cached
+  // unit's buffer fits that unit
+  std::vector<size_t> bsize(c.nbuf, 0);
+  for (int u = 0; u <= D.L; ++u) {
+    const int b = c.buf_of(u);
+    bsize[b] = std::max(bsize[b], c.units[u].lay.image_bytes(S));
+  }
   c.buf.resize(c.nbuf);
-  for (int i = 0; i < c.nbuf; ++i) ok &= dalloc(img, &c.buf[i]);
+  for (int i = 0; i < c.nbuf; ++i) ok &= dalloc(bsize[i], &c.buf[i]);
   ok &= dalloc((size_t)max_unit * 4, (void**)&c.gbuf[0]);
   ok &= dalloc((size_t)max_unit * 4, (void**)&c.gbuf[1]);
   Workspace& w = c.ws;
@@ -447,6 +457,7 @@ int mt_set_param(mt_ctx* h, int32_t id, const float* src) {
   if (id < 0 || id >= (int32_t)c.tensors.size() || !src) return set_error(&c, MT_EINVAL, "bad tensor id or NULL source");
   const TensorRef& r = c.tensors[id];
   Unit& u = r.unit < 0 ? c.emb() : c.units[r.unit];
+  if (r.unit >= 0) c.dev_current[r.unit] = 0;
   const int64_t ch = 1 << 20, n = r.numel;
   c.pool->run((n + ch - 1) / ch, [&](int64_t i) {
     const int64_t a = i * ch, b = std::min(n, a + ch);
@@ -546,7 +557,7 @@ int mt_trace_dump(mt_ctx* h, const char* path) {
   if (!h || !path) return MT_EINVAL;
   FILE* f = fopen(path, "w");
   if (!f) return set_error(&h->c, MT_EINVAL, std::string("cannot open ") + path);
-  static const char* ph[] = {"load", "fwd", "head", "bwd", "grad", "adamw", "ckpt out", "ckpt in"};
+  static const char* ph[] = {"load", "fwd", "head", "bwd", "grad", "adamw", "ckpt out", "ckpt in", "refresh"};
   static const char* st[] = {"copy-in", "compute", "copy-out", "host AdamW"};
   fprintf(f, "{\"traceEvents\":[\n");
   bool first = true;
@@ -559,7 +570,7 @@ int mt_trace_dump(mt_ctx* h, const char* path) {
     char unit[32];
     if (e.unit == MT_UNIT_HEAD) snprintf(unit, sizeof unit, "head");
     else if (e.unit == MT_UNIT_EMB) snprintf(unit, sizeof unit, "embedding");
-    else if (e.phase >= MT_PH_CKPT_OUT) snprintf(unit, sizeof unit, "x_%d", e.unit);
+    else if (e.phase == MT_PH_CKPT_OUT || e.phase == MT_PH_CKPT_IN) snprintf(unit, sizeof unit, "x_%d", e.unit);
     else snprintf(unit, sizeof unit, "layer %d", e.unit);
     fprintf(f, ",\n{\"name\":\"%s %s\",\"ph\":\"X\",\"pid\":0,\"tid\":%d,\"ts\":%.3f,\"dur\":%.3f,\"args\":{\"buffer\":%d}}",
             ph[e.phase], unit, e.stream, e.t0_ms * 1000.0, (e.t1_ms - e.t0_ms) * 1000.0, e.buffer);

@@ -165,8 +165,20 @@ struct Ctx {
   mt_model_cfg cfg;
   Dims D;
   int dtype;                 // 0 fp32, 1 bf16
+  // Layer buffers. Units with a buffer of their own (the device cache) are
+  // the head and the layers above L - ncache, i.e. u >= L + 1 - ncache; the
+  // other layers stream through buffers 0 and 1 (layer l in l % 2).
+  // ncache == L + 1: every unit has its own buffer (unit u in buffer u).
   int nbuf;
-  bool resident;
+  int ncache;
+  bool cached(int unit) const { return unit >= D.L + 1 - ncache; }
+  int buf_of(int unit) const {
+    if (ncache == D.L + 1) return unit;
+    return cached(unit) ? 2 + (D.L - unit) : unit % 2;
+  }
+  // per unit (layers, head): its buffer holds the unit's current image
+  // (cached units only; cleared when an update or mt_set_param changes it)
+  std::vector<char> dev_current;
   int64_t M_max;
   std::string err;
 

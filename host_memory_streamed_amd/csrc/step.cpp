@@ -14,10 +14,19 @@
 // layer template's kernels), copy-out (gradients and per-token losses device
 // -> host). Compute order: forward of layers 0..L-1, the head (final norm, LM
 // head, loss and its backward), then recompute + backward of layers L-1..0.
-// Layer l always lives in buffer l % 2 (the head in L % 2), so layer L-1 is
-// still resident when the backward starts and is not fetched again. A load
+// Streamed: layer l lives in buffer l % 2 (the head in L % 2), so layer L-1
+// is still resident when the backward starts and is not fetched again. A load
 // into a buffer waits for the compute that last used it; a gradient item
 // waits for the copy-out of the item two before it (two gradient buffers).
+//
+// Device cache (more than two buffers): "MegaTrain fits 120B LLM training on
+// one GPU using CPU RAM", section "Bottom line", and the technical brief's
+// "Implementing Host Memory Offloading for Persistent Model State" describe
+// device memory as a cache in front of the host store. The head and the top
+// layers then keep a buffer each: they are not fetched for their backward,
+// and once a unit's AdamW has landed its new image goes into its buffer on
+// the copy-in stream (idle in the backward when nothing streams), so the next
+// forward does not fetch it. Results are identical to the streamed schedule.
 // A host dispatcher loop submits copies only once the compute they depend on
 // has completed, enqueues compute with device-side waits on the copies, and
 // hands each unit's AdamW to the worker pool as its gradients land; the step
@@ -45,17 +54,24 @@ struct Item {
   int grad_k;     // -1, or the index among gradient-producing items
 };
 
+// The step's compute items in order, with their buffers and loads. A
+// streamed unit is loaded for its forward, and again for its backward unless
+// its buffer's last user was its own forward (layer L-1 at the turn, or the
+// last streamed layers below a device cache). A cached unit is loaded for its
+// forward only if its buffer does not hold its current image, and never for
+// its backward.
 std::vector<Item> build_items(const Ctx& c) {
   const int L = c.D.L;
   std::vector<Item> it;
-  auto bufof = [&](int unit) { return c.resident ? unit : unit % 2; };
-  for (int l = 0; l < L; ++l) it.push_back({PH_FWD, l, bufof(l), true, -1, -1});
-  it.push_back({PH_HEAD, L, bufof(L), true, -1, 0});
-  for (int l = L - 1; l >= 0; --l)
-    it.push_back({PH_BWD, l, bufof(l), !c.resident && l != L - 1, -1, L - l});
+  auto fwd_load = [&](int unit) { return !c.cached(unit) || !c.dev_current[unit]; };
+  for (int l = 0; l < L; ++l) it.push_back({PH_FWD, l, c.buf_of(l), fwd_load(l), -1, -1});
+  it.push_back({PH_HEAD, L, c.buf_of(L), fwd_load(L), -1, 0});
+  for (int l = L - 1; l >= 0; --l) it.push_back({PH_BWD, l, c.buf_of(l), false, -1, L - l});
   for (size_t i = 0; i < it.size(); ++i)
     for (int j = (int)i - 1; j >= 0; --j)
       if (it[j].buf == it[i].buf) { it[i].prev_user = j; break; }
+  for (auto& x : it)
+    if (x.phase == PH_BWD && !c.cached(x.unit)) x.load = x.prev_user < 0 || it[x.prev_user].unit != x.unit;
   return it;
 }
 
@@ -71,6 +87,8 @@ struct StepEvents {
   hipEvent_t x0 = nullptr, loss = nullptr, dx0 = nullptr, start = nullptr;
   std::vector<hipEvent_t> trace;   // timing events: per item 6 (load, compute, copy-out)
   std::vector<hipEvent_t> ck_trace;   // per checkpoint index 4 (out, in)
+  std::vector<hipEvent_t> refreshed;  // per gradient item: its unit's cache refresh
+  std::vector<hipEvent_t> rf_trace;   // per gradient item 2
 };
 
 int create_step_events(Ctx& c, StepEvents*& out);
@@ -90,6 +108,8 @@ int create_step_events(Ctx& c, StepEvents*& out) {
   e->drained.resize(c.D.L + 1);
   e->ck_saved.resize(c.D.L + 1);
   e->ck_loaded.resize(c.D.L + 1);
+  e->refreshed.resize(c.D.L + 1);
+  for (auto& ev : e->refreshed) ok &= mk(ev, sync);
   for (auto& ev : e->loaded) ok &= mk(ev, sync);
   for (auto& ev : e->freed) ok &= mk(ev, sync);
   for (auto& ev : e->drained) ok &= mk(ev, host);
@@ -104,6 +124,8 @@ int create_step_events(Ctx& c, StepEvents*& out) {
     for (auto& ev : e->trace) ok &= mk(ev, hipEventDefault);
     e->ck_trace.resize((size_t)(c.D.L + 1) * 4);
     for (auto& ev : e->ck_trace) ok &= mk(ev, hipEventDefault);
+    e->rf_trace.resize((size_t)(c.D.L + 1) * 2);
+    for (auto& ev : e->rf_trace) ok &= mk(ev, hipEventDefault);
   }
   out = e;
   if (!ok) return set_error(&c, MT_EHIP, "hipEventCreate failed");
@@ -112,7 +134,8 @@ int create_step_events(Ctx& c, StepEvents*& out) {
 
 void destroy_step_events(StepEvents* e) {
   if (!e) return;
-  for (auto* v : {&e->loaded, &e->freed, &e->drained, &e->trace, &e->ck_saved, &e->ck_loaded, &e->ck_trace})
+  for (auto* v : {&e->loaded, &e->freed, &e->drained, &e->trace, &e->ck_saved, &e->ck_loaded, &e->ck_trace,
+                 &e->refreshed, &e->rf_trace})
     for (auto ev : *v)
       if (ev) hipEventDestroy(ev);
   for (auto ev : {e->x0, e->loss, e->dx0, e->start})
@@ -359,6 +382,26 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
     HIPCK(hipEventRecord(E.loaded[j], c.s_in));
     load_issued[j] = 1;
     h2d_bytes += (double)bytes;
+    if (c.cached(it.unit)) c.dev_current[it.unit] = 1;
+    return MT_OK;
+  };
+  // device cache: the updated image of gradient item kk's unit into its own
+  // buffer, for the next step
+  std::vector<char> rf_issued(L + 1, 0);
+  int rf_last = -1;   // the refresh in flight (one at a time, so a load that
+                      // becomes ready waits behind at most one)
+  auto issue_refresh = [&](int kk) -> int {
+    const int ui = grad_uidx(kk);
+    const Unit& u = c.units[ui];
+    const size_t bytes = u.lay.image_bytes(c.dtype);
+    if (trace) HIPCK(hipEventRecord(E.rf_trace[(size_t)kk * 2], c.s_in));
+    HIPCK(hipMemcpyAsync(c.buf[c.buf_of(ui)], u.image(), bytes, hipMemcpyHostToDevice, c.s_in));
+    if (trace) HIPCK(hipEventRecord(E.rf_trace[(size_t)kk * 2 + 1], c.s_in));
+    HIPCK(hipEventRecord(E.refreshed[kk], c.s_in));
+    rf_issued[kk] = 1;
+    rf_last = kk;
+    h2d_bytes += (double)bytes;
+    c.dev_current[ui] = 1;
     return MT_OK;
   };
   auto issue_compute = [&](int i) -> int {
@@ -523,6 +566,7 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
       const int kk = next_a, ui = grad_uidx(kk);
       if (!abort) {
         adam_start_ms[ui] = last_land_ms;
+        c.dev_current[ui] = 0;
         submit_adamw(c, ui, grad_dest(kk), {{0, c.units[ui].lay.n}}, k, keep ? -1 : slot_of[kk],
                      adam_priority(ui));
       } else if (!keep) {
@@ -532,6 +576,19 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
       progress = true;
     }
     if (rc) break;
+    // cached units whose update has landed: refresh their buffers, in any
+    // order, after every load that could be issued
+    const int rf_free = c.ncache && !abort ? (rf_last < 0 ? 1 : event_done(E.refreshed[rf_last])) : 0;
+    if (rf_free < 0) { rc = rf_free; break; }
+    if (rf_free) {
+      for (int kk = 0; kk < next_a; ++kk) {
+        if (rf_issued[kk] || !c.cached(grad_uidx(kk)) || !unit_idle(grad_uidx(kk))) continue;
+        if ((rc = issue_refresh(kk))) break;
+        progress = true;
+        break;
+      }
+      if (rc) break;
+    }
     // the input gradient of layer 0 goes to the host for the embedding scatter
     if (!dx0_issued && next_g > L) {
       if ((rc = issue_dx0())) break;
@@ -551,6 +608,7 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
     hipStreamSynchronize(c.s_comp);
     hipStreamSynchronize(c.s_out);
     adam_drain(c);
+    std::fill(c.dev_current.begin(), c.dev_current.end(), 0);
     {
       std::lock_guard<std::mutex> lk(c.amu);
       std::fill(c.slot_busy.begin(), c.slot_busy.end(), 0);
@@ -588,9 +646,11 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
   if (!overlap) adam_drain(c);
   const hipError_t s1 = hipStreamSynchronize(c.s_in), s2 = hipStreamSynchronize(c.s_comp),
                    s3 = hipStreamSynchronize(c.s_out);
-  if (s1 != hipSuccess || s2 != hipSuccess || s3 != hipSuccess)
+  if (s1 != hipSuccess || s2 != hipSuccess || s3 != hipSuccess) {
+    std::fill(c.dev_current.begin(), c.dev_current.end(), 0);
     return set_error(&c, MT_EHIP, std::string("stream synchronize: ") +
                                       hipGetErrorString(s1 != hipSuccess ? s1 : s2 != hipSuccess ? s2 : s3));
+  }
 
   const double step_ms = ms_since(t_begin);
   const double loss = loss_sum / (double)M;
@@ -637,6 +697,13 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
         c.sched.push_back({MT_PH_GRAD, unit, it.grad_k % 2, 2, a2, b2});
         st.d2h_busy_ms += b2 - a2;
       }
+    }
+    for (int kk = 0; kk <= L; ++kk) {
+      if (!rf_issued[kk]) continue;
+      const double a = rel(E.rf_trace[(size_t)kk * 2]), b = rel(E.rf_trace[(size_t)kk * 2 + 1]);
+      const int ui = grad_uidx(kk);
+      c.sched.push_back({MT_PH_REFRESH, ui == L ? MT_UNIT_HEAD : ui, c.buf_of(ui), 0, a, b});
+      st.h2d_busy_ms += b - a;
     }
     for (int i = 1; i <= kpark; ++i) {
       const double a = rel(ck_ev(i, 0)), b = rel(ck_ev(i, 1));

@@ -81,7 +81,15 @@ typedef struct mt_model_cfg {
   int32_t max_batch;    /* largest B accepted by mt_train_step */
   int32_t max_seq;      /* largest T accepted by mt_train_step */
   int32_t compute_dtype;     /* MT_FP32 or MT_BF16 */
-  int32_t n_layer_buffers;   /* 2 = streamed; >= n_layers + 1 = every layer resident */
+  /* Device layer buffers. 2 = every unit (layer or head) streams through two
+   * buffers. k in [3, n_layers]: a device cache -- the head and the top k - 3
+   * layers keep a buffer each, the other layers stream through two. k >=
+   * n_layers + 1: every unit keeps a buffer of its own. A unit with its own
+   * buffer is not fetched again for its backward, and its updated image is
+   * copied into that buffer as soon as its AdamW has landed (during the
+   * backward, or in the next step's forward), so the next forward does not
+   * fetch it either. Results do not depend on k. */
+  int32_t n_layer_buffers;
   int32_t host_threads;      /* AdamW / gather pool size; 0 = online CPUs (at most 64) */
   uint32_t flags;            /* MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE | MT_OVERLAP_OPT */
   float rms_eps;
@@ -199,6 +207,7 @@ int mt_kernel_stats(mt_ctx* ctx, mt_kernel_stat* out, int32_t cap, int32_t* n);
 #define MT_PH_ADAMW 5     /* host AdamW of a unit (stream 3 = host) */
 #define MT_PH_CKPT_OUT 6  /* D2H of a parked residual checkpoint (stream 2; unit = its index) */
 #define MT_PH_CKPT_IN 7   /* H2D of a parked residual checkpoint (stream 0; unit = its index) */
+#define MT_PH_REFRESH 8   /* H2D of a cached unit's updated image into its own buffer (stream 0) */
 #define MT_UNIT_EMB -1
 #define MT_UNIT_HEAD -2
 typedef struct mt_sched_entry {

@@ -33,9 +33,11 @@ def init_params(cfg, seed, std=0.02):
 
 
 def make_ctx(cfg, B, T, params, dtype=mt.MT_FP32, resident=False, flags=mt.MT_KEEP_GRADS, threads=8,
-             chunk_rows=0, ckpt_host=0):
+             chunk_rows=0, ckpt_host=0, buffers=None):
+    if buffers is None:
+        buffers = cfg.n_layers + 1 if resident else 2
     c = mt.make_config(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn_dim,
-                       cfg.vocab, B, T, dtype=dtype, n_layer_buffers=(cfg.n_layers + 1 if resident else 2),
+                       cfg.vocab, B, T, dtype=dtype, n_layer_buffers=buffers,
                        host_threads=threads, flags=flags, rms_eps=cfg.rms_eps, rope_base=cfg.rope_base,
                        lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, adam_eps=cfg.adam_eps,
                        weight_decay=cfg.weight_decay, chunk_rows=chunk_rows, ckpt_host=ckpt_host)
@@ -294,24 +296,120 @@ def test_overlapped_optimizer_is_bitwise_synchronous(dtype, keep):
         assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("dtype", [mt.MT_FP32, mt.MT_BF16])
-def test_streamed_equals_resident_bitwise(dtype):
-    cfg = O.Config(5, 128, 2, 1, 64, 200, 300)
+def _run_cached_steps(ctx, n, seed, B, T, vocab, n_params, between=None):
+    losses, tls = [], []
+    for s in range(n):
+        if between:
+            between(ctx, s)
+        tok, tgt = synth.token_batch(seed + s, B, T, vocab)
+        losses.append(ctx.train_step(tok, tgt))
+        tls.append(ctx.token_losses().copy())
+    ctx.sync()
+    state = [ctx.params(i).copy() for i in range(n_params)]
+    state += [ctx.opt_state(i)[0].copy() for i in range(n_params)] + [ctx.opt_state(i)[1].copy() for i in range(n_params)]
+    if ctx.cfg.flags & mt.MT_KEEP_GRADS:
+        state += [ctx.grads(i).copy() for i in range(n_params)]
+    return losses, tls, state
+
+
+# A device cache (more than two layer buffers) changes only where the weights
+# wait between uses: every loss and the whole host state after four steps
+# equal the streamed schedule's bit for bit. 6 layers: 3 buffers cache the
+# head, 4 the head and layer 5, 7 every unit.
+@pytest.mark.parametrize("dtype,buffers,flags", [
+    (mt.MT_FP32, 7, mt.MT_KEEP_GRADS),
+    (mt.MT_BF16, 7, mt.MT_KEEP_GRADS),
+    (mt.MT_FP32, 3, mt.MT_OVERLAP_OPT),
+    (mt.MT_BF16, 4, mt.MT_KEEP_GRADS | mt.MT_OVERLAP_OPT),
+    (mt.MT_BF16, 7, mt.MT_OVERLAP_OPT),
+])
+def test_streamed_equals_device_cache_bitwise(dtype, buffers, flags):
+    cfg = O.Config(6, 128, 2, 1, 64, 200, 300)
     params = init_params(cfg, 21, 0.1)
     out = []
-    for resident in (False, True):
-        with make_ctx(cfg, 2, 64, params, dtype=dtype, resident=resident) as ctx:
-            losses = []
-            for s in range(3):
-                tok, tgt = synth.token_batch(21 + s, 2, 64, cfg.vocab)
-                losses.append(ctx.train_step(tok, tgt))
-            out.append((losses, [ctx.params(i) for i in range(len(params))], ctx.token_losses(),
-                        [ctx.grads(i) for i in range(len(params))]))
-    (l0, p0, t0, g0), (l1, p1, t1, g1) = out
+    for nb in (2, buffers):
+        with make_ctx(cfg, 2, 64, params, dtype=dtype, buffers=nb, flags=flags) as ctx:
+            out.append(_run_cached_steps(ctx, 4, 21, 2, 64, cfg.vocab, len(params)))
+    (l0, t0, s0), (l1, t1, s1) = out
     assert l0 == l1
-    np.testing.assert_array_equal(t0, t1)
-    for a, b in zip(p0 + g0, p1 + g1):
+    for a, b in zip(t0 + s0, t1 + s1):
         np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", [mt.MT_FP32, mt.MT_BF16])
+def test_set_param_reaches_cached_units(dtype):
+    """mt_set_param between steps changes a cached unit's host image; its
+    stale device copy must not be used by the next forward."""
+    cfg = O.Config(4, 128, 2, 1, 64, 200, 300)
+    params = init_params(cfg, 5, 0.1)
+    names = [n for n, _, _ in O.tensor_table(cfg)]
+    ids = [names.index("layers.3.wq"), names.index("layers.0.w_down"), names.index("lm_head")]
+    rng = np.random.default_rng(5)
+    fresh = {i: (0.05 * rng.standard_normal(params[i].shape)).astype(np.float32) for i in ids}
+
+    def between(ctx, s):
+        if s == 2:
+            for i in ids:
+                ctx.set_param(i, fresh[i])
+
+    out = []
+    for nb in (2, cfg.n_layers + 1):
+        with make_ctx(cfg, 2, 48, params, dtype=dtype, buffers=nb, flags=mt.MT_OVERLAP_OPT) as ctx:
+            out.append(_run_cached_steps(ctx, 4, 5, 2, 48, cfg.vocab, len(params), between))
+    (l0, t0, s0), (l1, t1, s1) = out
+    assert l0 == l1
+    for a, b in zip(t0 + s0, t1 + s1):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_device_cache_schedule():
+    """Every unit cached: the first step fetches each unit once, for its
+    forward; each unit's updated image is copied in after its gradients have
+    left and its AdamW has landed; the next step fetches only the units not
+    refreshed that way. Two of four buffers cached: the streamed layers still
+    held by their buffers at the turn are not fetched again."""
+    cfg = O.Config(6, 256, 4, 4, 64, 512, 512)
+    L = cfg.n_layers
+    params = init_params(cfg, 1, 0.05)
+    units = list(range(L)) + [mt.UNIT_HEAD]
+    with make_ctx(cfg, 2, 128, params, buffers=L + 1, flags=mt.MT_KEEP_GRADS | mt.MT_TRACE) as ctx:
+        tok, tgt = synth.token_batch(1, 2, 128, cfg.vocab)
+        scheds = []
+        for _ in range(3):
+            ctx.train_step(tok, tgt)
+            scheds.append(ctx.schedule())
+    for k, sched in enumerate(scheds):
+        for e in sorted(sched, key=lambda e: e["t0"]):   # shown on failure
+            print(k, f'{e["phase"]:7s} unit {e["unit"]:3d} stream {e["stream"]} {e["t0"]:9.3f} {e["t1"]:9.3f}')
+        comp = [(e["phase"], e["unit"]) for e in sched if e["stream"] == 1]
+        assert comp == [("fwd", l) for l in range(L)] + [("head", mt.UNIT_HEAD)] + \
+            [("bwd", l) for l in reversed(range(L))]
+    head_t0 = {k: [e for e in s if e["phase"] == "head"][0]["t0"] for k, s in enumerate(scheds)}
+    loads = [[e["unit"] for e in s if e["phase"] == "load" and e["stream"] == 0] for s in scheds]
+    refr = [[e for e in s if e["phase"] == "refresh" and e["stream"] == 0] for s in scheds]
+    assert loads[0] == units
+    for k in range(3):
+        # forward only
+        assert all(e["t1"] <= head_t0[k] for e in scheds[k] if e["phase"] == "load" and e["stream"] == 0)
+        by = {(e["phase"], e["unit"]): e for e in scheds[k] if e["stream"] in (1, 2, 3)}
+        for e in refr[k]:
+            assert e["t0"] >= by[("grad", e["unit"])]["t1"] - 1e-3
+            assert e["t0"] >= by[("adamw", e["unit"])]["t1"] - 0.5
+    for k in (1, 2):
+        done = {e["unit"] for e in refr[k - 1]}
+        assert sorted(loads[k], key=units.index) == [u for u in units if u not in done]
+    # (the first step's updates may all land after its last gradient: fresh
+    # host pages make them slow)
+    assert min(len(loads[1]), len(loads[2])) < len(units)
+    with make_ctx(cfg, 2, 128, params, buffers=4, flags=mt.MT_KEEP_GRADS | mt.MT_TRACE) as ctx:
+        ctx.train_step(tok, tgt)
+        ctx.train_step(tok, tgt)
+        sched = ctx.schedule()
+        refreshed = {e["unit"] for e in sched if e["phase"] == "refresh"}
+    assert refreshed <= {L - 1, mt.UNIT_HEAD}
+    t_head = [e for e in sched if e["phase"] == "head"][0]["t0"]
+    bwd_loads = [e["unit"] for e in sched if e["phase"] == "load" and e["stream"] == 0 and e["t0"] >= t_head]
+    assert bwd_loads == list(range(L - 4, -1, -1))
 
 
 def test_token_order_is_exact():
