@@ -103,6 +103,21 @@ def link_probe(mib=1024, reps=3):
     return out
 
 
+def host_probe(n=1 << 28, reps=3):
+    """The library's own host AdamW (the step's pool size) over n parameters
+    with a bf16 image, alone: the rate of host-memory traffic the box sustains
+    for it, 30 bytes per parameter (read p, m, v, g; write p, m, v, image)."""
+    from host_memory_streamed_amd import mt
+    p, m, v, g = (np.full(n, x, np.float32) for x in (0.01, 0.0, 0.0, 1e-3))
+    img = np.zeros(n, np.uint16)
+    best = 0.0
+    for t in range(1, reps + 1):
+        t0 = time.perf_counter()
+        mt.adamw_host(p, m, v, g, t, 1e-4, 0.9, 0.999, 1e-8, 0.01, bf16_out=img)
+        best = max(best, 30.0 * n / (time.perf_counter() - t0))
+    return best
+
+
 def link_roofline(w, stats, step_s, bw, wbytes):
     """The step's host-link bound from the bytes the step moves in each phase.
     Forward phase: every unit image in, plus x0 and the targets. Backward
@@ -353,6 +368,14 @@ def main():
             t_dup = max(h2d / bw["h2d"], d2h / bw["d2h"])
             out["link_roofline"] = {"bw_h2d_GBps": round(bw["h2d"] / 1e9, 2), "bw_d2h_GBps": round(bw["d2h"] / 1e9, 2),
                                     "t_link_duplex_s": round(t_dup, 4), "frac_duplex": round(t_dup / (ms * 1e-3), 4)}
+    if not args.no_link_probe:
+        # host-memory bound: every byte the step's AdamW moves plus every byte
+        # the copies move, at the rate the AdamW alone sustains
+        hbw = host_probe()
+        log(f"host probe: AdamW {hbw / 30e9:.2f} Gparam/s, {hbw / 1e9:.1f} GB/s")
+        hbytes = mean("adamw_bytes") + h2d + d2h
+        out["host_roofline"] = {"adamw_GBps": round(hbw / 1e9, 1), "bytes_step": hbytes,
+                                "t_host_s": round(hbytes / hbw, 4), "frac": round(hbytes / hbw / (ms * 1e-3), 4)}
     if args.copy_probe:
         n = args.copy_probe << 18   # fp32 elements
         src = torch.ones(n, device="cuda")
