@@ -220,6 +220,8 @@ def main():
     ap.add_argument("--sync-opt", action="store_true",
                     help="every AdamW update lands before its step returns (default: updates may finish "
                          "during the next step's forward, in the order it loads the units)")
+    ap.add_argument("--progress", action="store_true",
+                    help="print a line as each layer of a step finishes (for steps that take minutes)")
     ap.add_argument("--no-link-probe", action="store_true",
                     help="skip the plain pinned-copy measurement of the host link after the run")
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -242,7 +244,8 @@ def main():
     if args.layers:
         w = mt.Workload(**{**w.__dict__, "n_layers": args.layers})
     dtype = mt.MT_BF16 if args.dtype == "bf16" else mt.MT_FP32
-    flags = mt.MT_KERNEL_TIMING | mt.MT_TRACE | (0 if args.sync_opt else mt.MT_OVERLAP_OPT)
+    flags = mt.MT_KERNEL_TIMING | mt.MT_TRACE | (0 if args.sync_opt else mt.MT_OVERLAP_OPT) | \
+        (mt.MT_PROGRESS if args.progress else 0)
     buffers = w.n_layers + 1 if args.resident else min(max(2, args.layer_buffers), w.n_layers + 1)
     ctx = build_context(w, dtype, args.seed, flags, chunk_rows=args.chunk_rows, ckpt_host=args.ckpt_host,
                         buffers=buffers)
@@ -286,8 +289,8 @@ def main():
     mfu = mean("model_flops") / (ms * 1e-3) / peak
     h2d, d2h = mean("h2d_bytes"), mean("d2h_bytes")
     # copy engine rates over the last step's copies
-    loads = [e for e in sched if e["phase"] in ("load", "refresh") and e["stream"] == 0]
-    grads = [e for e in sched if e["phase"] == "grad" and e["stream"] == 2]
+    loads = [e for e in sched if e["phase"] in ("load", "refresh", "ckpt_in") and e["stream"] == 0]
+    grads = [e for e in sched if e["phase"] in ("grad", "ckpt_out") and e["stream"] == 2]
     h2d_busy = sum(e["t1"] - e["t0"] for e in loads) * 1e-3
     d2h_busy = sum(e["t1"] - e["t0"] for e in grads) * 1e-3
     unit_bytes_h2d = stats[-1]["h2d_bytes"] - M * (w.d_model + 1) * 4

@@ -123,7 +123,8 @@ static int validate(const mt_model_cfg* c, std::string& why) {
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f) || !(c->lr >= 0.0) || !(c->beta1 >= 0.0 && c->beta1 < 1.0) ||
       !(c->beta2 >= 0.0 && c->beta2 < 1.0) || !(c->adam_eps >= 0.0))
     return bad("invalid eps / rope_base / AdamW hyperparameters");
-  if (c->flags & ~(MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE | MT_OVERLAP_OPT)) return bad("unknown flags");
+  if (c->flags & ~(MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE | MT_OVERLAP_OPT | MT_PROGRESS))
+    return bad("unknown flags");
   if (c->chunk_rows < 0) return bad("chunk_rows must be >= 0");
   if (c->ckpt_host < 0 || (c->ckpt_host > 0 && c->ckpt_host > c->n_layers - 2))
     return bad("ckpt_host must be 0 or in [1, n_layers - 2]");
@@ -152,7 +153,9 @@ static void free_ctx(Ctx* c) {
     if (u.shadow) hipHostFree(u.shadow);
   }
   for (auto* p : c->ring_slot) hipHostFree(p);
-  for (auto* p : c->ck_host) hipHostFree(p);
+  for (auto* p : c->ck_host) host_free_plain(p, (size_t)c->M_max * c->D.d * 4);
+  for (auto* p : c->bounce)
+    if (p) hipHostFree(p);
   for (void* p : {(void*)c->x0_host, (void*)c->dx0_host, (void*)c->tgt_host, (void*)c->loss_host})
     if (p) hipHostFree(p);
   for (void* p : c->dev_allocs) hipFree(p);
@@ -406,10 +409,13 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
     ok &= dalloc(slot * (size_t)dev_slots, (void**)&c.ckpt);
     if (!ok) { mt_destroy(h); return set_error(nullptr, MT_EDEVOOM, "device allocation of residual checkpoints failed"); }
     for (int i = 0; i < k; ++i) {
-      float* p = nullptr;
-      HIP_OR(hipHostMalloc((void**)&p, slot, hipHostMallocDefault), MT_EHOSTOOM, "pinned checkpoint slab");
+      float* p = (float*)host_alloc_plain(slot);
+      if (!p) { mt_destroy(h); return set_error(nullptr, MT_EHOSTOOM, "host checkpoint slab"); }
       c.ck_host.push_back(p);
     }
+    if (k > 0)
+      for (auto*& b : c.bounce)
+        HIP_OR(hipHostMalloc((void**)&b, slot, hipHostMallocDefault), MT_EHOSTOOM, "pinned checkpoint bounce slab");
   }
 
 

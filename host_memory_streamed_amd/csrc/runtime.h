@@ -215,11 +215,15 @@ struct Ctx {
   // Residual checkpoints x_0..x_L (x_i is layer i's input, x_L the head's).
   // x_i with i >= ck_nh stays in a device slot from its forward to its
   // backward use. The others pass through two device staging buffers (x_i in
-  // stage[i % 2]): x_1..x_{ck_nh-3} are copied to pinned host slabs after
-  // their forward and back before their backward, x_0 comes back from the
+  // stage[i % 2]): x_1..x_{ck_nh-3} are parked in host slabs after their
+  // forward and come back before their backward, x_0 comes back from the
   // gathered embedding rows, and the last two fit in the stages throughout.
+  // The slabs are pageable (pinned memory is a scarce, capped resource): x_i
+  // crosses the link through the pinned bounce slab bounce[i % 2], and the
+  // worker pool copies between the bounce slab and the parked slab.
   int ck_nh = 0;                 // 0, or (host slabs) + 3
-  std::vector<float*> ck_host;   // slabs for x_1..x_{ck_nh-3}
+  std::vector<float*> ck_host;   // pageable slabs for x_1..x_{ck_nh-3}
+  float* bounce[2] = {nullptr, nullptr};   // pinned, M_max * d floats each
   float* stage[2] = {nullptr, nullptr};
   float* ckpt_dev(int i) const {
     return i >= ck_nh ? ckpt + (int64_t)(i - ck_nh) * M_max * D.d : stage[i & 1];

@@ -34,7 +34,9 @@
 #include <algorithm>
 #include <chrono>
 #include <cmath>
+#include <cstdio>
 #include <cstring>
+#include <memory>
 
 #include "kernels.h"
 #include "runtime.h"
@@ -334,22 +336,50 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
     return set_error(&c, MT_EHIP, std::string("hipEventQuery: ") + hipGetErrorString(r));
   };
   std::vector<char> grad_issued(L + 1, 0);
+  const bool show_progress = (c.cfg.flags & MT_PROGRESS) != 0;
+  int next_shown = 0;
   size_t next_l = 0;
   int next_c = 0, next_g = 0, next_a = 0;
   bool loss_issued = false, loss_checked = false, dx0_issued = false, dx0_done = false;
 
   // parked residual checkpoints (see Ctx::ckpt_dev): x_i, i in [1, kpark],
-  // goes to its host slab once the forward that wrote it has finished, and
-  // x_j, j in [0, kpark], comes back into stage[j % 2] once the last reader
-  // of x_{j+2} (which shares that stage) has finished
+  // goes to the pinned bounce slab bounce[i % 2] once the forward that wrote
+  // it has finished (and the pool has copied x_{i-2} out of that slab), then
+  // the pool copies it into its pageable host slab. In the backward the pool
+  // copies x_j back into bounce[j % 2] (once x_{j+2} has left it), and x_j,
+  // j in [0, kpark], comes back into stage[j % 2] once the last reader of
+  // x_{j+2} (which shares that stage) has finished; x_0 comes straight from
+  // the gathered embedding rows
   const int nh = c.ck_nh, kpark = nh ? nh - 3 : 0;
   const size_t ck_bytes = (size_t)M * d * 4;
   std::vector<char> save_issued(L + 1, 0), reload_issued(L + 1, 0);
   int next_s = 1, next_r = kpark;
   auto ck_ev = [&](int i, int slot) -> hipEvent_t { return E.ck_trace[(size_t)i * 4 + slot]; };
+  // host side of parking: the pool copies bounce[i % 2] -> slab after x_i's
+  // D2H (cp_out), and slab -> bounce[j % 2] before x_j's H2D (cp_in); the
+  // flags are set by the copy jobs, which all finish before the step returns
+  std::unique_ptr<std::atomic<char>[]> cp_out(new std::atomic<char>[L + 1]()), cp_in(new std::atomic<char>[L + 1]());
+  std::atomic<int> ck_jobs{0};
+  int next_co = 1, next_ci = kpark;
+  auto host_copy = [&](float* dst, const float* src, std::atomic<char>* flag) {
+    const size_t ch = (size_t)64 << 20;
+    const int64_t n = (int64_t)((ck_bytes + ch - 1) / ch);
+    ck_jobs.fetch_add(1);
+    c.pool->submit(
+        n,
+        [dst, src, ch, bytes = ck_bytes](int64_t t) {
+          const size_t a = (size_t)t * ch, b = std::min(bytes, a + ch);
+          std::memcpy(reinterpret_cast<char*>(dst) + a, reinterpret_cast<const char*>(src) + a, b - a);
+        },
+        [flag, &ck_jobs] {
+          flag->store(1);
+          ck_jobs.fetch_sub(1);
+        },
+        INT64_MIN + 1);
+  };
   auto issue_save = [&](int i) -> int {
     if (trace) HIPCK(hipEventRecord(ck_ev(i, 0), c.s_out));
-    HIPCK(hipMemcpyAsync(c.ck_host[i - 1], c.stage[i & 1], ck_bytes, hipMemcpyDeviceToHost, c.s_out));
+    HIPCK(hipMemcpyAsync(c.bounce[i & 1], c.stage[i & 1], ck_bytes, hipMemcpyDeviceToHost, c.s_out));
     if (trace) HIPCK(hipEventRecord(ck_ev(i, 1), c.s_out));
     HIPCK(hipEventRecord(E.ck_saved[i], c.s_out));
     save_issued[i] = 1;
@@ -357,7 +387,7 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
     return MT_OK;
   };
   auto issue_reload = [&](int j) -> int {
-    const float* src = j == 0 ? c.x0_host : c.ck_host[j - 1];
+    const float* src = j == 0 ? c.x0_host : c.bounce[j & 1];
     if (trace) HIPCK(hipEventRecord(ck_ev(j, 2), c.s_in));
     HIPCK(hipMemcpyAsync(c.stage[j & 1], src, ck_bytes, hipMemcpyHostToDevice, c.s_in));
     if (trace) HIPCK(hipEventRecord(ck_ev(j, 3), c.s_in));
@@ -488,13 +518,41 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
       progress = true;
     }
     if (rc) break;
-    // parked checkpoints out, in order, once the forward that wrote them is done
+    // parked checkpoints out, in order, once the forward that wrote them is
+    // done and their bounce slab has been copied out of
     while (next_s <= kpark) {
       const int st = item_done(next_s - 1);
       if (st < 0) { rc = st; break; }
       if (!st) break;
+      if (next_s - 2 >= 1 && !cp_out[next_s - 2].load()) break;
       if ((rc = issue_save(next_s))) break;
       ++next_s;
+      progress = true;
+    }
+    if (rc) break;
+    // bounce -> parked slab once the D2H has landed
+    while (next_co < next_s) {
+      const int st = event_done(E.ck_saved[next_co]);
+      if (st < 0) { rc = st; break; }
+      if (!st) break;
+      host_copy(c.ck_host[next_co - 1], c.bounce[next_co & 1], &cp_out[next_co]);
+      ++next_co;
+      progress = true;
+    }
+    if (rc) break;
+    // parked slab -> bounce, in backward order, once the slab is whole and
+    // the bounce slab's previous H2D (x_{j+2}) has landed
+    while (nh && next_ci >= 1) {
+      const int j = next_ci;
+      if (!cp_out[j].load()) break;
+      if (j + 2 <= kpark) {
+        if (!reload_issued[j + 2]) break;
+        const int st = event_done(E.ck_loaded[j + 2]);
+        if (st < 0) { rc = st; break; }
+        if (!st) break;
+      }
+      host_copy(c.bounce[j & 1], c.ck_host[j - 1], &cp_in[j]);
+      --next_ci;
       progress = true;
     }
     if (rc) break;
@@ -504,6 +562,7 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
       const int st = item_done(reader);
       if (st < 0) { rc = st; break; }
       if (!st) break;
+      if (next_r >= 1 && !cp_in[next_r].load()) break;
       if ((rc = issue_reload(next_r))) break;
       --next_r;
       progress = true;
@@ -521,6 +580,19 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
         progress = true;
       }
     }
+    // progress lines, as compute items finish in order
+    while (show_progress && next_shown < next_c) {
+      const int st = event_done(E.freed[next_shown]);
+      if (st < 0) { rc = st; break; }
+      if (!st) break;
+      const Item& it = items[next_shown];
+      fprintf(stderr, "[mt] step %lld: %s %d done at %.1f ms\n", (long long)c.step + 1,
+              it.phase == PH_FWD ? "forward layer" : it.phase == PH_HEAD ? "head" : "backward layer",
+              it.phase == PH_HEAD ? 0 : it.unit, ms_since(t_begin));
+      fflush(stderr);
+      ++next_shown;
+    }
+    if (rc) break;
     // per-token losses once the head has run
     if (!loss_issued) {
       const int st = item_done(head_item);
@@ -602,6 +674,8 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
     if (dx0_done && next_a > L) break;
     if (!progress) std::this_thread::sleep_for(std::chrono::microseconds(10));
   }
+  // the checkpoint copy jobs read and write this step's state: let them finish
+  while (ck_jobs.load()) std::this_thread::sleep_for(std::chrono::microseconds(20));
   if (rc) {
     // drain what was submitted before reporting the error
     hipStreamSynchronize(c.s_in);

@@ -69,6 +69,9 @@ extern "C" {
  * or write the host state (mt_params, mt_grads, mt_opt_state, mt_set_param)
  * and mt_destroy wait for pending updates first; mt_sync waits explicitly. */
 #define MT_OVERLAP_OPT 8u
+/* Print one line to stderr as each forward, head and backward item of a step
+ * finishes on the device (for steps that take minutes). */
+#define MT_PROGRESS 16u
 
 typedef struct mt_model_cfg {
   int32_t n_layers;
@@ -91,7 +94,7 @@ typedef struct mt_model_cfg {
    * fetch it either. Results do not depend on k. */
   int32_t n_layer_buffers;
   int32_t host_threads;      /* AdamW / gather pool size; 0 = online CPUs (at most 64) */
-  uint32_t flags;            /* MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE | MT_OVERLAP_OPT */
+  uint32_t flags;            /* MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE | MT_OVERLAP_OPT | MT_PROGRESS */
   float rms_eps;
   float rope_base;
   double lr, beta1, beta2, adam_eps, weight_decay;   /* AdamW hyperparameters */

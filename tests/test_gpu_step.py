@@ -192,6 +192,15 @@ def test_1p3b_layer_shape_reduced_depth(mode):
     run_parity(cfg, 1, 256, mode, seed=11)
 
 
+@pytest.mark.parametrize("mode", ["fp32", "bf16"])
+def test_1p3b_full_depth_short_sequence(mode):
+    # all 24 layers of the 1.3B workload (d 2048, FFN 5632, vocab 32000) on
+    # 1 x 96 tokens: the streamed schedule's accumulation through the full
+    # depth at the real width, against the oracle's whole step
+    cfg, _, _ = shape("1.3b")
+    run_parity(cfg, 1, 96, mode, seed=31)
+
+
 def test_14b_layer_shape_one_layer_bf16():
     # per-layer and head shape of the 14B workload (GQA 40/8, vocab 152064), 1 layer
     cfg, _, _ = shape("14b", n_layers=1)
