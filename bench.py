@@ -103,6 +103,28 @@ def link_probe(mib=1024, reps=3):
     return out
 
 
+def fit_layers(w, dtype, flags, share=0.85):
+    """The most layers of w (at most its own count) whose host store, as the
+    library sizes it, takes at most `share` of the memory available now."""
+    from host_memory_streamed_amd import mt
+    avail = None
+    with open("/proc/meminfo") as f:
+        for line in f:
+            if line.startswith("MemAvailable:"):
+                avail = int(line.split()[1]) * 1024
+    if avail is None:
+        return w.n_layers
+    best = 0
+    for L in range(1, w.n_layers + 1):
+        cfg = mt.make_config(L, w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn_dim, w.vocab,
+                             w.batch, w.seq, dtype=dtype, flags=flags)
+        hb = mt.host_bytes(cfg)
+        if hb["pinned"] + hb["pageable"] > share * avail:
+            break
+        best = L
+    return max(best, 1)
+
+
 def host_probe(n=1 << 28, reps=3):
     """The library's own host AdamW (the step's pool size) over n parameters
     with a bf16 image, alone: the rate of host-memory traffic the box sustains
@@ -241,11 +263,20 @@ def main():
         import __graft_entry__
         __graft_entry__.build()
     w = mt.WORKLOADS[args.workload]
-    if args.layers:
-        w = mt.Workload(**{**w.__dict__, "n_layers": args.layers})
     dtype = mt.MT_BF16 if args.dtype == "bf16" else mt.MT_FP32
     flags = mt.MT_KERNEL_TIMING | mt.MT_TRACE | (0 if args.sync_opt else mt.MT_OVERLAP_OPT) | \
         (mt.MT_PROGRESS if args.progress else 0)
+    layers_note = None
+    if args.layers:
+        w = mt.Workload(**{**w.__dict__, "n_layers": args.layers})
+    elif args.workload == "120b":
+        # the 120B-shaped workload keeps its per-layer shape and is cut to the
+        # layers whose host store fits in this machine's RAM
+        L = fit_layers(w, dtype, flags)
+        if L < w.n_layers:
+            layers_note = f"cut from {w.n_layers} to {L} layers to fit host RAM"
+            log(layers_note)
+            w = mt.Workload(**{**w.__dict__, "n_layers": L})
     buffers = w.n_layers + 1 if args.resident else min(max(2, args.layer_buffers), w.n_layers + 1)
     ctx = build_context(w, dtype, args.seed, flags, chunk_rows=args.chunk_rows, ckpt_host=args.ckpt_host,
                         buffers=buffers)
@@ -321,6 +352,7 @@ def main():
                        "every unit in a device cache refreshed by each update" if buffers == w.n_layers + 1 else
                        f"head and top {buffers - 3} layers in a device cache, the rest streamed through 2 buffers"),
                    "layer_buffers": buffers,
+                   **({"layers_note": layers_note} if layers_note else {}),
                    "n_layers": w.n_layers, "d_model": w.d_model, "n_heads": w.n_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ffn_dim": w.ffn_dim,
                    "vocab": w.vocab, "global_batch": w.batch, "seq_len": w.seq,

@@ -105,6 +105,23 @@ static std::vector<TensorRef> tensor_table(const Dims& D) {
   return t;
 }
 
+// Element counts of the pinned gradient staging slots (MT_KEEP_GRADS off).
+// Synchronous updates keep up with the gradients: three slots that fit any
+// unit. Overlapped updates fall behind during the backward and catch up in
+// the next forward: layer-sized slots for as many layers as fit in 16 GiB (3
+// to 16), plus one slot kept for the head (the last entry).
+static std::vector<int64_t> ring_sizes(const mt_model_cfg& cfg, int64_t layer_n, int64_t head_n) {
+  std::vector<int64_t> sizes;
+  if (cfg.flags & MT_OVERLAP_OPT) {
+    const int r = (int)std::max<int64_t>(3, std::min<int64_t>(16, (16LL << 30) / (layer_n * 4)));
+    sizes.assign(r, layer_n);
+    sizes.push_back(head_n);
+  } else {
+    sizes.assign(3, std::max(layer_n, head_n));
+  }
+  return sizes;
+}
+
 static int validate(const mt_model_cfg* c, std::string& why) {
   if (!c) { why = "cfg is NULL"; return MT_EINVAL; }
   auto bad = [&](const char* m) { why = m; return MT_EINVAL; };
@@ -269,20 +286,8 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
   }
   int64_t max_unit = std::max(c.units[0].lay.n, c.units[D.L].lay.n);
   if (!keep) {
-    // Synchronous updates keep up with the gradients: three slots that fit
-    // any unit. Overlapped updates fall behind during the backward and catch
-    // up in the next forward: layer-sized slots for as many layers as fit in
-    // 16 GiB (3 to 16), plus one slot kept for the head.
-    std::vector<int64_t> sizes;
-    if (cfg->flags & MT_OVERLAP_OPT) {
-      const int64_t ln = c.units[0].lay.n;
-      const int r = (int)std::max<int64_t>(3, std::min<int64_t>(16, (16LL << 30) / (ln * 4)));
-      sizes.assign(r, ln);
-      sizes.push_back(c.units[D.L].lay.n);
-      c.head_slot = r;
-    } else {
-      sizes.assign(3, max_unit);
-    }
+    const std::vector<int64_t> sizes = ring_sizes(*cfg, c.units[0].lay.n, c.units[D.L].lay.n);
+    if (cfg->flags & MT_OVERLAP_OPT) c.head_slot = (int)sizes.size() - 1;
     for (int64_t n : sizes) {
       float* p = nullptr;
       HIP_OR(hipHostMalloc((void**)&p, (size_t)n * 4, hipHostMallocDefault), MT_EHOSTOOM, "pinned gradient ring");
@@ -447,6 +452,38 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
     }
   }
   *out = h;
+  return MT_OK;
+}
+
+int mt_host_bytes(const mt_model_cfg* cfg, int64_t* state_bytes, int64_t* pinned_bytes,
+                  int64_t* pageable_bytes, int64_t* parked_ckpt_bytes) {
+  std::string why;
+  if (validate(cfg, why)) return set_error(nullptr, MT_EINVAL, why);
+  const Dims D = make_dims(*cfg);
+  const UnitLayout ll = layer_layout(D), hl = head_layout(D), el = emb_layout(D);
+  const int S = cfg->compute_dtype;
+  const bool keep = cfg->flags & MT_KEEP_GRADS;
+  const int64_t M = (int64_t)cfg->max_batch * cfg->max_seq;
+  int64_t state = 0, pinned = 0, pageable = 0;
+  auto unit = [&](const UnitLayout& u, bool streamed) {
+    const int64_t nb = u.n * 4;
+    state += 3 * nb;                                  // p, m, v
+    if (streamed && S == 0) { pinned += nb; pageable += 2 * nb; }
+    else pageable += 3 * nb;
+    if (streamed && keep) pinned += nb;               // kept gradients
+    if (!streamed) pageable += nb;                    // embedding gradient
+    if (streamed && S == 1) pinned += (int64_t)u.image_bytes(S);   // bf16 image
+  };
+  for (int l = 0; l < D.L; ++l) unit(ll, true);
+  unit(hl, true);
+  unit(el, false);
+  if (!keep)
+    for (int64_t n : ring_sizes(*cfg, ll.n, hl.n)) pinned += n * 4;
+  pinned += 2 * M * D.d * 4 + 2 * M * 4;             // x0 / dx0, targets / losses staging
+  if (state_bytes) *state_bytes = state;
+  if (pinned_bytes) *pinned_bytes = pinned;
+  if (pageable_bytes) *pageable_bytes = pageable;
+  if (parked_ckpt_bytes) *parked_ckpt_bytes = M * D.d * 4;
   return MT_OK;
 }
 

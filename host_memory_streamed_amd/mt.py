@@ -68,6 +68,8 @@ _P = ctypes.c_void_p
 _I32, _I64, _F = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 _SIGS = {
     "mt_tensor_count": (_I32, [ctypes.POINTER(ModelConfig)]),
+    "mt_host_bytes": (ctypes.c_int, [ctypes.POINTER(ModelConfig), ctypes.POINTER(_I64), ctypes.POINTER(_I64),
+                                     ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "mt_tensor_info": (ctypes.c_int, [ctypes.POINTER(ModelConfig), _I32, ctypes.c_char_p, _I32,
                                       ctypes.POINTER(_I64), ctypes.POINTER(_I32)]),
     "mt_create": (ctypes.c_int, [ctypes.POINTER(ModelConfig), _P, ctypes.POINTER(DeviceEnv), ctypes.POINTER(_P)]),
@@ -156,6 +158,14 @@ def make_config(n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab
     return ModelConfig(n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab, max_batch,
                        max_seq, dtype, n_layer_buffers, host_threads, flags, rms_eps, rope_base, lr,
                        beta1, beta2, adam_eps, weight_decay, chunk_rows, ckpt_host)
+
+
+def host_bytes(cfg: ModelConfig) -> dict:
+    """Host memory a context of cfg allocates (no GPU needed)."""
+    st, pin, pag, ck = _I64(), _I64(), _I64(), _I64()
+    _check(lib().mt_host_bytes(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(pin), ctypes.byref(pag),
+                               ctypes.byref(ck)))
+    return {"state": st.value, "pinned": pin.value, "pageable": pag.value, "parked_ckpt": ck.value}
 
 
 def tensor_table(cfg: ModelConfig):

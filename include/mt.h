@@ -132,6 +132,21 @@ int32_t mt_tensor_count(const mt_model_cfg* cfg);
 int mt_tensor_info(const mt_model_cfg* cfg, int32_t id, char* name, int32_t name_cap,
                    int64_t shape[2], int32_t* ndim);
 
+/* Host memory that mt_create(cfg) allocates, without allocating it (no GPU
+ * needed): for sizing a model to a machine's RAM. state_bytes: the fp32
+ * master p and the AdamW moments m and v, 12 bytes per parameter ("MegaTrain
+ * fits 120B LLM training on one GPU using CPU RAM", section "Who this is
+ * actually for": about 12 GB of host RAM per billion parameters).
+ * pinned_bytes: page-locked memory (the bf16
+ * images, the gradient slots or kept gradients, staging; the fp32 master in
+ * fp32 mode). pageable_bytes: the rest (m, v, the embedding). Parked residual
+ * checkpoints, chosen at create time from free device memory, add
+ * parked_ckpt_bytes of pageable memory each, plus two pinned bounce slabs of
+ * that size when any is parked. Any output may be NULL. MT_EINVAL on a bad
+ * cfg. */
+int mt_host_bytes(const mt_model_cfg* cfg, int64_t* state_bytes, int64_t* pinned_bytes,
+                  int64_t* pageable_bytes, int64_t* parked_ckpt_bytes);
+
 /* Create a context: validates cfg, allocates the host store (fp32 master p,
  * AdamW m and v zeroed, step count 0, the bf16 device-format shadow in bf16
  * mode, gradient buffers), the device layer buffers, gradient buffers,
