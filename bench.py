@@ -227,6 +227,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="14b", help="tiny | 1.3b | 14b | 120b (120b: --layers)")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="override the batch (sequences per step): more tokens per streamed byte")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp32"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -267,6 +269,8 @@ def main():
     flags = mt.MT_KERNEL_TIMING | mt.MT_TRACE | (0 if args.sync_opt else mt.MT_OVERLAP_OPT) | \
         (mt.MT_PROGRESS if args.progress else 0)
     layers_note = None
+    if args.batch:
+        w = mt.Workload(**{**w.__dict__, "batch": args.batch})
     if args.layers:
         w = mt.Workload(**{**w.__dict__, "n_layers": args.layers})
     elif args.workload == "120b":

@@ -253,6 +253,64 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict
   }
 }
 
+// Four consecutive f per thread (F % 4 == 0, 16-byte aligned gu and dact,
+// act / dgu aligned to four elements): one row per blockIdx.y step, 16-byte
+// loads, no per-element index division. Same arithmetic per element as the
+// kernels above.
+template <typename OutT>
+__global__ __launch_bounds__(256) void swiglu_fwd4_kernel(const float* __restrict__ gu,
+                                                          OutT* __restrict__ act, int64_t M, int F) {
+  const int F4 = F / 4;
+  for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+    const floatx4* g4 = reinterpret_cast<const floatx4*>(gu + m * 2 * F);
+    const floatx4* u4 = reinterpret_cast<const floatx4*>(gu + m * 2 * F + F);
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < F4; j += gridDim.x * blockDim.x) {
+      const floatx4 g = g4[j], u = u4[j];
+      floatx4 a;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = g[e] * sigmoidf(g[e]) * u[e];
+      store4<OutT>(act + m * F + 4 * j, a);
+    }
+  }
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(256) void swiglu_bwd4_kernel(const float* __restrict__ gu,
+                                                          const float* __restrict__ dact,
+                                                          OutT* __restrict__ dgu, int64_t M, int F) {
+  const int F4 = F / 4;
+  for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+    const floatx4* g4 = reinterpret_cast<const floatx4*>(gu + m * 2 * F);
+    const floatx4* u4 = reinterpret_cast<const floatx4*>(gu + m * 2 * F + F);
+    const floatx4* d4 = reinterpret_cast<const floatx4*>(dact + m * F);
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < F4; j += gridDim.x * blockDim.x) {
+      const floatx4 g = g4[j], u = u4[j], da = d4[j];
+      floatx4 dg, du;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float sg = sigmoidf(g[e]);
+        dg[e] = da[e] * u[e] * sg * (1.f + g[e] * (1.f - sg));
+        du[e] = da[e] * g[e] * sg;
+      }
+      store4<OutT>(dgu + m * 2 * F + 4 * j, dg);
+      store4<OutT>(dgu + m * 2 * F + F + 4 * j, du);
+    }
+  }
+}
+
+// grid of the row-wise vector kernels: blocks across a row's F/4 groups,
+// rows strided over at most 8192 block rows
+dim3 grid4(int64_t M, int F) {
+  const int bx = (F / 4 + 255) / 256;
+  return dim3((unsigned)bx, (unsigned)(M < 8192 ? M : 8192));
+}
+
+bool vec4_ok(int F, const void* a, const void* b, const void* c, size_t out_bytes) {
+  const uintptr_t o = out_bytes == 2 ? 7 : 15;
+  return F % 4 == 0 && (reinterpret_cast<uintptr_t>(a) & 15) == 0 && (reinterpret_cast<uintptr_t>(b) & 15) == 0 &&
+         (reinterpret_cast<uintptr_t>(c) & o) == 0;
+}
+
 // ---------------------------------------------------------- cross-entropy ---
 
 // One block per row: logsumexp by an online max/sum per thread, then
@@ -304,6 +362,23 @@ __global__ void cast_kernel(const float* __restrict__ x, OutT* __restrict__ y, i
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
     y[i] = from_f32<OutT>(x[i]);
+}
+
+// Eight elements per thread: two 16-byte loads, one 16-byte store (n8 groups
+// of eight; x and y 16-byte aligned).
+__global__ void cast8_bf16_kernel(const float* __restrict__ x, bf16* __restrict__ y, int64_t n8) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const floatx4 a = reinterpret_cast<const floatx4*>(x)[2 * i];
+    const floatx4 b = reinterpret_cast<const floatx4*>(x)[2 * i + 1];
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[e] = to_bf16(a[e]);
+      o[4 + e] = to_bf16(b[e]);
+    }
+    reinterpret_cast<bf16x8*>(y)[i] = o;
+  }
 }
 
 unsigned grid_for(int64_t n) {
@@ -368,20 +443,32 @@ hipError_t rope(int out_dtype, int backward, const float* in, void* out, const f
 
 hipError_t swiglu_fwd(int out_dtype, const float* gu, void* act, int64_t M, int F, hipStream_t s) {
   if (M * F == 0) return hipSuccess;
-  if (out_dtype == 1)
+  if (vec4_ok(F, gu, gu, act, out_dtype == 1 ? 2 : 4)) {
+    if (out_dtype == 1)
+      hipLaunchKernelGGL(swiglu_fwd4_kernel<bf16>, grid4(M, F), dim3(256), 0, s, gu, (bf16*)act, M, F);
+    else
+      hipLaunchKernelGGL(swiglu_fwd4_kernel<float>, grid4(M, F), dim3(256), 0, s, gu, (float*)act, M, F);
+  } else if (out_dtype == 1) {
     hipLaunchKernelGGL(swiglu_fwd_kernel<bf16>, dim3(grid_for(M * F)), dim3(256), 0, s, gu, (bf16*)act, M, F);
-  else
+  } else {
     hipLaunchKernelGGL(swiglu_fwd_kernel<float>, dim3(grid_for(M * F)), dim3(256), 0, s, gu, (float*)act, M, F);
+  }
   return hipGetLastError();
 }
 
 hipError_t swiglu_bwd(int out_dtype, const float* gu, const float* dact, void* dgu, int64_t M, int F,
                       hipStream_t s) {
   if (M * F == 0) return hipSuccess;
-  if (out_dtype == 1)
+  if (vec4_ok(F, gu, dact, dgu, out_dtype == 1 ? 2 : 4)) {
+    if (out_dtype == 1)
+      hipLaunchKernelGGL(swiglu_bwd4_kernel<bf16>, grid4(M, F), dim3(256), 0, s, gu, dact, (bf16*)dgu, M, F);
+    else
+      hipLaunchKernelGGL(swiglu_bwd4_kernel<float>, grid4(M, F), dim3(256), 0, s, gu, dact, (float*)dgu, M, F);
+  } else if (out_dtype == 1) {
     hipLaunchKernelGGL(swiglu_bwd_kernel<bf16>, dim3(grid_for(M * F)), dim3(256), 0, s, gu, dact, (bf16*)dgu, M, F);
-  else
+  } else {
     hipLaunchKernelGGL(swiglu_bwd_kernel<float>, dim3(grid_for(M * F)), dim3(256), 0, s, gu, dact, (float*)dgu, M, F);
+  }
   return hipGetLastError();
 }
 
@@ -397,7 +484,11 @@ hipError_t xent(int out_dtype, const float* logits, const int32_t* targets, floa
 
 hipError_t cast(int out_dtype, const float* x, void* y, int64_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  if (out_dtype == 1)
+  const bool vec = n % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+  if (out_dtype == 1 && vec)
+    hipLaunchKernelGGL(cast8_bf16_kernel, dim3(grid_for(n / 8)), dim3(256), 0, s, x, (bf16*)y, n / 8);
+  else if (out_dtype == 1)
     hipLaunchKernelGGL(cast_kernel<bf16>, dim3(grid_for(n)), dim3(256), 0, s, x, (bf16*)y, n);
   else
     hipLaunchKernelGGL(cast_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, x, (float*)y, n);

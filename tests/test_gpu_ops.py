@@ -412,9 +412,11 @@ def test_attention_512k_tokens_sampled():
 
 # ------------------------------------------------------- SwiGLU / CE / cast ---
 
+# F % 4 == 0: four per thread, row-wise; F = 170: one per thread; the real FFN
+# width of the 14B-shaped model
 @pytest.mark.parametrize("dtype", [mt.MT_FP32, mt.MT_BF16])
-def test_swiglu(dtype):
-    M, F = 77, 172
+@pytest.mark.parametrize("M,F", [(77, 172), (33, 170), (5, 13824)])
+def test_swiglu(dtype, M, F):
     gu = (RNG.standard_normal((M, 2 * F)) * 4).astype(np.float32)
     da = RNG.standard_normal((M, F)).astype(np.float32)
     tdt = torch.bfloat16 if dtype else torch.float32
@@ -429,6 +431,29 @@ def test_swiglu(dtype):
     rt = 2.0 ** -8 if dtype else 2e-6
     assert np.all(np.abs(host(act) - aref) <= rt * np.abs(aref) + 1e-6)
     assert np.all(np.abs(host(dgu) - dref) <= rt * np.abs(dref) + 1e-6)
+
+
+@pytest.mark.parametrize("dtype", [mt.MT_FP32, mt.MT_BF16])
+def test_swiglu_vector_path_is_bitwise_scalar(dtype):
+    # the same operands one element off 16-byte alignment take the
+    # one-per-thread kernels: identical bits
+    M, F = 40, 512
+    gu = (RNG.standard_normal((M, 2 * F)) * 4).astype(np.float32)
+    da = RNG.standard_normal((M, F)).astype(np.float32)
+    tdt = torch.bfloat16 if dtype else torch.float32
+    outs = []
+    for off in (0, 1):
+        gbuf = torch.zeros(M * 2 * F + off, device=DEV)
+        gbuf[off:] = dev(gu).reshape(-1)
+        dbuf = torch.zeros(M * F + off, device=DEV)
+        dbuf[off:] = dev(da).reshape(-1)
+        act = torch.empty(M * F + off, device=DEV, dtype=tdt)
+        dgu = torch.empty(M * 2 * F + off, device=DEV, dtype=tdt)
+        mt.swiglu_fwd(dtype, gbuf[off:], act[off:], M, F)
+        mt.swiglu_bwd(dtype, gbuf[off:], dbuf[off:], dgu[off:], M, F)
+        outs.append((host(act[off:]), host(dgu[off:])))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
 
 
 @pytest.mark.parametrize("dtype", [mt.MT_FP32, mt.MT_BF16])
@@ -462,9 +487,13 @@ def test_cross_entropy_in_place_repeated():
         np.testing.assert_allclose(host(zd), dref * rows, rtol=1e-5, atol=1e-7)
 
 
-def test_cast_is_round_to_nearest_even():
-    x = np.concatenate([RNG.standard_normal(10000).astype(np.float32),
-                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8)], np.float32)])
-    y = torch.empty(x.size, device=DEV, dtype=torch.bfloat16)
-    mt.cast(mt.MT_BF16, dev(x), y, x.size)
-    np.testing.assert_array_equal(host(y), O.bf16(x))
+# 10003 elements: the scalar path; 8 * 4099: eight per thread (16-byte
+# loads and stores); the same from an offset of one element: scalar again
+@pytest.mark.parametrize("n,off", [(10003, 0), (8 * 4099, 0), (8 * 4099, 1)])
+def test_cast_is_round_to_nearest_even(n, off):
+    ties = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 0.0, -0.0, 3.0e38], np.float32)
+    x = np.concatenate([RNG.standard_normal(n + off - ties.size).astype(np.float32), ties])
+    xd = dev(x)
+    y = torch.empty(n + off, device=DEV, dtype=torch.bfloat16)
+    mt.cast(mt.MT_BF16, xd[off:], y[off:], n)
+    np.testing.assert_array_equal(host(y[off:]), O.bf16(x[off:]))
