@@ -244,6 +244,9 @@ def main():
     ap.add_argument("--sync-opt", action="store_true",
                     help="every AdamW update lands before its step returns (default: updates may finish "
                          "during the next step's forward, in the order it loads the units)")
+    ap.add_argument("--no-refresh", action="store_true",
+                    help="with a device cache, fetch cached units in the next forward instead of refreshing them "
+                         "in the backward")
     ap.add_argument("--progress", action="store_true",
                     help="print a line as each layer of a step finishes (for steps that take minutes)")
     ap.add_argument("--no-link-probe", action="store_true",
@@ -267,7 +270,7 @@ def main():
     w = mt.WORKLOADS[args.workload]
     dtype = mt.MT_BF16 if args.dtype == "bf16" else mt.MT_FP32
     flags = mt.MT_KERNEL_TIMING | mt.MT_TRACE | (0 if args.sync_opt else mt.MT_OVERLAP_OPT) | \
-        (mt.MT_PROGRESS if args.progress else 0)
+        (mt.MT_PROGRESS if args.progress else 0) | (mt.MT_CACHE_NO_REFRESH if args.no_refresh else 0)
     layers_note = None
     if args.batch:
         w = mt.Workload(**{**w.__dict__, "batch": args.batch})
@@ -353,7 +356,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name + "-shaped decoder, " + (
                        "streamed through 2 layer buffers" if buffers == 2 else
-                       "every unit in a device cache refreshed by each update" if buffers == w.n_layers + 1 else
+                       ("every unit in a device cache, " + ("fetched in the forward" if args.no_refresh else
+                                                            "refreshed by each update"))
+                       if buffers == w.n_layers + 1 else
                        f"head and top {buffers - 3} layers in a device cache, the rest streamed through 2 buffers"),
                    "layer_buffers": buffers,
                    **({"layers_note": layers_note} if layers_note else {}),

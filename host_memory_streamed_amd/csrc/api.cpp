@@ -140,7 +140,7 @@ static int validate(const mt_model_cfg* c, std::string& why) {
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f) || !(c->lr >= 0.0) || !(c->beta1 >= 0.0 && c->beta1 < 1.0) ||
       !(c->beta2 >= 0.0 && c->beta2 < 1.0) || !(c->adam_eps >= 0.0))
     return bad("invalid eps / rope_base / AdamW hyperparameters");
-  if (c->flags & ~(MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE | MT_OVERLAP_OPT | MT_PROGRESS))
+  if (c->flags & ~(MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE | MT_OVERLAP_OPT | MT_PROGRESS | MT_CACHE_NO_REFRESH))
     return bad("unknown flags");
   if (c->chunk_rows < 0) return bad("chunk_rows must be >= 0");
   if (c->ckpt_host < 0 || (c->ckpt_host > 0 && c->ckpt_host > c->n_layers - 2))

@@ -650,7 +650,8 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
     if (rc) break;
     // cached units whose update has landed: refresh their buffers, in any
     // order, after every load that could be issued
-    const int rf_free = c.ncache && !abort ? (rf_last < 0 ? 1 : event_done(E.refreshed[rf_last])) : 0;
+    const bool refresh = c.ncache && !abort && !(c.cfg.flags & MT_CACHE_NO_REFRESH);
+    const int rf_free = refresh ? (rf_last < 0 ? 1 : event_done(E.refreshed[rf_last])) : 0;
     if (rf_free < 0) { rc = rf_free; break; }
     if (rf_free) {
       for (int kk = 0; kk < next_a; ++kk) {

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmt.so")
 MT_OK, MT_EINVAL, MT_EHOSTOOM, MT_EDEVOOM, MT_EHIP, MT_ENONFINITE, MT_ETIMEOUT, MT_ENOGRADS, MT_ESTATE = (
     0, -1, -2, -3, -4, -5, -6, -7, -8)
 MT_FP32, MT_BF16 = 0, 1
-MT_KEEP_GRADS, MT_KERNEL_TIMING, MT_TRACE, MT_OVERLAP_OPT, MT_PROGRESS = 1, 2, 4, 8, 16
+MT_KEEP_GRADS, MT_KERNEL_TIMING, MT_TRACE, MT_OVERLAP_OPT, MT_PROGRESS, MT_CACHE_NO_REFRESH = 1, 2, 4, 8, 16, 32
 MT_GEMM_NT, MT_GEMM_NN, MT_GEMM_TN = 0, 1, 2
 PHASES = {0: "load", 1: "fwd", 2: "head", 3: "bwd", 4: "grad", 5: "adamw", 6: "ckpt_out", 7: "ckpt_in",
           8: "refresh"}

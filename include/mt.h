@@ -72,6 +72,10 @@ extern "C" {
 /* Print one line to stderr as each forward, head and backward item of a step
  * finishes on the device (for steps that take minutes). */
 #define MT_PROGRESS 16u
+/* With a device cache (n_layer_buffers > 2): do not refresh cached units in
+ * the backward; their next image is fetched by the next forward instead, so
+ * the backward's link carries only gradients. */
+#define MT_CACHE_NO_REFRESH 32u
 
 typedef struct mt_model_cfg {
   int32_t n_layers;
@@ -94,7 +98,8 @@ typedef struct mt_model_cfg {
    * fetch it either. Results do not depend on k. */
   int32_t n_layer_buffers;
   int32_t host_threads;      /* AdamW / gather pool size; 0 = online CPUs (at most 64) */
-  uint32_t flags;            /* MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE | MT_OVERLAP_OPT | MT_PROGRESS */
+  uint32_t flags;            /* MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE | MT_OVERLAP_OPT | MT_PROGRESS |
+                                MT_CACHE_NO_REFRESH */
   float rms_eps;
   float rope_base;
   double lr, beta1, beta2, adam_eps, weight_decay;   /* AdamW hyperparameters */

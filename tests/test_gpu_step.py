@@ -358,6 +358,7 @@ def _run_cached_steps(ctx, n, seed, B, T, vocab, n_params, between=None):
     (mt.MT_FP32, 3, mt.MT_OVERLAP_OPT),
     (mt.MT_BF16, 4, mt.MT_KEEP_GRADS | mt.MT_OVERLAP_OPT),
     (mt.MT_BF16, 7, mt.MT_OVERLAP_OPT),
+    (mt.MT_BF16, 7, mt.MT_OVERLAP_OPT | mt.MT_CACHE_NO_REFRESH),
 ])
 def test_streamed_equals_device_cache_bitwise(dtype, buffers, flags):
     cfg = O.Config(6, 128, 2, 1, 64, 200, 300)
