@@ -164,21 +164,24 @@ def link_roofline(w, stats, step_s, bw, wbytes):
     }
 
 
-def cpu_baseline(w, budget_tokens=512):
-    """The CPU oracle (plain float64 NumPy) timed on a bounded sample of the
-    same workload: one decoder layer of the real shape and the real head on
-    1 x budget_tokens tokens, and AdamW on a 16M-element sample; composed into
-    a full-depth step time and reported as tokens/s of that sample."""
+def cpu_baseline(w, vocab_share=8):
+    """The CPU oracle (plain float64 NumPy, as it stands) timed on a bounded
+    sample of the same workload: one decoder layer of the real shape forward
+    and backward on the workload's own 1 x T tokens, the head on the same
+    tokens over 1/vocab_share of the vocabulary (its products and its
+    cross-entropy are linear in the vocabulary size), and AdamW on 16M
+    elements; composed into a full-depth step and reported as tokens/s."""
     import oracle as O
-    from oracle.decoder import _Prec
+    from oracle.decoder import _Prec, _threads
     from host_memory_streamed_amd import synth
 
-    cfg = O.Config(1, w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn_dim, w.vocab)
+    Vs = max(2, w.vocab // vocab_share)
+    cfg = O.Config(1, w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn_dim, Vs)
     table = O.tensor_table(cfg)
     params = [synth.init_tensor(0, i, s, g) for i, (_, s, g) in enumerate(table)]
     P = [p.astype(np.float64) for p in params]
-    B, T = 1, budget_tokens
-    tokens, targets = synth.token_batch(0, B, T, w.vocab)
+    B, T = 1, w.seq
+    tokens, targets = synth.token_batch(0, B, T, Vs)
     prec = _Prec("bf16")
     rope = O.rope_tables(T, cfg.head_dim, cfg.rope_base)
     W = {n: P[1 + i] for i, n in enumerate(O.LAYER_TENSORS)}
@@ -188,7 +191,7 @@ def cpu_baseline(w, budget_tokens=512):
     t_fwd = time.perf_counter() - t0
     t0 = time.perf_counter()
     _, g, _, _ = O.head_fwd_bwd(y, P[-2], P[-1], targets.reshape(-1), cfg, prec)
-    t_head = time.perf_counter() - t0
+    t_head = (time.perf_counter() - t0) * (w.vocab / Vs)
     t0 = time.perf_counter()
     O.layer_bwd(g, cache, W, cfg, prec, rope, B, T)
     t_bwd = time.perf_counter() - t0
@@ -201,22 +204,27 @@ def cpu_baseline(w, budget_tokens=512):
     layer_params = sum(int(np.prod(s)) for _, s, _ in table[1:10])
     total_params = w.n_layers * layer_params + 2 * w.vocab * w.d_model + w.d_model
     step = w.n_layers * (t_fwd + t_bwd) + t_head + total_params * t_adam
+    blas = None
     try:
         import threadpoolctl
-        cores = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or os.cpu_count()
+        blas = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info())
     except Exception:
-        cores = os.cpu_count()
+        pass
+    heads = _threads()
     return {
         "value": round(B * T / step, 4),
         "unit": "tokens/s",
-        "cores": int(cores),
+        "cores": int(max(blas or 1, heads)),
         "kind": "oracle",
-        "sample": (f"float64 NumPy oracle, bf16 cast emulation, on 1x{T} tokens of the "
-                   f"{w.name} shape: one decoder layer forward ({t_fwd:.2f}s) and backward "
-                   f"({t_bwd:.2f}s), head forward+backward ({t_head:.2f}s), AdamW "
-                   f"{t_adam * 1e9:.2f} ns/param on 16M params; composed as "
-                   f"{w.n_layers} x (fwd + bwd) + head + AdamW over {total_params / 1e9:.2f}B params "
-                   f"= {step:.1f}s per {T}-token step"),
+        "os_cpu_count": os.cpu_count(),
+        "blas_threads": blas,
+        "attention_threads": heads,
+        "sample": (f"float64 NumPy oracle, bf16 cast emulation, on the {w.name} shape at its own "
+                   f"{B}x{T} tokens: one decoder layer forward ({t_fwd:.2f}s) and backward ({t_bwd:.2f}s); "
+                   f"the head forward+backward over {Vs} of the {w.vocab} vocabulary rows, scaled by "
+                   f"{w.vocab / Vs:.2f} to {t_head:.2f}s; AdamW {t_adam * 1e9:.2f} ns/param on 16M params; "
+                   f"composed as {w.n_layers} x (fwd + bwd) + head + AdamW over {total_params / 1e9:.2f}B "
+                   f"params = {step:.1f}s per {B * T}-token step"),
     }
 
 

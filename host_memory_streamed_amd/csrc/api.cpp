@@ -11,8 +11,10 @@
 // they are kept. Device memory holds only the layer buffers, two gradient
 // buffers, the residual checkpoints and one layer's activations: its size does
 // not grow with depth apart from the checkpoints.
+#include <chrono>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "kernels.h"
@@ -110,17 +112,26 @@ static std::vector<TensorRef> tensor_table(const Dims& D) {
 // unit. Overlapped updates fall behind during the backward and catch up in
 // the next forward: layer-sized slots for as many layers as fit in 16 GiB (3
 // to 16), plus one slot kept for the head (the last entry).
+// cfg.grad_ring_slots > 0 sets the count (of layer slots, with MT_OVERLAP_OPT).
 static std::vector<int64_t> ring_sizes(const mt_model_cfg& cfg, int64_t layer_n, int64_t head_n) {
   std::vector<int64_t> sizes;
+  const int k = cfg.grad_ring_slots;
   if (cfg.flags & MT_OVERLAP_OPT) {
-    const int r = (int)std::max<int64_t>(3, std::min<int64_t>(16, (16LL << 30) / (layer_n * 4)));
+    const int r = k > 0 ? k : (int)std::max<int64_t>(3, std::min<int64_t>(16, (16LL << 30) / (layer_n * 4)));
     sizes.assign(r, layer_n);
     sizes.push_back(head_n);
   } else {
-    sizes.assign(3, std::max(layer_n, head_n));
+    sizes.assign(k > 0 ? k : 3, std::max(layer_n, head_n));
   }
   return sizes;
 }
+
+// Gradients pass through the pinned staging slots unless they are kept in
+// fp32 host buffers as they come (MT_KEEP_GRADS without MT_BF16_GRADS).
+static bool staged_grads(const mt_model_cfg& c) {
+  return !(c.flags & MT_KEEP_GRADS) || (c.flags & MT_BF16_GRADS);
+}
+static int64_t grad_bytes(const mt_model_cfg& c) { return (c.flags & MT_BF16_GRADS) ? 2 : 4; }
 
 static int validate(const mt_model_cfg* c, std::string& why) {
   if (!c) { why = "cfg is NULL"; return MT_EINVAL; }
@@ -140,17 +151,45 @@ static int validate(const mt_model_cfg* c, std::string& why) {
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f) || !(c->lr >= 0.0) || !(c->beta1 >= 0.0 && c->beta1 < 1.0) ||
       !(c->beta2 >= 0.0 && c->beta2 < 1.0) || !(c->adam_eps >= 0.0))
     return bad("invalid eps / rope_base / AdamW hyperparameters");
-  if (c->flags & ~(MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE | MT_OVERLAP_OPT | MT_PROGRESS | MT_CACHE_NO_REFRESH))
+  if (c->flags & ~(MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE | MT_OVERLAP_OPT | MT_PROGRESS | MT_CACHE_NO_REFRESH |
+                   MT_BF16_GRADS))
     return bad("unknown flags");
   if (c->chunk_rows < 0) return bad("chunk_rows must be >= 0");
   if (c->ckpt_host < 0 || (c->ckpt_host > 0 && c->ckpt_host > c->n_layers - 2))
     return bad("ckpt_host must be 0 or in [1, n_layers - 2]");
+  if (c->grad_ring_slots < 0 || c->grad_ring_slots > 64) return bad("grad_ring_slots must be in [0, 64]");
+  if (c->wait_timeout_ms < 0) return bad("wait_timeout_ms must be >= 0");
+  if (c->micro_batches < 0 || c->micro_batches > c->max_batch) return bad("micro_batches must be in [0, max_batch]");
   return MT_OK;
 }
 
 void adam_drain(Ctx& c) {
   std::unique_lock<std::mutex> lk(c.amu);
   c.acv.wait(lk, [&] { return c.adam_pending == 0; });
+}
+
+int adam_drain_for(Ctx& c, int64_t ms, const char* what) {
+  if (ms <= 0) {
+    adam_drain(c);
+    return MT_OK;
+  }
+  std::string busy;
+  {
+    std::unique_lock<std::mutex> lk(c.amu);
+    if (c.acv.wait_for(lk, std::chrono::milliseconds(ms), [&] { return c.adam_pending == 0; })) return MT_OK;
+    const int L = c.D.L;
+    for (int u = 0; u < (int)c.unit_busy.size(); ++u)
+      if (c.unit_busy[u])
+        busy += (busy.empty() ? "" : ", ") +
+                (u < L ? "layer " + std::to_string(u) : u == L ? std::string("head") : std::string("embedding"));
+  }
+  return set_error(&c, MT_ETIMEOUT, std::string(what) + ": AdamW updates still running after " +
+                                        std::to_string(ms) + " ms (" + busy + ")");
+}
+
+static int64_t env_int(const char* name) {
+  const char* v = std::getenv(name);
+  return v ? std::max<int64_t>(0, std::strtoll(v, nullptr, 10)) : 0;
 }
 
 static void free_ctx(Ctx* c) {
@@ -252,8 +291,17 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
   }
   c.dev_current.assign(c.D.L + 1, 0);
   c.M_max = (int64_t)cfg->max_batch * cfg->max_seq;
+  {
+    const int k = std::max(1, cfg->micro_batches);
+    c.mb_seqs = (cfg->max_batch + k - 1) / k;
+    c.M_ws = (int64_t)c.mb_seqs * cfg->max_seq;
+  }
   c.tensors = tensor_table(c.D);
   c.pool = new Pool(default_threads(cfg->host_threads));
+  c.delay_h2d_us = env_int("MT_TEST_DELAY_H2D_US");
+  c.delay_d2h_us = env_int("MT_TEST_DELAY_D2H_US");
+  c.delay_adamw_us = env_int("MT_TEST_DELAY_ADAMW_US");
+  c.poison = env_int("MT_TEST_POISON") != 0;
   const Dims& D = c.D;
   const bool keep = cfg->flags & MT_KEEP_GRADS;
   const int S = c.dtype;
@@ -285,12 +333,13 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
       HIP_OR(hipHostMalloc(&u.shadow, u.lay.image_bytes(S), hipHostMallocDefault), MT_EHOSTOOM, "pinned shadow allocation");
   }
   int64_t max_unit = std::max(c.units[0].lay.n, c.units[D.L].lay.n);
-  if (!keep) {
+  if (staged_grads(*cfg)) {
     const std::vector<int64_t> sizes = ring_sizes(*cfg, c.units[0].lay.n, c.units[D.L].lay.n);
     if (cfg->flags & MT_OVERLAP_OPT) c.head_slot = (int)sizes.size() - 1;
     for (int64_t n : sizes) {
       float* p = nullptr;
-      HIP_OR(hipHostMalloc((void**)&p, (size_t)n * 4, hipHostMallocDefault), MT_EHOSTOOM, "pinned gradient ring");
+      HIP_OR(hipHostMalloc((void**)&p, (size_t)n * grad_bytes(*cfg), hipHostMallocDefault), MT_EHOSTOOM,
+             "pinned gradient ring");
       c.ring_slot.push_back(p);
       c.ring_elems.push_back(n);
     }
@@ -337,8 +386,14 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
   for (int i = 0; i < c.nbuf; ++i) ok &= dalloc(bsize[i], &c.buf[i]);
   ok &= dalloc((size_t)max_unit * 4, (void**)&c.gbuf[0]);
   ok &= dalloc((size_t)max_unit * 4, (void**)&c.gbuf[1]);
+  if (cfg->flags & MT_BF16_GRADS) {
+    ok &= dalloc((size_t)max_unit * 2, &c.gbuf16[0]);
+    ok &= dalloc((size_t)max_unit * 2, &c.gbuf16[1]);
+  }
   Workspace& w = c.ws;
-  const int64_t M = c.M_max, d = D.d, F = D.F, V = D.V;
+  // activations hold one micro-batch (M rows); the residual gradient, the
+  // per-token losses and the targets the whole batch (Mb rows)
+  const int64_t M = c.M_ws, Mb = c.M_max, d = D.d, F = D.F, V = D.V;
   const size_t es = S ? 2 : 4;
   // token chunk of the QKV projection and the MLP
   {
@@ -361,7 +416,7 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
   ok &= dalloc(Q * d * es, &w.h2);
   ok &= dalloc(Q * 2 * F * 4, (void**)&w.gu_f);
   ok &= dalloc(Q * F * es, &w.act);
-  ok &= dalloc(M * d * 4, (void**)&w.g_f);
+  ok &= dalloc(Mb * d * 4, (void**)&w.g_f);
   if (S) ok &= dalloc(M * d * es, &w.g_s); else w.g_s = w.g_f;
   ok &= dalloc(Q * F * 4, (void**)&w.dact_f);
   ok &= dalloc(Q * 2 * F * es, &w.dgu_s);
@@ -370,7 +425,7 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
   ok &= dalloc(M * std::max<int64_t>(d, D.qd) * 4, (void**)&w.dh_f);
   w.do_f = w.dh_f;
   ok &= dalloc(M * D.qkvd * es, &w.dqkv_s);
-  ok &= dalloc((size_t)mt_op_attn_bwd_ws_bytes(S, cfg->max_batch, cfg->max_seq, D.H, D.hd), &w.attn_ws);
+  ok &= dalloc((size_t)mt_op_attn_bwd_ws_bytes(S, c.mb_seqs, cfg->max_seq, D.H, D.hd), &w.attn_ws);
   ok &= dalloc((size_t)rmsnorm_bwd_partials(M) * d * 4, (void**)&w.rms_ws);
   ok &= dalloc((size_t)GEMM_WS_BYTES, &w.gemm_ws);
   w.hf = w.h;   // the head runs between the last forward and the first recompute
@@ -381,8 +436,8 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
   w.head_chunk = std::min(chunk, M);
   ok &= dalloc(w.head_chunk * V * 4, (void**)&w.logits);
   if (S) ok &= dalloc(w.head_chunk * V * es, &w.dz_s); else w.dz_s = w.logits;
-  ok &= dalloc(M * 4, (void**)&w.tok_loss);
-  ok &= dalloc(M * 4, (void**)&w.targets);
+  ok &= dalloc(Mb * 4, (void**)&w.tok_loss);
+  ok &= dalloc(Mb * 4, (void**)&w.targets);
   const int half = D.hd / 2;
   ok &= dalloc((size_t)cfg->max_seq * half * 4, (void**)&w.rope_cos);
   ok &= dalloc((size_t)cfg->max_seq * half * 4, (void**)&w.rope_sin);
@@ -390,7 +445,7 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
 
   // ---- residual checkpoints: device slots, parking the rest in host memory ----
   {
-    const size_t slot = (size_t)M * d * 4;
+    const size_t slot = (size_t)Mb * d * 4;
     int k = cfg->ckpt_host;
     if (k == 0) {
       size_t free_b = 0, total_b = 0;
@@ -477,8 +532,8 @@ int mt_host_bytes(const mt_model_cfg* cfg, int64_t* state_bytes, int64_t* pinned
   for (int l = 0; l < D.L; ++l) unit(ll, true);
   unit(hl, true);
   unit(el, false);
-  if (!keep)
-    for (int64_t n : ring_sizes(*cfg, ll.n, hl.n)) pinned += n * 4;
+  if (staged_grads(*cfg))
+    for (int64_t n : ring_sizes(*cfg, ll.n, hl.n)) pinned += n * grad_bytes(*cfg);
   pinned += 2 * M * D.d * 4 + 2 * M * 4;             // x0 / dx0, targets / losses staging
   if (state_bytes) *state_bytes = state;
   if (pinned_bytes) *pinned_bytes = pinned;
@@ -489,8 +544,7 @@ int mt_host_bytes(const mt_model_cfg* cfg, int64_t* state_bytes, int64_t* pinned
 
 int mt_sync(mt_ctx* h) {
   if (!h) return MT_EINVAL;
-  adam_drain(h->c);
-  return MT_OK;
+  return adam_drain_for(h->c, h->c.cfg.wait_timeout_ms, "mt_sync");
 }
 
 int mt_set_param(mt_ctx* h, int32_t id, const float* src) {
@@ -522,6 +576,7 @@ int mt_train_step(mt_ctx* h, const int32_t* tokens, const int32_t* targets, int3
                   float* loss_out) {
   if (!h) return MT_EINVAL;
   Ctx& c = h->c;
+  if (c.broken) return set_error(&c, MT_ESTATE, "an earlier step exceeded wait_timeout_ms; no further step runs");
   if (!tokens || !targets) return set_error(&c, MT_EINVAL, "NULL tokens or targets");
   if (B < 1 || T < 1 || B > c.cfg.max_batch || T > c.cfg.max_seq)
     return set_error(&c, MT_EINVAL, "B/T outside [1, max_batch] x [1, max_seq]");
@@ -601,10 +656,10 @@ int mt_trace_dump(mt_ctx* h, const char* path) {
   FILE* f = fopen(path, "w");
   if (!f) return set_error(&h->c, MT_EINVAL, std::string("cannot open ") + path);
   static const char* ph[] = {"load", "fwd", "head", "bwd", "grad", "adamw", "ckpt out", "ckpt in", "refresh"};
-  static const char* st[] = {"copy-in", "compute", "copy-out", "host AdamW"};
+  static const char* st[] = {"copy-in", "compute", "copy-out", "host AdamW", "host submit"};
   fprintf(f, "{\"traceEvents\":[\n");
   bool first = true;
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 5; ++i) {
     fprintf(f, "%s{\"name\":\"thread_name\",\"ph\":\"M\",\"pid\":0,\"tid\":%d,\"args\":{\"name\":\"%s\"}}",
             first ? "" : ",\n", i, st[i]);
     first = false;

@@ -129,10 +129,27 @@ static inline uint16_t bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-static inline void adamw_scalar(float* p, float* m, float* v, const float* g, int64_t i0,
-                                int64_t i1, const AdamConst& k, uint16_t* bo, float* fo) {
+static inline float bf16_to_f32(uint16_t h) {
+  const uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// Gradients as fp32 (G16 false) or as bf16 bit patterns (G16 true, widened
+// exactly; with g32 the widened values are also written out).
+template <bool G16>
+static inline float grad_at(const void* g, int64_t i) {
+  if constexpr (G16) return bf16_to_f32(static_cast<const uint16_t*>(g)[i]);
+  else return static_cast<const float*>(g)[i];
+}
+
+template <bool G16>
+static inline void adamw_scalar(float* p, float* m, float* v, const void* g, int64_t i0, int64_t i1,
+                                const AdamConst& k, uint16_t* bo, float* fo, float* g32) {
   for (int64_t i = i0; i < i1; ++i) {
-    const float gi = g[i];
+    const float gi = grad_at<G16>(g, i);
+    if (g32) g32[i] = gi;
     float pi = p[i] * k.decay;
     const float mi = m[i] * k.b1 + k.omb1 * gi;
     const float vi = v[i] * k.b2 + k.omb2 * gi * gi;
@@ -145,9 +162,10 @@ static inline void adamw_scalar(float* p, float* m, float* v, const float* g, in
   }
 }
 
+template <bool G16>
 __attribute__((target("avx512f,avx512bw,avx512vl"))) static void adamw_avx512(
-    float* p, float* m, float* v, const float* g, int64_t n, const AdamConst& k, uint16_t* bo,
-    float* fo) {
+    float* p, float* m, float* v, const void* g, int64_t n, const AdamConst& k, uint16_t* bo, float* fo,
+    float* g32) {
   const __m512 decay = _mm512_set1_ps(k.decay), b1 = _mm512_set1_ps(k.b1),
                omb1 = _mm512_set1_ps(k.omb1), b2 = _mm512_set1_ps(k.b2),
                omb2 = _mm512_set1_ps(k.omb2), ss = _mm512_set1_ps(k.step_size),
@@ -159,10 +177,17 @@ __attribute__((target("avx512f,avx512bw,avx512vl"))) static void adamw_avx512(
   int64_t i = 0;
   if (bo) {
     while (i < n && (reinterpret_cast<uintptr_t>(bo + i) & 31)) ++i;
-    adamw_scalar(p, m, v, g, 0, i, k, bo, fo);
+    adamw_scalar<G16>(p, m, v, g, 0, i, k, bo, fo, g32);
   }
   for (; i + 16 <= n; i += 16) {
-    const __m512 gi = _mm512_loadu_ps(g + i);
+    __m512 gi;
+    if constexpr (G16) {
+      const __m256i h = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(static_cast<const uint16_t*>(g) + i));
+      gi = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(h), 16));
+      if (g32) _mm512_storeu_ps(g32 + i, gi);
+    } else {
+      gi = _mm512_loadu_ps(static_cast<const float*>(g) + i);
+    }
     __m512 pi = _mm512_mul_ps(_mm512_loadu_ps(p + i), decay);
     const __m512 mi = _mm512_add_ps(_mm512_mul_ps(_mm512_loadu_ps(m + i), b1), _mm512_mul_ps(omb1, gi));
     const __m512 vi = _mm512_add_ps(_mm512_mul_ps(_mm512_loadu_ps(v + i), b2),
@@ -180,20 +205,32 @@ __attribute__((target("avx512f,avx512bw,avx512vl"))) static void adamw_avx512(
     }
     if (fo) _mm512_storeu_ps(fo + i, pi);
   }
-  adamw_scalar(p, m, v, g, i, n, k, bo, fo);
+  adamw_scalar<G16>(p, m, v, g, i, n, k, bo, fo, g32);
   // streaming stores are weakly ordered: make them visible before the caller
   // reports the range done
   if (bo) _mm_sfence();
 }
 
+static bool have_avx512() {
+  static const bool a = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+                        __builtin_cpu_supports("avx512vl");
+  return a;
+}
+
 void adamw_range(float* p, float* m, float* v, const float* g, int64_t n, const AdamConst& k,
                  uint16_t* bo, float* fo) {
-  static const bool avx512 = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
-                             __builtin_cpu_supports("avx512vl");
-  if (avx512)
-    adamw_avx512(p, m, v, g, n, k, bo, fo);
+  if (have_avx512())
+    adamw_avx512<false>(p, m, v, g, n, k, bo, fo, nullptr);
   else
-    adamw_scalar(p, m, v, g, 0, n, k, bo, fo);
+    adamw_scalar<false>(p, m, v, g, 0, n, k, bo, fo, nullptr);
+}
+
+void adamw_range_g16(float* p, float* m, float* v, const uint16_t* g, int64_t n, const AdamConst& k,
+                     uint16_t* bo, float* fo, float* g32) {
+  if (have_avx512())
+    adamw_avx512<true>(p, m, v, g, n, k, bo, fo, g32);
+  else
+    adamw_scalar<true>(p, m, v, g, 0, n, k, bo, fo, g32);
 }
 
 void to_bf16_range(const float* x, uint16_t* y, int64_t n) {
@@ -235,6 +272,28 @@ extern "C" int mt_adamw_host(float* p, float* m, float* v, const float* g, int64
   pool.run(nch, [&](int64_t i) {
     const int64_t a = i * chunk, b = std::min(n, a + chunk);
     adamw_range(p + a, m + a, v + a, g + a, b - a, k, bf16_out ? bf16_out + a : nullptr, nullptr);
+  });
+  return MT_OK;
+}
+
+extern "C" int mt_adamw_host_g16(float* p, float* m, float* v, const uint16_t* g16, float* g32_out, int64_t n,
+                                 int64_t t, double lr, double beta1, double beta2, double eps,
+                                 double weight_decay, uint16_t* bf16_out, int32_t threads) {
+  if (!p || !m || !v || !g16 || n < 0 || t < 1) return MT_EINVAL;
+  mt_model_cfg c{};
+  c.lr = lr;
+  c.beta1 = beta1;
+  c.beta2 = beta2;
+  c.adam_eps = eps;
+  c.weight_decay = weight_decay;
+  const AdamConst k = adam_const(c, t);
+  const int64_t chunk = 1 << 18;
+  const int64_t nch = (n + chunk - 1) / chunk;
+  Pool pool(default_threads(threads));
+  pool.run(nch, [&](int64_t i) {
+    const int64_t a = i * chunk, b = std::min(n, a + chunk);
+    adamw_range_g16(p + a, m + a, v + a, g16 + a, b - a, k, bf16_out ? bf16_out + a : nullptr, nullptr,
+                    g32_out ? g32_out + a : nullptr);
   });
   return MT_OK;
 }

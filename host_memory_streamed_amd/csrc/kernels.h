@@ -48,9 +48,10 @@ hipError_t attn_bwd(int dtype, const void* qkv, const float* o, const float* dou
 int rmsnorm_bwd_partials(int64_t rows);
 hipError_t rmsnorm_fwd(int out_dtype, const float* x, const float* w, void* y, float* rstd,
                        int64_t rows, int d, float eps, hipStream_t s);
+// dx written (accumulate 0) or added to; dw written (dw_accumulate 0) or added to
 hipError_t rmsnorm_bwd(const float* x, const float* w, const float* rstd, const float* dy,
                        float* dx, int accumulate, float* dw, float* ws, int64_t rows, int d,
-                       hipStream_t s);
+                       hipStream_t s, int dw_accumulate = 0);
 // rows [row0, row0 + rows) of the token sequence (positions (row0 + i) % T);
 // `in` and `out` point at the first of those rows
 hipError_t rope(int out_dtype, int backward, const float* in, void* out, const float* cos,

@@ -105,12 +105,12 @@ static int mlp_front(Ctx& c, const LayerPtrs& W, int64_t r0, int64_t mc) {
   return MT_OK;
 }
 
-int layer_forward(Ctx& c, const LayerPtrs& W, int l, int B, int T, bool recompute) {
+int layer_forward(Ctx& c, const LayerPtrs& W, int l, int B, int T, bool recompute, int64_t row0) {
   const Dims& D = c.D;
   const int S = c.dtype;
   Workspace& w = c.ws;
   const int64_t M = (int64_t)B * T, d = D.d, F = D.F;
-  const float* x = c.ckpt_dev(l);
+  const float* x = c.ckpt_dev(l) + row0 * d;
   const float eps = c.cfg.rms_eps;
   const double attn_fl = 2.0 * B * (double)T * T * D.H * D.hd;
 
@@ -123,7 +123,7 @@ int layer_forward(Ctx& c, const LayerPtrs& W, int l, int B, int T, bool recomput
       gemm_ws(S, MT_GEMM_NT, w.o_s, D.qd, W.wo, D.qd, w.x1, d, x, d, M, d, D.qd, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
   // the recompute stops here: the backward rebuilds the MLP chunk by chunk
   if (recompute) return MT_OK;
-  float* xn = c.ckpt_dev(l + 1);
+  float* xn = c.ckpt_dev(l + 1) + row0 * d;
   for (int64_t r0 = 0; r0 < M; r0 += w.chunk) {
     const int64_t mc = std::min(w.chunk, M - r0);
     if ((rc = mlp_front(c, W, r0, mc))) return rc;
@@ -133,27 +133,33 @@ int layer_forward(Ctx& c, const LayerPtrs& W, int l, int B, int T, bool recomput
   return MT_OK;
 }
 
-int layer_backward(Ctx& c, const LayerPtrs& W, int l, int B, int T, float* gu) {
-  // gu: this unit's gradient slab on the device (master unit layout)
+int layer_backward(Ctx& c, const LayerPtrs& W, int l, int B, int T, float* gu, int64_t row0, bool first) {
+  // gu: this unit's gradient slab on the device (master unit layout); rows
+  // [row0, row0 + B T) of the step's batch; the weight gradients are written
+  // (first) or added to those of the earlier micro-batches
   const Dims& D = c.D;
   const int S = c.dtype;
   Workspace& w = c.ws;
   const UnitLayout& U = c.units[0].lay;
   const int64_t M = (int64_t)B * T, d = D.d, F = D.F, qd = D.qd, qkvd = D.qkvd;
-  const float* x = c.ckpt_dev(l);
+  const float* x = c.ckpt_dev(l) + row0 * d;
+  float* gf = w.g_f + row0 * d;   // the residual gradient of these rows
+  // its matrix-product operand: the bf16 cast, or (fp32 mode) itself
+  void* gsb = S ? w.g_s : (void*)gf;
   const double attn_fl = 2.0 * B * (double)T * T * D.H * D.hd;
+  const float* acc_w = first ? nullptr : gu;   // base of the slab to add to, or none
 
-  int rc = layer_forward(c, W, l, B, T, true);
+  int rc = layer_forward(c, W, l, B, T, true, row0);
   if (rc) return rc;
 
   // MLP, chunk by chunk: recompute h2, gu, act; then
   // down: x_{l+1} = x1 + act Wd^T;  gate/up: gu = h2 Wgu^T.
   // The weight gradients accumulate over the chunks in chunk order.
-  if (S) RUN(K_CAST, 0, (double)M * d * 6, cast(S, w.g_f, w.g_s, M * d, c.s_comp));
+  if (S) RUN(K_CAST, 0, (double)M * d * 6, cast(S, gf, w.g_s, M * d, c.s_comp));
   for (int64_t r0 = 0; r0 < M; r0 += w.chunk) {
     const int64_t mc = std::min(w.chunk, M - r0);
-    const bool acc = r0 > 0;
-    const void* gs = static_cast<const char*>(w.g_s) + r0 * d * esz(S);
+    const bool acc = r0 > 0 || !first;
+    const void* gs = static_cast<const char*>(gsb) + r0 * d * esz(S);
     if ((rc = mlp_front(c, W, r0, mc))) return rc;
     RUN(K_GEMM_NN, 2.0 * mc * F * d, gemm_bytes(mc, F, d, S, false),
         gemm_ws(S, MT_GEMM_NN, gs, d, W.wdown, F, w.dact_f, F, nullptr, 0, mc, F, d, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
@@ -168,13 +174,14 @@ int layer_backward(Ctx& c, const LayerPtrs& W, int l, int B, int T, float* gu) {
                 d, mc, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
   }
   RUN(K_RMS_BWD, 0, (double)M * d * 20,
-      rmsnorm_bwd(w.x1, W.mlp_norm, w.rstd2, w.dh_f, w.g_f, 1, gu + U.off[1], w.rms_ws, M, D.d, c.s_comp));
+      rmsnorm_bwd(w.x1, W.mlp_norm, w.rstd2, w.dh_f, gf, 1, gu + U.off[1], w.rms_ws, M, D.d, c.s_comp, !first));
   // out projection: x1 = x + o Wo^T
-  if (S) RUN(K_CAST, 0, (double)M * d * 6, cast(S, w.g_f, w.g_s, M * d, c.s_comp));
+  if (S) RUN(K_CAST, 0, (double)M * d * 6, cast(S, gf, w.g_s, M * d, c.s_comp));
   RUN(K_GEMM_NN, 2.0 * M * qd * d, gemm_bytes(M, qd, d, S, false),
-      gemm_ws(S, MT_GEMM_NN, w.g_s, d, W.wo, qd, w.do_f, qd, nullptr, 0, M, qd, d, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
-  RUN(K_GEMM_TN, 2.0 * d * qd * M, gemm_bytes(d, qd, M, S, false),
-      gemm_ws(S, MT_GEMM_TN, w.g_s, d, w.o_s, qd, gu + U.off[3], qd, nullptr, 0, d, qd, M, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
+      gemm_ws(S, MT_GEMM_NN, gsb, d, W.wo, qd, w.do_f, qd, nullptr, 0, M, qd, d, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
+  RUN(K_GEMM_TN, 2.0 * d * qd * M, gemm_bytes(d, qd, M, S, !first),
+      gemm_ws(S, MT_GEMM_TN, gsb, d, w.o_s, qd, gu + U.off[3], qd, acc_w ? acc_w + U.off[3] : nullptr, qd, d, qd,
+              M, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
   // attention, with the rotation's backward applied as the gradients are written
   RUN(K_ATTN_BWD, 2.5 * attn_fl, (double)M * qkvd * 2 * esz(S) + (double)M * qd * 8,
       attn_bwd(S, w.qkv_s, w.o_f, w.do_f, w.lse, w.dqkv_s, S, w.rope_cos, w.rope_sin, w.attn_ws, B, T, D.H,
@@ -182,14 +189,18 @@ int layer_backward(Ctx& c, const LayerPtrs& W, int l, int B, int T, float* gu) {
   // qkv projection
   RUN(K_GEMM_NN, 2.0 * M * d * qkvd, gemm_bytes(M, d, qkvd, S, false),
       gemm_ws(S, MT_GEMM_NN, w.dqkv_s, qkvd, W.wqkv, d, w.dh_f, d, nullptr, 0, M, d, qkvd, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
-  RUN(K_GEMM_TN, 2.0 * qkvd * d * M, gemm_bytes(qkvd, d, M, S, false),
-      gemm_ws(S, MT_GEMM_TN, w.dqkv_s, qkvd, w.h, d, gu + U.off[2], d, nullptr, 0, qkvd, d, M, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
+  RUN(K_GEMM_TN, 2.0 * qkvd * d * M, gemm_bytes(qkvd, d, M, S, !first),
+      gemm_ws(S, MT_GEMM_TN, w.dqkv_s, qkvd, w.h, d, gu + U.off[2], d, acc_w ? acc_w + U.off[2] : nullptr, d, qkvd,
+              d, M, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
   RUN(K_RMS_BWD, 0, (double)M * d * 20,
-      rmsnorm_bwd(x, W.attn_norm, w.rstd1, w.dh_f, w.g_f, 1, gu + U.off[0], w.rms_ws, M, D.d, c.s_comp));
+      rmsnorm_bwd(x, W.attn_norm, w.rstd1, w.dh_f, gf, 1, gu + U.off[0], w.rms_ws, M, D.d, c.s_comp, !first));
   return MT_OK;
 }
 
-int head_forward_backward(Ctx& c, const void* image, int B, int T, float* gu) {
+int head_forward_backward(Ctx& c, const void* image, int B, int T, float* gu, int64_t row0, bool first,
+                          int64_t M_step) {
+  // rows [row0, row0 + B T) of a step of M_step tokens (the loss is the mean
+  // over all of them); the head's gradients are written (first) or added to
   const Dims& D = c.D;
   const int S = c.dtype;
   Workspace& w = c.ws;
@@ -198,25 +209,27 @@ int head_forward_backward(Ctx& c, const void* image, int B, int T, float* gu) {
   const char* base = static_cast<const char*>(image);
   const float* w_norm = reinterpret_cast<const float*>(base + U.image_offset(U.off[0], S));
   const void* w_head = base + U.image_offset(U.off[1], S);
-  const float* x = c.ckpt_dev(D.L);
+  const float* x = c.ckpt_dev(D.L) + row0 * d;
   float* d_head = gu + U.off[1];
 
   RUN(K_RMS_FWD, 0, (double)M * d * (4 + esz(S)), rmsnorm_fwd(S, x, w_norm, w.hf, w.rstdf, M, D.d, c.cfg.rms_eps, c.s_comp));
-  const float scale = 1.f / (float)M;
+  const float scale = 1.f / (float)M_step;
   for (int64_t r0 = 0; r0 < M; r0 += w.head_chunk) {
     const int64_t mc = std::min(w.head_chunk, M - r0);
+    const bool acc = r0 > 0 || !first;
     const void* hf = static_cast<const char*>(w.hf) + r0 * d * esz(S);
     RUN(K_GEMM_NT, 2.0 * mc * V * d, gemm_bytes(mc, V, d, S, false),
         gemm_ws(S, MT_GEMM_NT, hf, d, w_head, d, w.logits, V, nullptr, 0, mc, V, d, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
     RUN(K_XENT, 0, (double)mc * V * (4 + esz(S)),
-        xent(S, w.logits, w.targets + r0, w.tok_loss + r0, w.dz_s, mc, (int)V, scale, c.s_comp));
-    RUN(K_GEMM_TN, 2.0 * V * d * mc, gemm_bytes(V, d, mc, S, r0 > 0),
-        gemm_ws(S, MT_GEMM_TN, w.dz_s, V, hf, d, d_head, d, r0 > 0 ? d_head : nullptr, d, V, d, mc, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
+        xent(S, w.logits, w.targets + row0 + r0, w.tok_loss + row0 + r0, w.dz_s, mc, (int)V, scale, c.s_comp));
+    RUN(K_GEMM_TN, 2.0 * V * d * mc, gemm_bytes(V, d, mc, S, acc),
+        gemm_ws(S, MT_GEMM_TN, w.dz_s, V, hf, d, d_head, d, acc ? d_head : nullptr, d, V, d, mc, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
     RUN(K_GEMM_NN, 2.0 * mc * d * V, gemm_bytes(mc, d, V, S, false),
         gemm_ws(S, MT_GEMM_NN, w.dz_s, V, w_head, d, w.dh_f + r0 * d, d, nullptr, 0, mc, d, V, w.gemm_ws, GEMM_WS_BYTES, c.s_comp));
   }
   RUN(K_RMS_BWD, 0, (double)M * d * 20,
-      rmsnorm_bwd(x, w_norm, w.rstdf, w.dh_f, w.g_f, 0, gu + U.off[0], w.rms_ws, M, D.d, c.s_comp));
+      rmsnorm_bwd(x, w_norm, w.rstdf, w.dh_f, w.g_f + row0 * d, 0, gu + U.off[0], w.rms_ws, M, D.d, c.s_comp,
+                  !first));
   return MT_OK;
 }
 

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restric
 // p = lane, lane + 16, ... in order, and the 16 lane sums are added in lane
 // order. Reads are 256-byte coalesced rows; d % 4 == 0.
 __global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restrict__ ws, float* __restrict__ dw,
-                                                          int nparts, int d) {
+                                                          int nparts, int d, int acc) {
   __shared__ floatx4 part[16][16];
   const int cg = threadIdx.x & 15, pl = threadIdx.x >> 4;
   const int c = blockIdx.x * 64 + cg * 4;
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restric
 #pragma unroll
     for (int q = 1; q < 16; ++q) t += part[q][cg];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dw[c + e] = t[e];   // dw needs no alignment
+    for (int e = 0; e < 4; ++e) dw[c + e] = acc ? dw[c + e] + t[e] : t[e];   // dw needs no alignment
   }
 }
 
@@ -407,7 +407,7 @@ hipError_t rmsnorm_fwd(int out_dtype, const float* x, const float* w, void* y, f
 
 hipError_t rmsnorm_bwd(const float* x, const float* w, const float* rstd, const float* dy,
                        float* dx, int accumulate, float* dw, float* ws, int64_t rows, int d,
-                       hipStream_t s) {
+                       hipStream_t s, int dw_accumulate) {
   const int parts = rmsnorm_bwd_partials(rows);
   const int64_t rpb = (rows + parts - 1) / parts;
   if (rows > 0) {
@@ -418,7 +418,7 @@ hipError_t rmsnorm_bwd(const float* x, const float* w, const float* rstd, const 
   }
   // with no rows the reduction over zero partials writes dw = 0
   const int used = rows > 0 ? (int)((rows + rpb - 1) / rpb) : 0;
-  hipLaunchKernelGGL(reduce_rows_kernel, dim3((d + 63) / 64), dim3(256), 0, s, ws, dw, used, d);
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3((d + 63) / 64), dim3(256), 0, s, ws, dw, used, d, dw_accumulate);
   return hipGetLastError();
 }
 

@@ -180,6 +180,11 @@ struct Ctx {
   // (cached units only; cleared when an update or mt_set_param changes it)
   std::vector<char> dev_current;
   int64_t M_max;
+  // sequences per micro-batch (cfg.micro_batches): the layer template runs a
+  // step's batch in pieces of at most mb_seqs sequences; the workspace holds
+  // one piece (M_ws = mb_seqs * max_seq token rows)
+  int mb_seqs = 0;
+  int64_t M_ws = 0;
   std::string err;
 
   std::vector<Unit> units;   // [0, L) layers, L head, L+1 embedding
@@ -188,8 +193,9 @@ struct Ctx {
   Unit& emb() { return units[D.L + 1]; }
   std::vector<TensorRef> tensors;
 
-  // Gradient staging (MT_KEEP_GRADS off): slots of ring_elems[i] floats. A
-  // slot is busy from its D2H until the AdamW that reads it has finished.
+  // Gradient staging (MT_KEEP_GRADS off, or MT_BF16_GRADS): slots of
+  // ring_elems[i] gradients (fp32, or bf16 with MT_BF16_GRADS). A slot is
+  // busy from its D2H until the AdamW that reads it has finished.
   std::vector<float*> ring_slot;
   std::vector<int64_t> ring_elems;
   int head_slot = -1;              // slot reserved for the head (-1: any slot fits it)
@@ -232,6 +238,7 @@ struct Ctx {
   // device
   std::vector<void*> buf;        // layer buffers
   float* gbuf[2] = {nullptr, nullptr};
+  void* gbuf16[2] = {nullptr, nullptr};   // MT_BF16_GRADS: the bf16 copy that crosses the link
   float* ckpt = nullptr;         // device slots for x_{ck_nh}..x_L
   Workspace ws;
   std::vector<void*> dev_allocs;
@@ -242,6 +249,17 @@ struct Ctx {
 
   Pool* pool = nullptr;
   int64_t step = 0;
+  // Set when a step exceeded cfg.wait_timeout_ms: no further step runs.
+  bool broken = false;
+  // Schedule test hooks, read from the environment at creation (results must
+  // not depend on them): host delays before each layer-image load
+  // (MT_TEST_DELAY_H2D_US), before each gradient copy (MT_TEST_DELAY_D2H_US)
+  // and at the start of each unit's AdamW (MT_TEST_DELAY_ADAMW_US); and
+  // MT_TEST_POISON=1, which fills every tensor of a layer buffer with NaN
+  // before it is loaded and of a gradient buffer after its copy has left, so
+  // that a read of a released buffer shows up in the results.
+  int64_t delay_h2d_us = 0, delay_d2h_us = 0, delay_adamw_us = 0;
+  bool poison = false;
   mt_step_stats stats{};
   KTiming kt;
   std::vector<mt_kernel_stat> kstats;
@@ -253,6 +271,9 @@ struct Ctx {
 int set_error(Ctx* c, int code, const std::string& msg);
 // Wait until every submitted AdamW job has finished.
 void adam_drain(Ctx& c);
+// As adam_drain, for at most ms milliseconds (ms <= 0: no limit); MT_ETIMEOUT
+// (with an error naming the units still updating) if they have not finished.
+int adam_drain_for(Ctx& c, int64_t ms, const char* what);
 void* host_alloc_plain(size_t bytes);
 void host_free_plain(void* p, size_t bytes);
 
@@ -263,6 +284,10 @@ AdamConst adam_const(const mt_model_cfg& c, int64_t t);
 // p, m, v, g over [0, n); optional outputs: bf16 image and/or fp32 copy of p.
 void adamw_range(float* p, float* m, float* v, const float* g, int64_t n, const AdamConst& k,
                  uint16_t* bf16_out, float* f32_out);
+// As adamw_range with the gradient given as bf16 (widened exactly); g32, if
+// not NULL, receives the widened gradient.
+void adamw_range_g16(float* p, float* m, float* v, const uint16_t* g, int64_t n, const AdamConst& k,
+                     uint16_t* bf16_out, float* f32_out, float* g32);
 void to_bf16_range(const float* x, uint16_t* y, int64_t n);
 
 // Layer template (layer.cpp)
@@ -275,9 +300,11 @@ struct LayerPtrs {
   const void* wdown;
 };
 LayerPtrs bind_layer(const Ctx& c, const void* image);
-int layer_forward(Ctx& c, const LayerPtrs& W, int l, int B, int T, bool recompute);
-int layer_backward(Ctx& c, const LayerPtrs& W, int l, int B, int T, float* grad_unit);
-int head_forward_backward(Ctx& c, const void* image, int B, int T, float* grad_unit);
+// B sequences starting at token row row0 of the step's batch (one micro-batch)
+int layer_forward(Ctx& c, const LayerPtrs& W, int l, int B, int T, bool recompute, int64_t row0);
+int layer_backward(Ctx& c, const LayerPtrs& W, int l, int B, int T, float* grad_unit, int64_t row0, bool first);
+int head_forward_backward(Ctx& c, const void* image, int B, int T, float* grad_unit, int64_t row0, bool first,
+                          int64_t M_step);
 
 // kernel-timing wrapper: run fn on the compute stream, bracketed by events
 int timed(Ctx& c, int cls, double flops, double bytes, const std::function<hipError_t()>& fn);

@@ -156,8 +156,8 @@ void destroy_step_events(StepEvents* e) {
 // fp32 gains + bf16 matrices). `uidx` is the unit's index in Ctx::units; the
 // unit counts as busy until the job has finished, and the gradient staging
 // slot `slot` (or -1) is released then.
-static void submit_adamw(Ctx& c, int uidx, const float* g, std::vector<std::pair<int64_t, int64_t>> ranges,
-                         const AdamConst& k, int slot, int64_t priority) {
+static void submit_adamw(Ctx& c, int uidx, const void* g, std::vector<std::pair<int64_t, int64_t>> ranges,
+                         const AdamConst& k, int slot, int64_t priority, bool g16 = false, float* g32 = nullptr) {
   constexpr int64_t CH = 1 << 20;
   Unit& u = c.units[uidx];
   auto chunks = std::make_shared<std::vector<std::pair<int64_t, int64_t>>>();
@@ -172,21 +172,29 @@ static void submit_adamw(Ctx& c, int uidx, const float* g, std::vector<std::pair
   Ctx* cp = &c;
   c.pool->submit(
       (int64_t)chunks->size(),
-      [&u, g, chunks, k, dt, cp](int64_t i) {
+      [&u, g, chunks, k, dt, cp, g16, g32](int64_t i) {
+        if (i == 0 && cp->delay_adamw_us) std::this_thread::sleep_for(std::chrono::microseconds(cp->delay_adamw_us));
         const auto t0 = std::chrono::steady_clock::now();
         const int64_t a = (*chunks)[i].first, b = (*chunks)[i].second;
         const int64_t mb = u.lay.mat_base;
+        // g: fp32, or bf16 widened on the fly (written out to g32 if given)
+        auto update = [&](int64_t x, int64_t n, uint16_t* bo, float* f32) {
+          if (g16)
+            adamw_range_g16(u.p + x, u.m + x, u.v + x, static_cast<const uint16_t*>(g) + x, n, k, bo, f32,
+                            g32 ? g32 + x : nullptr);
+          else
+            adamw_range(u.p + x, u.m + x, u.v + x, static_cast<const float*>(g) + x, n, k, bo, f32);
+        };
         if (a < mb) {   // gains region: fp32 in the image
           const int64_t e = std::min(b, mb);
-          float* f32 = (dt && u.shadow) ? static_cast<float*>(u.shadow) + a : nullptr;
-          adamw_range(u.p + a, u.m + a, u.v + a, g + a, e - a, k, nullptr, f32);
+          update(a, e - a, nullptr, (dt && u.shadow) ? static_cast<float*>(u.shadow) + a : nullptr);
         }
         if (b > mb) {   // matrices: bf16 in the image (bf16 mode)
           const int64_t s = std::max(a, mb);
-          uint16_t* bo = (dt && u.shadow)
-                             ? reinterpret_cast<uint16_t*>(static_cast<char*>(u.shadow) + mb * 4) + (s - mb)
-                             : nullptr;
-          adamw_range(u.p + s, u.m + s, u.v + s, g + s, b - s, k, bo, nullptr);
+          update(s, b - s,
+                 (dt && u.shadow) ? reinterpret_cast<uint16_t*>(static_cast<char*>(u.shadow) + mb * 4) + (s - mb)
+                                  : nullptr,
+                 nullptr);
         }
         cp->adam_ns.fetch_add((int64_t)(std::chrono::duration<double, std::nano>(
                                             std::chrono::steady_clock::now() - t0).count()));
@@ -214,6 +222,10 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
   const bool trace = (c.cfg.flags & MT_TRACE) != 0;
   const bool keep = (c.cfg.flags & MT_KEEP_GRADS) != 0;
   const bool overlap = (c.cfg.flags & MT_OVERLAP_OPT) != 0;
+  // bf16 gradients cross the link; they (and unkept fp32 ones) go through the staging slots
+  const bool g16 = (c.cfg.flags & MT_BF16_GRADS) != 0;
+  const bool staged = !keep || g16;
+  const size_t gbytes = g16 ? 2 : 4;
   c.kt.on = (c.cfg.flags & MT_KERNEL_TIMING) != 0;
   c.kt.used = 0;
   c.kt.recs.clear();
@@ -225,9 +237,18 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
 
   // ---- inputs: targets and the embedding gather x0 = E[tokens] (host) ----
   // (an overlapped update of the embedding from the last step lands first)
+  const int64_t limit_ms = c.cfg.wait_timeout_ms;
   {
     std::unique_lock<std::mutex> lk(c.amu);
-    c.acv.wait(lk, [&] { return c.unit_busy[L + 1] == 0; });
+    auto idle = [&] { return c.unit_busy[L + 1] == 0; };
+    if (limit_ms <= 0) {
+      c.acv.wait(lk, idle);
+    } else if (!c.acv.wait_for(lk, std::chrono::milliseconds(limit_ms), idle)) {
+      lk.unlock();
+      c.broken = true;
+      return set_error(&c, MT_ETIMEOUT, "waited more than " + std::to_string(limit_ms) +
+                                            " ms for the previous step's AdamW update of the embedding");
+    }
   }
   std::memcpy(c.tgt_host, targets, (size_t)M * 4);
   Unit& emb = c.emb();
@@ -268,7 +289,7 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
   auto grad_uidx = [&](int kk) { return kk == 0 ? L : L - kk; };
   auto grad_unit = [&](int kk) -> Unit& { return c.units[grad_uidx(kk)]; };
   std::vector<int> slot_of(L + 1, -1);
-  auto grad_dest = [&](int kk) -> float* { return keep ? grad_unit(kk).g : c.ring_slot[slot_of[kk]]; };
+  auto grad_dest = [&](int kk) -> void* { return staged ? (void*)c.ring_slot[slot_of[kk]] : (void*)grad_unit(kk).g; };
   auto unit_id = [&](const Item& it) { return it.phase == PH_HEAD ? MT_UNIT_HEAD : it.unit; };
   // AdamW order: synchronous updates in arrival order (embedding's untouched
   // rows first); overlapped updates in the order the next forward needs them
@@ -400,10 +421,30 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
   auto fwd_needs_save = [&](int l) { return nh && l + 1 < nh && l - 1 >= 1 && l - 1 <= kpark; };
   auto bwd_needs_reload = [&](int l) { return nh && l <= kpark; };
 
+  // test hook: NaN over every tensor of a unit-layout buffer (an image, or a
+  // gradient slab with elem_bytes 4), leaving the alignment padding alone
+  auto poison_unit = [&](void* base, const UnitLayout& lay, int unit, int image_dtype,
+                         hipStream_t s) -> int {
+    const int64_t dd = d, n_groups = unit == L ? 2 : 6;
+    const int64_t len_layer[6] = {dd, dd, (int64_t)D.qkvd * dd, dd * D.qd, 2LL * D.F * dd, dd * D.F};
+    const int64_t len_head[2] = {dd, (int64_t)D.V * dd};
+    for (int64_t gi = 0; gi < n_groups; ++gi) {
+      const int64_t e0 = lay.off[gi], n = unit == L ? len_head[gi] : len_layer[gi];
+      const size_t b0 = image_dtype < 0 ? (size_t)e0 * 4 : lay.image_offset(e0, image_dtype);
+      const size_t b1 = image_dtype < 0 ? (size_t)(e0 + n) * 4 : lay.image_offset(e0 + n, image_dtype);
+      HIPCK(hipMemsetAsync(static_cast<char*>(base) + b0, 0xFF, b1 - b0, s));
+    }
+    return MT_OK;
+  };
   auto issue_load = [&](int j) -> int {
     const Item& it = items[j];
     const Unit& u = it.phase == PH_HEAD ? c.head() : c.layer(it.unit);
     const size_t bytes = u.lay.image_bytes(c.dtype);
+    if (c.delay_h2d_us) std::this_thread::sleep_for(std::chrono::microseconds(c.delay_h2d_us));
+    if (c.poison) {
+      const int rp = poison_unit(c.buf[it.buf], u.lay, it.phase == PH_HEAD ? L : it.unit, c.dtype, c.s_in);
+      if (rp) return rp;
+    }
     if (trace) HIPCK(hipEventRecord(trace_ev(j, 0), c.s_in));
     const auto hq = std::chrono::steady_clock::now();
     HIPCK(hipMemcpyAsync(c.buf[it.buf], u.image(), bytes, hipMemcpyHostToDevice, c.s_in));
@@ -446,14 +487,27 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
     if (trace) HIPCK(hipEventRecord(trace_ev(i, 2), c.s_comp));
     float* gdev = it.grad_k >= 0 ? c.gbuf[it.grad_k % 2] : nullptr;
     const auto hc = std::chrono::steady_clock::now();
-    int r;
-    if (it.phase == PH_FWD)
-      r = layer_forward(c, bind_layer(c, c.buf[it.buf]), it.unit, B, T, false);
-    else if (it.phase == PH_HEAD)
-      r = head_forward_backward(c, c.buf[it.buf], B, T, gdev);
-    else
-      r = layer_backward(c, bind_layer(c, c.buf[it.buf]), it.unit, B, T, gdev);
+    int r = MT_OK;
+    // the batch in micro-batches of at most mb_seqs sequences, in order
+    for (int b0 = 0; b0 < B && !r; b0 += c.mb_seqs) {
+      const int bj = std::min(c.mb_seqs, B - b0);
+      const int64_t row0 = (int64_t)b0 * T;
+      if (it.phase == PH_FWD)
+        r = layer_forward(c, bind_layer(c, c.buf[it.buf]), it.unit, bj, T, false, row0);
+      else if (it.phase == PH_HEAD)
+        r = head_forward_backward(c, c.buf[it.buf], bj, T, gdev, row0, b0 == 0, M);
+      else
+        r = layer_backward(c, bind_layer(c, c.buf[it.buf]), it.unit, bj, T, gdev, row0, b0 == 0);
+    }
     if (r) return r;
+    if (g16 && gdev) {
+      // the unit's gradient slab as bf16 for the link
+      const Unit& gu = it.phase == PH_HEAD ? c.head() : c.layer(it.unit);
+      void* g16dev = c.gbuf16[it.grad_k % 2];
+      const int64_t n = gu.lay.n;
+      r = timed(c, K_CAST, 0, (double)n * 6, [&] { return cast(MT_BF16, gdev, g16dev, n, c.s_comp); });
+      if (r) return r;
+    }
     span(it.phase, unit_id(it), hc);
     if (trace) HIPCK(hipEventRecord(trace_ev(i, 3), c.s_comp));
     HIPCK(hipEventRecord(E.freed[i], c.s_comp));
@@ -463,14 +517,20 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
   auto issue_grad = [&](int kk) -> int {
     const int i = grad_item[kk];
     const Unit& u = grad_unit(kk);
+    if (c.delay_d2h_us) std::this_thread::sleep_for(std::chrono::microseconds(c.delay_d2h_us));
     if (trace) HIPCK(hipEventRecord(trace_ev(i, 4), c.s_out));
     const auto hg = std::chrono::steady_clock::now();
-    HIPCK(hipMemcpyAsync(grad_dest(kk), c.gbuf[kk % 2], (size_t)u.lay.n * 4, hipMemcpyDeviceToHost, c.s_out));
+    HIPCK(hipMemcpyAsync(grad_dest(kk), g16 ? c.gbuf16[kk % 2] : (void*)c.gbuf[kk % 2], (size_t)u.lay.n * gbytes,
+                         hipMemcpyDeviceToHost, c.s_out));
     span(MT_PH_GRAD, unit_id(items[i]), hg);
     if (trace) HIPCK(hipEventRecord(trace_ev(i, 5), c.s_out));
+    if (c.poison) {
+      const int rp = poison_unit(c.gbuf[kk % 2], u.lay, kk == 0 ? L : L - kk, -1, c.s_out);
+      if (rp) return rp;
+    }
     HIPCK(hipEventRecord(E.drained[kk], c.s_out));
     grad_issued[kk] = 1;
-    d2h_bytes += (double)u.lay.n * 4;
+    d2h_bytes += (double)u.lay.n * gbytes;
     return MT_OK;
   };
   auto issue_loss = [&]() -> int {
@@ -499,6 +559,38 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
     adam_start_ms[L + 1] = ms_since(t_begin);
     submit_adamw(c, L + 1, emb.g, std::move(runs), k, -1, adam_priority(L + 1));
   };
+
+  // what the dispatcher waits for, for the error of a wait that exceeded its limit
+  auto item_name = [&](int i) {
+    const Item& it = items[i];
+    return std::string(it.phase == PH_FWD ? "forward of layer " : it.phase == PH_HEAD ? "head" : "backward of layer ") +
+           (it.phase == PH_HEAD ? "" : std::to_string(it.unit));
+  };
+  auto unit_name = [&](int uidx) {
+    return uidx < L ? "layer " + std::to_string(uidx) : uidx == L ? std::string("head") : std::string("embedding");
+  };
+  auto pending = [&]() {
+    std::string w;
+    auto add = [&](const std::string& x) { w += (w.empty() ? "" : "; ") + x; };
+    if (next_l < loads.size()) {
+      const int j = loads[next_l], p = items[j].prev_user;
+      const int ui = items[j].phase == PH_HEAD ? L : items[j].unit;
+      if (p >= 0 && !done_seen[p]) add("load of " + unit_name(ui) + " (its buffer's last user, the " + item_name(p) +
+                                       ", has not finished)");
+      else add("load of " + unit_name(ui) + " (its AdamW update has not landed)");
+    }
+    if (next_c < n_items) add("the " + item_name(next_c) + " (its inputs have not been issued)");
+    if (loss_issued && next_g <= L)
+      add("gradient copy of " + unit_name(grad_uidx(next_g)) +
+          (computed[grad_item[next_g]] && done_seen[grad_item[next_g]] ? " (no free staging slot)"
+                                                                       : " (its compute has not finished)"));
+    if (next_a < next_g) add("gradients of " + unit_name(grad_uidx(next_a)) + " landing in host memory");
+    if (dx0_issued && !dx0_done) add("input gradient of layer 0 landing in host memory");
+    if (nh && next_s <= kpark) add("checkpoint " + std::to_string(next_s) + " leaving the device");
+    if (nh && next_r >= 0) add("checkpoint " + std::to_string(next_r) + " returning to the device");
+    return w.empty() ? std::string("nothing issued") : w;
+  };
+  auto t_progress = std::chrono::steady_clock::now();
 
   for (;;) {
     bool progress = false;
@@ -619,7 +711,7 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
       const int st = item_done(grad_item[next_g]);
       if (st < 0) { rc = st; break; }
       if (!st) break;
-      if (!keep) {
+      if (staged) {
         const int sidx = take_slot(next_g);
         if (sidx < 0) break;
         slot_of[next_g] = sidx;
@@ -639,9 +731,9 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
       if (!abort) {
         adam_start_ms[ui] = last_land_ms;
         c.dev_current[ui] = 0;
-        submit_adamw(c, ui, grad_dest(kk), {{0, c.units[ui].lay.n}}, k, keep ? -1 : slot_of[kk],
-                     adam_priority(ui));
-      } else if (!keep) {
+        submit_adamw(c, ui, grad_dest(kk), {{0, c.units[ui].lay.n}}, k, staged ? slot_of[kk] : -1,
+                     adam_priority(ui), g16, (g16 && keep) ? c.units[ui].g : nullptr);
+      } else if (staged) {
         free_slot(slot_of[kk]);
       }
       ++next_a;
@@ -673,10 +765,26 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
       if (st) dx0_done = progress = true;
     }
     if (dx0_done && next_a > L) break;
-    if (!progress) std::this_thread::sleep_for(std::chrono::microseconds(10));
+    if (progress) {
+      t_progress = std::chrono::steady_clock::now();
+    } else {
+      if (limit_ms > 0 && ms_since(t_progress) > (double)limit_ms) {
+        rc = set_error(&c, MT_ETIMEOUT, "no progress for " + std::to_string(limit_ms) + " ms; waiting for: " + pending());
+        break;
+      }
+      std::this_thread::sleep_for(std::chrono::microseconds(10));
+    }
   }
-  // the checkpoint copy jobs read and write this step's state: let them finish
+  // the checkpoint copy jobs read and write this step's state (they are plain
+  // host copies): let them finish, whatever the limit
   while (ck_jobs.load()) std::this_thread::sleep_for(std::chrono::microseconds(20));
+  if (rc == MT_ETIMEOUT) {
+    // work already issued stays in flight (mt_destroy waits for the device;
+    // the state accessors wait for the updates)
+    c.broken = true;
+    std::fill(c.dev_current.begin(), c.dev_current.end(), 0);
+    return rc;
+  }
   if (rc) {
     // drain what was submitted before reporting the error
     hipStreamSynchronize(c.s_in);
@@ -718,7 +826,14 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
     submit_adamw(c, L + 1, emb.g, std::move(runs), k, -1, adam_priority(L + 1));
   }
   // synchronous mode: every update lands before the step returns
-  if (!overlap) adam_drain(c);
+  if (!overlap) {
+    const int ra = adam_drain_for(c, limit_ms, "end of step");
+    if (ra) {
+      c.broken = true;
+      std::fill(c.dev_current.begin(), c.dev_current.end(), 0);
+      return ra;
+    }
+  }
   const hipError_t s1 = hipStreamSynchronize(c.s_in), s2 = hipStreamSynchronize(c.s_comp),
                    s3 = hipStreamSynchronize(c.s_out);
   if (s1 != hipSuccess || s2 != hipSuccess || s3 != hipSuccess) {

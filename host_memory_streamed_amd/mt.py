@@ -19,6 +19,7 @@ MT_OK, MT_EINVAL, MT_EHOSTOOM, MT_EDEVOOM, MT_EHIP, MT_ENONFINITE, MT_ETIMEOUT, 
     0, -1, -2, -3, -4, -5, -6, -7, -8)
 MT_FP32, MT_BF16 = 0, 1
 MT_KEEP_GRADS, MT_KERNEL_TIMING, MT_TRACE, MT_OVERLAP_OPT, MT_PROGRESS, MT_CACHE_NO_REFRESH = 1, 2, 4, 8, 16, 32
+MT_BF16_GRADS = 64
 MT_GEMM_NT, MT_GEMM_NN, MT_GEMM_TN = 0, 1, 2
 PHASES = {0: "load", 1: "fwd", 2: "head", 3: "bwd", 4: "grad", 5: "adamw", 6: "ckpt_out", 7: "ckpt_in",
           8: "refresh"}
@@ -37,7 +38,8 @@ class ModelConfig(ctypes.Structure):
         "max_seq", "compute_dtype", "n_layer_buffers", "host_threads")] + [
         ("flags", ctypes.c_uint32), ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float)] + [
         (n, ctypes.c_double) for n in ("lr", "beta1", "beta2", "adam_eps", "weight_decay")] + [
-        ("chunk_rows", ctypes.c_int32), ("ckpt_host", ctypes.c_int32)]
+        ("chunk_rows", ctypes.c_int32), ("ckpt_host", ctypes.c_int32), ("grad_ring_slots", ctypes.c_int32),
+        ("wait_timeout_ms", ctypes.c_int32), ("micro_batches", ctypes.c_int32)]
 
 
 class DeviceEnv(ctypes.Structure):
@@ -111,6 +113,8 @@ _SIGS = {
     "mt_op_cast": (ctypes.c_int, [_I32, _P, _P, _I64, _P]),
     "mt_adamw_host": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, ctypes.c_double, ctypes.c_double,
                                      ctypes.c_double, ctypes.c_double, ctypes.c_double, _P, _I32]),
+    "mt_adamw_host_g16": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, ctypes.c_double, ctypes.c_double,
+                                         ctypes.c_double, ctypes.c_double, ctypes.c_double, _P, _I32]),
 }
 _lib = None
 
@@ -154,10 +158,12 @@ def _ptr(a) -> int:
 def make_config(n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab, max_batch, max_seq,
                 dtype=MT_FP32, n_layer_buffers=2, host_threads=0, flags=0, rms_eps=1e-5,
                 rope_base=10000.0, lr=1e-3, beta1=0.9, beta2=0.999, adam_eps=1e-8,
-                weight_decay=0.01, chunk_rows=0, ckpt_host=0) -> ModelConfig:
+                weight_decay=0.01, chunk_rows=0, ckpt_host=0, grad_ring_slots=0,
+                wait_timeout_ms=0, micro_batches=0) -> ModelConfig:
     return ModelConfig(n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab, max_batch,
                        max_seq, dtype, n_layer_buffers, host_threads, flags, rms_eps, rope_base, lr,
-                       beta1, beta2, adam_eps, weight_decay, chunk_rows, ckpt_host)
+                       beta1, beta2, adam_eps, weight_decay, chunk_rows, ckpt_host, grad_ring_slots,
+                       wait_timeout_ms, micro_batches)
 
 
 def host_bytes(cfg: ModelConfig) -> dict:
@@ -384,6 +390,16 @@ def adamw_host(p, m, v, g, t, lr, beta1, beta2, eps, weight_decay, bf16_out=None
         assert a.dtype == np.float32 and a.flags.c_contiguous
     _check(lib().mt_adamw_host(_ptr(p), _ptr(m), _ptr(v), _ptr(g), p.size, t, lr, beta1, beta2, eps,
                                weight_decay, _ptr(bf16_out), threads))
+
+
+def adamw_host_g16(p, m, v, g16, t, lr, beta1, beta2, eps, weight_decay, g32_out=None, bf16_out=None,
+                   threads=0):
+    """mt_adamw_host with the gradient as bf16 bit patterns (uint16)."""
+    for a in (p, m, v):
+        assert a.dtype == np.float32 and a.flags.c_contiguous
+    assert g16.dtype == np.uint16 and g16.flags.c_contiguous
+    _check(lib().mt_adamw_host_g16(_ptr(p), _ptr(m), _ptr(v), _ptr(g16), _ptr(g32_out), p.size, t, lr, beta1,
+                                   beta2, eps, weight_decay, _ptr(bf16_out), threads))
 
 
 @dataclass

@@ -76,6 +76,14 @@ extern "C" {
  * the backward; their next image is fetched by the next forward instead, so
  * the backward's link carries only gradients. */
 #define MT_CACHE_NO_REFRESH 32u
+/* Gradients cross the host link as bf16 (round to nearest even) instead of
+ * fp32, halving the gradient copy bytes; the host AdamW widens them exactly
+ * (mt_grads then returns the widened values). A measured variant: the
+ * default keeps the gradients at full precision ("MegaTrain: Full Precision
+ * Training of 100B+ Parameter Large Language Models on a Single GPU"); the
+ * technical brief's "Limitations of Current Throughput Metrics and Empirical
+ * Validation" leaves batch and transfer configurations open. */
+#define MT_BF16_GRADS 64u
 
 typedef struct mt_model_cfg {
   int32_t n_layers;
@@ -99,7 +107,7 @@ typedef struct mt_model_cfg {
   int32_t n_layer_buffers;
   int32_t host_threads;      /* AdamW / gather pool size; 0 = online CPUs (at most 64) */
   uint32_t flags;            /* MT_KEEP_GRADS | MT_KERNEL_TIMING | MT_TRACE | MT_OVERLAP_OPT | MT_PROGRESS |
-                                MT_CACHE_NO_REFRESH */
+                                MT_CACHE_NO_REFRESH | MT_BF16_GRADS */
   float rms_eps;
   float rope_base;
   double lr, beta1, beta2, adam_eps, weight_decay;   /* AdamW hyperparameters */
@@ -117,6 +125,33 @@ typedef struct mt_model_cfg {
    * device slots (x_0 is re-sent from the gathered embedding rows). Results
    * do not depend on k. */
   int32_t ckpt_host;
+  /* Pinned gradient staging slots when MT_KEEP_GRADS is off (each holds one
+   * unit's gradients from their D2H until that unit's AdamW has read them).
+   * 0 = automatic (synchronous: 3 slots of the largest unit; MT_OVERLAP_OPT:
+   * as many layer-sized slots as fit in 16 GiB, 3 to 16, plus one for the
+   * head). k in [1, 64] = exactly k slots (plus the head's with
+   * MT_OVERLAP_OPT). Fewer slots make a gradient copy wait for an earlier
+   * unit's update to release its slot; results do not depend on k. */
+  int32_t grad_ring_slots;
+  /* Limit, in milliseconds, on any host-side wait inside a step (the
+   * dispatcher waiting for a copy, a kernel sequence, a staging slot or an
+   * AdamW update to make progress; the final wait for the updates). 0 = no
+   * limit. When a wait exceeds it, mt_train_step stops issuing work, waits
+   * for what it already issued, and returns MT_ETIMEOUT with mt_last_error()
+   * naming the item it was waiting for; the host state may then hold part of
+   * the step's updates, and the context accepts no further steps (MT_ESTATE)
+   * but can still be read and destroyed. */
+  int32_t wait_timeout_ms;
+  /* Gradient accumulation over micro-batches inside each streamed unit. 0 or
+   * 1: the step's B sequences run through each layer together. k >= 2: each
+   * unit runs them as k micro-batches of ceil(B / k) sequences (the last may
+   * be smaller), and its weight gradients sum over the micro-batches on the
+   * device before they leave it; the weights still cross the link once per
+   * step. The activation workspace is sized for one micro-batch (the
+   * residual checkpoints and the residual gradient still hold the whole
+   * batch). Results equal the whole-batch step up to the order in which the
+   * weight gradients add up. Must be at most max_batch. */
+  int32_t micro_batches;
 } mt_model_cfg;
 
 /* Optional streams for the three pipeline stages (hipStream_t values passed as

@@ -141,6 +141,13 @@ int mt_adamw_host(float* p, float* m, float* v, const float* g, int64_t n, int64
                   double beta1, double beta2, double eps, double weight_decay, uint16_t* bf16_out,
                   int32_t threads);
 
+/* mt_adamw_host with the gradient given as bf16 bit patterns g16[n] (the
+ * MT_BF16_GRADS transfer format), widened exactly to fp32 before the same
+ * update; if g32_out is not NULL it receives the widened gradient. */
+int mt_adamw_host_g16(float* p, float* m, float* v, const uint16_t* g16, float* g32_out, int64_t n, int64_t t,
+                      double lr, double beta1, double beta2, double eps, double weight_decay,
+                      uint16_t* bf16_out, int32_t threads);
+
 #ifdef __cplusplus
 }
 #endif

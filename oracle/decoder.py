@@ -48,25 +48,30 @@ the same points and accumulates in float64:
   loss, ``D = rowsum(dO * O)``, the weight gradients, AdamW) stays full
   precision.
 
-Where P is rounded has two readings. The plain one (``mode="bf16"``) rounds
-the normalised probabilities P = softmax(S). A flash-style kernel never holds
-the normalised P before the product with V: it rounds exp(S - m) against the
-running row maximum m over successive key blocks, rescales the partial sums
-when m grows, and divides by the row sum at the end. ``mode="bf16-flash64"``
-follows that reading with 64-key blocks (the rest is identical; the backward
-rounds the normalised P recomputed from the logsumexp in both readings).
+The attention probabilities are rounded where the definition forms them:
+the normalised P = softmax(S), once, before the product with V (and the
+same P, recomputed from the logsumexp, before the product that gives dV).
+This is the plain reading of "bf16 operands into the matrix product"; no
+implementation's blocking or running maximum enters it.
 
-The exact rounding outcomes in bf16 mode are parity unpinned: they are checked
-to a tolerance only.
+The exact rounding outcomes in bf16 mode are parity unpinned: a bf16
+implementation is held to this reading within tolerances derived from the
+distance of this reading itself from the float64 step (``mode="fp32"``).
 
 Master state is stored in fp32 (the method's "full precision" state), so
 ``train_step`` rounds p, m and v to fp32 after each update.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
+from threadpoolctl import threadpool_limits
+
+# attention heads run on a thread pool (False: one after another)
+PARALLEL_HEADS = True
 
 LAYER_TENSORS = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
 
@@ -126,10 +131,9 @@ def fp32(x) -> np.ndarray:
 
 class _Prec:
     def __init__(self, mode: str):
-        if mode not in ("fp32", "bf16", "bf16-flash64"):
+        if mode not in ("fp32", "bf16"):
             raise ValueError(mode)
         self.mode = mode
-        self.p_block = 64 if mode == "bf16-flash64" else None
 
     def op(self, x):
         """Operand of a matrix product."""
@@ -180,6 +184,28 @@ def rope_bwd(dy, cos, sin):
     return np.concatenate([d1 * c + d2 * s, d2 * c - d1 * s], axis=-1)
 
 
+def _threads():
+    """Worker threads: the CPUs this process may run on, at most
+    OMP_NUM_THREADS when that is set, and at most 16."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, min(16, n))
+
+
+def _per_head(fn, B, H):
+    """[fn(b, h) for b < B, h < H] in that order. Heads are independent, so
+    they run on a thread pool (one BLAS thread each); the results, and every
+    sum formed from them, are exactly those of the plain loop."""
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    workers = min(len(pairs), _threads())
+    if workers <= 1 or not PARALLEL_HEADS:
+        return [fn(b, h) for b, h in pairs]
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(lambda bh: fn(*bh), pairs))
+
+
 def attention_fwd(q, k, v, prec: _Prec):
     """Causal GQA attention. q: [B,T,H,hd], k/v: [B,T,Hkv,hd] (already the
     matrix-product operands). Query head h reads kv head h // (H/Hkv).
@@ -192,33 +218,19 @@ def attention_fwd(q, k, v, prec: _Prec):
     mask = np.triu(np.ones((T, T), dtype=bool), 1)
     o = np.empty_like(q)
     lse = np.empty((B, H, T))
-    for b in range(B):
-        for h in range(H):
-            kv = h // grp
-            S = (q[b, :, h, :] @ k[b, :, kv, :].T) * scale
-            S[mask] = -np.inf
-            if prec.p_block is None:
-                m = S.max(axis=1, keepdims=True)
-                e = np.exp(S - m)
-                l = e.sum(axis=1, keepdims=True)
-                P = e / l
-                lse[b, h] = (m + np.log(l))[:, 0]
-                o[b, :, h, :] = prec.op(P) @ v[b, :, kv, :]
-            else:
-                # running maximum over key blocks; unnormalised probabilities rounded
-                m = np.full(T, -np.inf)
-                l = np.zeros(T)
-                acc = np.zeros((T, hd))
-                for k0 in range(0, T, prec.p_block):
-                    s = S[:, k0:k0 + prec.p_block]
-                    mn = np.maximum(m, s.max(axis=1))
-                    a = np.exp(m - mn)
-                    e = np.exp(s - mn[:, None])
-                    l = l * a + e.sum(axis=1)
-                    acc = acc * a[:, None] + prec.op(e) @ v[b, k0:k0 + prec.p_block, kv, :]
-                    m = mn
-                o[b, :, h, :] = acc / l[:, None]
-                lse[b, h] = m + np.log(l)
+
+    def head(b, h):
+        kv = h // grp
+        S = (q[b, :, h, :] @ k[b, :, kv, :].T) * scale
+        S[mask] = -np.inf
+        m = S.max(axis=1, keepdims=True)
+        e = np.exp(S - m)
+        l = e.sum(axis=1, keepdims=True)
+        P = e / l
+        lse[b, h] = (m + np.log(l))[:, 0]
+        o[b, :, h, :] = prec.op(P) @ v[b, :, kv, :]
+
+    _per_head(head, B, H)
     return o, lse
 
 
@@ -226,7 +238,7 @@ def attention_bwd(q, k, v, o, lse, do, prec: _Prec):
     """Backward of attention_fwd given dO (full precision). With P recomputed
     from lse: dP = dO V^T, D = rowsum(dO*O), dS = P*(dP - D),
     dq = scale dS k, dk = scale dS^T q, dv = P^T dO; dk and dv are summed over
-    the query heads of each kv group."""
+    the query heads of each kv group, in head order."""
     B, T, H, hd = q.shape
     Hkv = k.shape[2]
     grp = H // Hkv
@@ -236,18 +248,22 @@ def attention_bwd(q, k, v, o, lse, do, prec: _Prec):
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     dob = prec.op(do)
-    for b in range(B):
-        for h in range(H):
-            kv = h // grp
-            S = (q[b, :, h, :] @ k[b, :, kv, :].T) * scale
-            S[mask] = -np.inf
-            P = np.exp(S - lse[b, h][:, None])
-            dP = dob[b, :, h, :] @ v[b, :, kv, :].T
-            D = np.sum(do[b, :, h, :] * o[b, :, h, :], axis=1)
-            dS = prec.op(P * (dP - D[:, None]))
-            dq[b, :, h, :] = (dS @ k[b, :, kv, :]) * scale
-            dk[b, :, kv, :] += (dS.T @ q[b, :, h, :]) * scale
-            dv[b, :, kv, :] += prec.op(P).T @ dob[b, :, h, :]
+
+    def head(b, h):
+        kv = h // grp
+        S = (q[b, :, h, :] @ k[b, :, kv, :].T) * scale
+        S[mask] = -np.inf
+        P = np.exp(S - lse[b, h][:, None])
+        dP = dob[b, :, h, :] @ v[b, :, kv, :].T
+        D = np.sum(do[b, :, h, :] * o[b, :, h, :], axis=1)
+        dS = prec.op(P * (dP - D[:, None]))
+        dq[b, :, h, :] = (dS @ k[b, :, kv, :]) * scale
+        return (dS.T @ q[b, :, h, :]) * scale, prec.op(P).T @ dob[b, :, h, :]
+
+    parts = _per_head(head, B, H)
+    for (b, h), (dkh, dvh) in zip([(b, h) for b in range(B) for h in range(H)], parts):
+        dk[b, :, h // grp, :] += dkh
+        dv[b, :, h // grp, :] += dvh
     return dq, dk, dv
 
 

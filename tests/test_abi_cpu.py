@@ -56,7 +56,9 @@ def test_tensor_table_matches_oracle(name):
 @pytest.mark.parametrize("field,value", [("n_layers", 0), ("n_kv_heads", 3), ("head_dim", 48),
                                          ("compute_dtype", 7), ("n_layer_buffers", 1), ("d_model", 66),
                                          ("max_seq", 0), ("flags", 1 << 10), ("chunk_rows", -1),
-                                         ("ckpt_host", -1), ("ckpt_host", 1)])
+                                         ("ckpt_host", -1), ("ckpt_host", 1), ("grad_ring_slots", -1),
+                                         ("grad_ring_slots", 65), ("wait_timeout_ms", -5), ("micro_batches", -1),
+                                         ("micro_batches", 3)])
 def test_create_rejects_bad_config(field, value):
     # two layers: no checkpoint can be parked (x_1..x_k with k <= n_layers - 2)
     c = mt.make_config(2, 64, 4, 4, 16, 172, 256, 2, 32)
@@ -98,6 +100,29 @@ def test_host_adamw_matches_oracle_over_steps():
         # the bf16 image is exactly the rounding of the updated fp32 value
         img = (bf.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         np.testing.assert_array_equal(img, O.bf16(p))
+
+
+def test_host_adamw_with_bf16_gradients():
+    """The bf16-gradient form widens each gradient exactly and then takes the
+    same update: it equals the fp32 form given the widened gradient, bit for
+    bit, and writes the widened gradient out."""
+    rng = np.random.default_rng(6)
+    n = 70_001
+    g32 = (rng.standard_normal(n) * 10.0 ** rng.integers(-8, -1, n)).astype(np.float32)
+    g16 = (O.bf16(g32).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    wide = (g16.astype(np.uint32) << 16).view(np.float32)
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    state = [p, np.zeros(n, np.float32), np.zeros(n, np.float32)]
+    ref = [a.copy() for a in state]
+    out = np.full(n, np.nan, np.float32)
+    bf_a, bf_b = np.empty(n, np.uint16), np.empty(n, np.uint16)
+    for t in (1, 2):
+        mt.adamw_host_g16(*state, g16, t, 1e-3, 0.9, 0.999, 1e-8, 0.01, g32_out=out, bf16_out=bf_a, threads=3)
+        mt.adamw_host(*ref, wide.copy(), t, 1e-3, 0.9, 0.999, 1e-8, 0.01, bf16_out=bf_b, threads=3)
+        for a, b in zip(state, ref):
+            np.testing.assert_array_equal(a, b)
+        np.testing.assert_array_equal(bf_a, bf_b)
+        np.testing.assert_array_equal(out, wide)
 
 
 def test_host_adamw_rejects_bad_arguments():

@@ -1,26 +1,29 @@
 """The streamed training step through the C-ABI against the CPU oracle.
 
 fp32 mode: loss, per-token losses, every gradient, updated parameters and
-AdamW moments within rtol 1e-4 / atol 1e-5 of the oracle. bf16-compute mode:
-every tensor within rtol 2e-2 normwise (||gpu - ref|| <= 2e-2 ||ref||) of the
-oracle under the flash-block reading of where attention probabilities are
-rounded (the one the kernels implement) and elementwise within
-2e-2 |ref| + 0.2 rms(row) of it (all but 0.1% of the elements; every element
-within 2e-2 |ref| + 0.5 rms(row)); against the normalised-P reading within
-2e-2 plus the distance between the two readings themselves. Two
-bf16 implementations that differ in any one rounding decision diverge by a
-cascade of flipped decisions downstream, so individual elements formed by
-heavy cancellation carry noise of a few percent of the tensor's rms; the
-elementwise term catches localised errors (a wrong row, tail or head).
+AdamW moments within rtol 1e-4 / atol 1e-5 of the oracle elementwise, and
+each tensor within 1e-4 of the oracle normwise (||gpu - ref|| <= 1e-4 ||ref||,
+which binds where most elements sit below the absolute tolerance).
+
+bf16-compute mode: against the oracle's plain bf16 reading (``mode="bf16"``:
+every matrix-product operand rounded where the definition forms it, the
+normalised attention probabilities included), with the fixed tolerances of
+``tolerances.py``: per tensor kind and depth class, a normwise bound and an
+elementwise guard on each row's own scale, each at least twice the oracle's
+own distance between that reading and its float64 step (measured by
+``golden/bf16_distance.py``, recorded in ``golden/bf16_distance.json``).
+
 Token order is bit-exact (per-token losses in (b, t) order), streamed equals
 fully resident bitwise, and the schedule log follows the layer order."""
 import math
+import os
 
 import numpy as np
 import pytest
 
 import oracle as O
 from oracle.configs import shape
+from tolerances import bf16_tol
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -28,151 +31,198 @@ pytestmark = pytest.mark.gpu
 from host_memory_streamed_amd import mt, synth  # noqa: E402
 
 
+def release_on_failure(fn):
+    """Run fn; on an assertion failure raise a fresh AssertionError (with the
+    original traceback as text) once fn's frames, and the oracle arrays they
+    hold, are released: a failed multi-gigabyte comparison must not keep its
+    memory for the rest of the session."""
+    import functools
+    import traceback
+
+    @functools.wraps(fn)
+    def wrapper(*a, **kw):
+        msg = None
+        try:
+            return fn(*a, **kw)
+        except AssertionError as e:
+            msg = "".join(traceback.format_exception(type(e), e, e.__traceback__))[-6000:]
+        raise AssertionError(msg)
+    return wrapper
+
+
 def init_params(cfg, seed, std=0.02):
     return [synth.init_tensor(seed, i, shp, gain, std) for i, (_, shp, gain) in enumerate(O.tensor_table(cfg))]
 
 
 def make_ctx(cfg, B, T, params, dtype=mt.MT_FP32, resident=False, flags=mt.MT_KEEP_GRADS, threads=8,
-             chunk_rows=0, ckpt_host=0, buffers=None):
+             chunk_rows=0, ckpt_host=0, buffers=None, ring_slots=0, micro_batches=0):
     if buffers is None:
         buffers = cfg.n_layers + 1 if resident else 2
     c = mt.make_config(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn_dim,
                        cfg.vocab, B, T, dtype=dtype, n_layer_buffers=buffers,
                        host_threads=threads, flags=flags, rms_eps=cfg.rms_eps, rope_base=cfg.rope_base,
                        lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, adam_eps=cfg.adam_eps,
-                       weight_decay=cfg.weight_decay, chunk_rows=chunk_rows, ckpt_host=ckpt_host)
+                       weight_decay=cfg.weight_decay, chunk_rows=chunk_rows, ckpt_host=ckpt_host,
+                       grad_ring_slots=ring_slots, micro_batches=micro_batches)
     return mt.Context(c, params)
+
+
+def check_normwise(name, got, ref, tol):
+    n = np.linalg.norm(ref)
+    err = np.linalg.norm(np.asarray(got, np.float64) - ref)
+    assert err <= tol * n + 1e-30, f"{name}: normwise {err / (n + 1e-300):.3g} > {tol}"
 
 
 def check_fp32(name, got, ref, rtol=1e-4, atol=1e-5):
     np.testing.assert_allclose(got, ref, rtol=rtol, atol=atol, err_msg=name)
+    check_normwise(name, got, ref, rtol)
 
 
-def check_bf16(name, got, ref, tol=2e-2, rms_frac=0.2, hard_frac=0.5, spill=1e-3):
-    check_normwise(name, got, ref, tol)
-    # elementwise guard on each row's own scale (a row is one output unit):
-    # at most a fraction `spill` of the elements beyond rms_frac rms(row), none
-    # beyond hard_frac rms(row). The two oracle readings of where P is rounded
-    # differ on query/key gradients by up to ~0.06% of elements beyond
-    # 0.2 rms(row) and at most ~0.3 rms(row); a localised bug (a wrong tile,
-    # row, tail or head) moves whole blocks by O(rms).
+def check_bf16(name, got, ref, tol, spill=1e-3):
+    """tol = (tau, gamma, rho): ||got - ref|| <= tau ||ref||; |got - ref| <=
+    gamma rms(row of ref) for all but a fraction `spill` of the elements; and
+    ||got_row - ref_row|| <= rho ||ref_row|| for every row. A row is one
+    output unit (the whole vector for gains and per-token losses)."""
+    tau, gamma, rho = tol
+    got = np.asarray(got, np.float64)
     r2 = ref.reshape(ref.shape[0], -1) if ref.ndim > 1 else ref.reshape(1, -1)
-    rms = np.sqrt(np.mean(np.square(r2), axis=1, keepdims=True))
-    dev_ = np.abs(got.reshape(r2.shape) - r2) - tol * np.abs(r2)
-    n_soft = int((dev_ > rms_frac * rms).sum())
-    assert n_soft <= spill * r2.size, f"{name}: {n_soft} elements beyond 2e-2|ref| + {rms_frac} rms(row)"
-    n_hard = int((dev_ > hard_frac * rms).sum())
-    assert n_hard == 0, f"{name}: {n_hard} elements beyond 2e-2|ref| + {hard_frac} rms(row)"
+    diff = got.reshape(r2.shape) - r2
+    rn = np.sqrt(np.sum(np.square(r2), axis=1))
+    dn = np.sqrt(np.sum(np.square(diff), axis=1))
+    rms = (rn / np.sqrt(r2.shape[1]))[:, None]
+    if os.environ.get("MT_TEST_REPORT"):
+        # the measured distances against their bounds, for the record
+        q = float(np.quantile(np.abs(diff) / (rms + 1e-300), 0.999))
+        ok = rn > 0
+        rmax = float(np.max(dn[ok] / rn[ok])) if ok.any() else 0.0
+        print(f"BF16REPORT {name}: norm {np.linalg.norm(diff) / (np.linalg.norm(r2) + 1e-300):.4g}/{tau} "
+              f"q999 {q:.4g}/{gamma} row {rmax:.4g}/{rho}", flush=True)
+    check_normwise(name, got, ref, tau)
+    n_out = int((np.abs(diff) > gamma * rms).sum())
+    assert n_out <= spill * r2.size, f"{name}: {n_out} of {r2.size} elements beyond {gamma} rms(row)"
+    bad = dn > rho * rn + 1e-30
+    if bad.any():
+        worst = int(np.argmax(dn / (rn + 1e-300)))
+        raise AssertionError(f"{name}: {int(bad.sum())} rows beyond {rho} normwise; row {worst} at "
+                             f"{dn[worst] / (rn[worst] + 1e-300):.3g}")
 
 
-def check_normwise(name, got, ref, tol=2e-2):
-    n = np.linalg.norm(ref)
-    assert np.linalg.norm(got - ref) <= tol * n + 1e-30, f"{name}: normwise {np.linalg.norm(got - ref) / n:.3g}"
+def _kind(name):
+    return name.split(".")[-1]
 
 
-def check_other_reading(name, got, plain, flash):
-    """Against the normalised-P reading, allowing for the distance between the
-    two readings of where P is rounded (the oracle's own flash-block and
-    normalised results differ by up to ~2% normwise on sensitive tensors)."""
-    gap = np.linalg.norm(flash - plain) / (np.linalg.norm(plain) + 1e-300)
-    check_normwise(name, got, plain, 2e-2 + gap)
-
-
-def compare_step(ctx, res, cfg, mode, prev, plain=None, tokens=None, guard=True):
+def compare_step(ctx, res, cfg, mode, prev, tokens=None, depth="shallow", sample=None, extra=0.0):
     """Gradients against the oracle's; the update against the oracle's AdamW
     applied to the library's own gradient (fp32 rounding only); and the
     updated state against the oracle's end-to-end step, except (fp32 mode)
     where the first-moment update g/(|g|+eps) is ill-conditioned: |g| < 1e-5,
     where a gradient difference inside the gradient tolerance can move it by
-    O(1) (the update of such an element is still checked given the gradient)."""
-    if mode == "bf16" and not guard:
-        # deep bf16: the stated tolerance (normwise) plus the oracle's own
-        # distance, for this quantity, between its two readings of where P is
-        # rounded (they drift apart with depth like any two bf16 schedules)
-        def chk(name, got, ref, alt):
-            gap = np.linalg.norm(ref - alt) / (np.linalg.norm(ref) + 1e-300)
-            check_normwise(name, got, ref, 2e-2 + gap)
-    else:
-        base = check_bf16 if mode == "bf16" else check_fp32
-
-        def chk(name, got, ref, alt=None):
-            base(name, got, ref)
-    alt = plain if plain is not None else res
+    O(1) (the update of such an element is still checked given the gradient).
+    bf16 mode uses the fixed tolerances of its depth class. `sample`: check
+    AdamW (an elementwise map) on that many random elements per tensor
+    instead of all of them. `extra`: a relative error the gradients carry
+    by design (bf16 gradient transfer: 2^-8), added to rtol, tau and rho."""
     P0, M0, V0, t0 = prev
+    rng = np.random.default_rng(0)
+    keep = bool(ctx.cfg.flags & mt.MT_KEEP_GRADS)
     for i, (name, _, _) in enumerate(O.tensor_table(cfg)):
-        g = ctx.grads(i)
+        kind = _kind(name)
+        # without kept gradients, m and v (which the update forms from the
+        # gradient) stand in for it below
+        g = ctx.grads(i) if keep else None
+        def tg(what):
+            tau, gamma, rho = bf16_tol(depth, what + " " + kind)
+            return tau + extra, gamma, rho + extra
+        chk = (lambda n_, a, b, what: check_bf16(n_, a, b, tg(what))) if mode == "bf16" else \
+              (lambda n_, a, b, what: check_fp32(n_, a, b, rtol=1e-4 + extra))
+        rows = None
         if i == 0 and tokens is not None:
             # embedding: rows outside the batch have an exactly zero gradient;
             # the touched rows are compared on their own scale
             rows = np.unique(tokens)
-            other = np.setdiff1d(np.arange(cfg.vocab), rows)
-            assert not g[other].any(), "embedding rows outside the batch must have zero gradient"
-            chk(f"grad {name}", g[rows], res.grads[i][rows], alt.grads[i][rows])
-            if plain is not None:
-                check_other_reading(f"grad {name} (normalised-P reading)", g[rows], plain.grads[i][rows],
-                                    res.grads[i][rows])
-        else:
-            chk(f"grad {name}", g, res.grads[i], alt.grads[i])
-            if plain is not None:
-                check_other_reading(f"grad {name} (normalised-P reading)", g, plain.grads[i], res.grads[i])
+            if keep:
+                other = np.setdiff1d(np.arange(cfg.vocab), rows)
+                assert not g[other].any(), "embedding rows outside the batch must have zero gradient"
+                chk(f"grad {name}", g[rows], res.grads[i][rows], "grad")
+        elif keep:
+            chk(f"grad {name}", g, res.grads[i], "grad")
         p = ctx.params(i)
         m, v, t = ctx.opt_state(i)
         assert t == res.t == t0 + 1
-        # AdamW given the library's gradient
-        pg, mg, vg = O.adamw(np.asarray(P0[i], np.float64), g.astype(np.float64), np.asarray(M0[i], np.float64),
-                             np.asarray(V0[i], np.float64), t, cfg)
+        sel = rows if rows is not None else slice(None)
+        if sample is not None and p.size > sample and rows is None:
+            sel = np.sort(rng.choice(p.size, sample, replace=False))
+        flat = lambda a: np.asarray(a).reshape(-1) if isinstance(sel, np.ndarray) and rows is None else a
+        pick = lambda a: flat(a)[sel]
+        ps, ms, vs = pick(p), pick(m), pick(v)
+        P0s, M0s, V0s = (np.asarray(pick(a), np.float64) for a in (P0[i], M0[i], V0[i]))
         u = 2.0 ** -24
-        g64, m0, v0 = g.astype(np.float64), np.asarray(M0[i], np.float64), np.asarray(V0[i], np.float64)
-        assert np.all(np.abs(m - mg) <= 8 * u * (cfg.beta1 * np.abs(m0) + (1 - cfg.beta1) * np.abs(g64)) + 1e-45), \
-            f"m(g) {name}"
-        assert np.all(np.abs(v - vg) <= 8 * u * (cfg.beta2 * v0 + (1 - cfg.beta2) * g64 * g64) + 1e-45), f"v(g) {name}"
-        # magnitude of the terms the step sums: lr/bc1 (b1|m0| + (1-b1)|g|) / denom
-        denom = np.sqrt(vg / (1 - cfg.beta2 ** t)) + cfg.adam_eps
-        step_terms = cfg.lr / (1 - cfg.beta1 ** t) * (cfg.beta1 * np.abs(m0) + (1 - cfg.beta1) * np.abs(g64)) / denom
-        assert np.all(np.abs(p - pg) <= 8 * u * (np.abs(np.asarray(P0[i], np.float64)) + step_terms) + 1e-45), \
-            f"p(g) {name}"
-        # end to end (embedding: the rows of this step's tokens)
-        sel = np.unique(tokens) if (i == 0 and tokens is not None) else slice(None)
-        p, m, v = p[sel], m[sel], v[sel]
-        rp, rm, rv, rg = res.params[i][sel], res.m[i][sel], res.v[i][sel], res.grads[i][sel]
+        if keep:
+            # AdamW given the library's gradient
+            g64 = pick(g).astype(np.float64)
+            pg, mg, vg = O.adamw(P0s, g64, M0s, V0s, t, cfg)
+            assert np.all(np.abs(ms - mg) <= 8 * u * (cfg.beta1 * np.abs(M0s) + (1 - cfg.beta1) * np.abs(g64))
+                          + 1e-45), f"m(g) {name}"
+            assert np.all(np.abs(vs - vg) <= 8 * u * (cfg.beta2 * V0s + (1 - cfg.beta2) * g64 * g64) + 1e-45), \
+                f"v(g) {name}"
+            # magnitude of the terms the step sums: lr/bc1 (b1|m0| + (1-b1)|g|) / denom
+            denom = np.sqrt(vg / (1 - cfg.beta2 ** t)) + cfg.adam_eps
+            step_terms = cfg.lr / (1 - cfg.beta1 ** t) * (cfg.beta1 * np.abs(M0s) + (1 - cfg.beta1) * np.abs(g64)) \
+                / denom
+            assert np.all(np.abs(ps - pg) <= 8 * u * (np.abs(P0s) + step_terms) + 1e-45), f"p(g) {name}"
+        # end to end (embedding: the rows of this step's tokens); an oracle
+        # result without updated state carries the gradients only, and its
+        # update is the oracle's AdamW taken on the compared elements
+        rg = pick(res.grads[i])
+        if res.params is None:
+            rp, rm, rv = (O.decoder.fp32(a) for a in O.adamw(P0s, np.asarray(rg, np.float64), M0s, V0s, t, cfg))
+        else:
+            rp, rm, rv = pick(res.params[i]), pick(res.m[i]), pick(res.v[i])
         if mode == "bf16":
-            chk(f"param {name}", p, rp, alt.params[i][sel])
-            chk(f"m {name}", m, rm, alt.m[i][sel])
+            chk(f"param {name}", ps, rp, "param")
+            chk(f"m {name}", ms, rm, "m")
             # v = (1-b2) g^2: compare on g's scale
-            chk(f"sqrt v {name}", np.sqrt(v), np.sqrt(rv), np.sqrt(alt.v[i][sel]))
+            chk(f"sqrt v {name}", np.sqrt(vs), np.sqrt(rv), "sqrt v")
         else:
             ok = np.abs(rg) >= 1e-5
-            check_fp32(f"param {name}", p[ok], rp[ok])
-            check_fp32(f"m {name}", m, rm)
+            check_fp32(f"param {name}", ps[ok], rp[ok], rtol=1e-4 + extra)
+            check_fp32(f"m {name}", ms, rm, rtol=1e-4 + extra)
             # v = b2 v0 + (1 - b2) g^2 with v0 equal on both sides: a gradient
             # inside its own tolerance d = 1e-5 + 1e-4 |g| moves v by up to
             # (1 - b2)(2 |g| d + d^2); fp32 rounding adds a few ulp
             ga = np.abs(rg.astype(np.float64))
-            dg = 1e-5 + 1e-4 * ga
+            dg = 1e-5 + (1e-4 + extra) * ga
             tol_v = (1 - cfg.beta2) * (2 * ga * dg + dg * dg) + 2e-4 * np.abs(rv) + 1e-12
-            bad = np.abs(v.astype(np.float64) - rv) > tol_v
+            bad = np.abs(vs.astype(np.float64) - rv) > tol_v
             assert not bad.any(), f"v {name}: {int(bad.sum())} elements beyond the gradient-implied bound"
 
 
-def run_parity(cfg, B, T, mode, steps=1, seed=0, std=0.02, guard=True, **ctx_kw):
+def check_losses(mode, loss, tl, res, depth="shallow"):
+    if mode == "bf16":
+        assert abs(loss - res.loss) <= bf16_tol(depth, "loss")[0] * abs(res.loss), (loss, res.loss)
+        check_bf16("token losses", tl, res.token_loss, bf16_tol(depth, "token_loss"))
+    else:
+        assert abs(loss - res.loss) <= 1e-4 * abs(res.loss) + 1e-5
+        check_fp32("token losses", tl, res.token_loss)
+
+
+@release_on_failure
+def run_parity(cfg, B, T, mode, steps=1, seed=0, std=0.02, depth="shallow", sample=None, extra=0.0, **ctx_kw):
     params = init_params(cfg, seed, std)
     zeros = [np.zeros_like(p) for p in params]
     dtype = mt.MT_BF16 if mode == "bf16" else mt.MT_FP32
+    ctx_kw.setdefault("flags", mt.MT_KEEP_GRADS)
     with make_ctx(cfg, B, T, params, dtype=dtype, **ctx_kw) as ctx:
         P, Mm, Vv, t = params, zeros, zeros, 0
         for s in range(steps):
             tokens, targets = synth.token_batch(seed + 10 * s, B, T, cfg.vocab)
+            print(f"step {s + 1}/{steps}: gpu", flush=True)
             loss = ctx.train_step(tokens, targets)
-            res = O.train_step(P, Mm, Vv, t, tokens, targets, cfg, "bf16-flash64" if mode == "bf16" else mode)
-            plain = O.train_step(P, Mm, Vv, t, tokens, targets, cfg, "bf16") if mode == "bf16" else None
-            tl = ctx.token_losses().reshape(B, T)
-            if mode == "bf16":
-                assert abs(loss - res.loss) <= 2e-2 * abs(res.loss)
-                (check_bf16 if guard else check_normwise)("token losses", tl, res.token_loss)
-            else:
-                assert abs(loss - res.loss) <= 1e-4 * abs(res.loss) + 1e-5
-                check_fp32("token losses", tl, res.token_loss)
-            compare_step(ctx, res, cfg, mode, (P, Mm, Vv, t), plain, tokens, guard)
+            ctx.sync()
+            print(f"step {s + 1}/{steps}: oracle", flush=True)
+            res = O.train_step(P, Mm, Vv, t, tokens, targets, cfg, mode)
+            check_losses(mode, loss, ctx.token_losses().reshape(B, T), res, depth)
+            compare_step(ctx, res, cfg, mode, (P, Mm, Vv, t), tokens, depth, sample, extra)
             t = res.t
             # continue both sides from the library's state (fp32 master values)
             P = [ctx.params(i).astype(np.float64) for i in range(len(params))]
@@ -216,32 +266,11 @@ def test_1p3b_layer_shape_reduced_depth(mode):
 def test_1p3b_full_depth_short_sequence(mode):
     # all 24 layers of the 1.3B workload (d 2048, FFN 5632, vocab 32000) on
     # 1 x 96 tokens: the streamed schedule's accumulation through the full
-    # depth at the real width, against the oracle's whole step. bf16 is held
-    # normwise to the stated 2e-2 plus the distance between the oracle's two
-    # readings of where P is rounded, without the elementwise guard of the
-    # shallow cases: at this depth the two readings differ by 2.4-2.8% on the
-    # query/key projection gradients (each 3.3-3.8% from exact arithmetic),
-    # and flipped bf16 rounding decisions leave isolated elements beyond half
-    # their row's rms. The fp32 run of the same schedule is held elementwise
-    # to 1e-4 / 1e-5
+    # depth at the real width, against the oracle's whole step; bf16 with the
+    # deep class's bounds (the oracle's own bf16 reading lies up to 3.8%
+    # normwise from its float64 step on the query/key projection gradients)
     cfg, _, _ = shape("1.3b")
-    run_parity(cfg, 1, 96, mode, seed=31, guard=(mode != "bf16"))
-
-
-def test_14b_layer_shape_one_layer_bf16():
-    # per-layer and head shape of the 14B workload (GQA 40/8, vocab 152064), 1 layer
-    cfg, _, _ = shape("14b", n_layers=1)
-    run_parity(cfg, 1, 64, "bf16", seed=13)
-
-
-def test_120b_layer_shape_one_layer_bf16():
-    # per-layer shape of the 120B-shaped workload (d 10240, GQA 80/8, FFN 28672,
-    # 1.11B parameters per layer), 1 layer; the vocabulary is cut to 2048 so
-    # that two fp64 oracle steps fit in host memory (the head is not part of
-    # the per-layer shape; its full-size product runs in the 14B test)
-    cfg, _, _ = shape("120b", n_layers=1)
-    cfg = O.Config(**{**cfg.__dict__, "vocab": 2048})
-    run_parity(cfg, 1, 64, "bf16", seed=17)
+    run_parity(cfg, 1, 96, mode, seed=31, depth="deep")
 
 
 @pytest.mark.parametrize("mode", ["fp32", "bf16"])
@@ -543,15 +572,10 @@ def test_step_smaller_than_allocated(mode):
     with mt.Context(c, params) as ctx:
         tokens, targets = synth.token_batch(31, 2, 45, cfg.vocab)
         loss = ctx.train_step(tokens, targets)
-        res = O.train_step(params, zeros, zeros, 0, tokens, targets, cfg,
-                           "bf16-flash64" if mode == "bf16" else "fp32")
+        res = O.train_step(params, zeros, zeros, 0, tokens, targets, cfg, mode)
         assert ctx.token_losses().shape == (2 * 45,)
-        if mode == "bf16":
-            assert abs(loss - res.loss) <= 2e-2 * abs(res.loss)
-        else:
-            assert abs(loss - res.loss) <= 1e-4 * abs(res.loss) + 1e-5
-        plain = O.train_step(params, zeros, zeros, 0, tokens, targets, cfg, "bf16") if mode == "bf16" else None
-        compare_step(ctx, res, cfg, mode, (params, zeros, zeros, 0), plain, tokens)
+        check_losses(mode, loss, ctx.token_losses().reshape(2, 45), res)
+        compare_step(ctx, res, cfg, mode, (params, zeros, zeros, 0), tokens)
 
 
 def test_nonfinite_loss_applies_no_update():
@@ -587,3 +611,172 @@ def test_gradients_not_kept_without_flag():
         # the staging ring gives the same update as kept gradients
         for i in range(len(params)):
             np.testing.assert_array_equal(a.params(i), b.params(i))
+
+
+# ---------------------------------------------------------------------------
+# The launch configuration bench.py times: overlapped optimizer, no kept
+# gradients (pinned staging ring), kernel timing and trace on. Two staging
+# slots for six layers make every step recycle slots while earlier updates
+# still hold them; three steps carry the moments forward.
+
+BENCH_FLAGS = mt.MT_OVERLAP_OPT | mt.MT_KERNEL_TIMING | mt.MT_TRACE
+
+
+@pytest.mark.parametrize("mode", ["fp32", "bf16"])
+def test_bench_flag_set_recycled_ring(mode):
+    cfg = O.Config(6, 128, 2, 1, 64, 200, 300)
+    run_parity(cfg, 2, 32, mode, steps=3, seed=37, std=0.05, flags=BENCH_FLAGS, ring_slots=2)
+
+
+@pytest.mark.parametrize("mode", ["fp32", "bf16"])
+def test_bench_flag_set_every_unit_cached(mode):
+    cfg = O.Config(6, 128, 2, 1, 64, 200, 300)
+    run_parity(cfg, 2, 32, mode, steps=3, seed=37, std=0.05, flags=BENCH_FLAGS, buffers=cfg.n_layers + 1)
+
+
+# ---------------------------------------------------------------------------
+# Micro-batch gradient accumulation inside each streamed unit: 5 sequences in
+# micro-batches of 2, 2 and 1 (the workspace holds 2), weight gradients summed
+# on the device over them, against the oracle's whole-batch step; plus the
+# same split with token chunks and parked checkpoints, and the bench flag set.
+
+@pytest.mark.parametrize("mode,kw", [("fp32", {}), ("bf16", {}),
+                                     ("fp32", dict(chunk_rows=24, ckpt_host=2)),
+                                     ("bf16", dict(flags=BENCH_FLAGS, ring_slots=2))])
+def test_micro_batch_accumulation(mode, kw):
+    cfg = O.Config(4, 128, 2, 1, 64, 200, 300)
+    run_parity(cfg, 5, 20, mode, steps=2, seed=47, std=0.05, micro_batches=3, **kw)
+
+
+def test_micro_batches_change_only_rounding():
+    """Micro-batches change only the order in which the weight gradients
+    add up: losses within fp32 rounding, gradients within a few ulp of their
+    terms' magnitude, of the whole-batch step."""
+    cfg = O.Config(3, 128, 2, 1, 64, 200, 300)
+    params = init_params(cfg, 49, 0.05)
+    tok, tgt = synth.token_batch(49, 4, 24, cfg.vocab)
+    out = []
+    for k in (0, 4):
+        with make_ctx(cfg, 4, 24, params, micro_batches=k) as ctx:
+            loss = ctx.train_step(tok, tgt)
+            out.append((loss, ctx.token_losses().copy(), [ctx.grads(i) for i in range(len(params))]))
+    (l0, t0, g0), (l1, t1, g1) = out
+    assert abs(l0 - l1) <= 1e-6 * abs(l0)
+    np.testing.assert_allclose(t1, t0, rtol=1e-6, atol=1e-7)
+    for a, b in zip(g0, g1):
+        np.testing.assert_allclose(b, a, rtol=1e-5, atol=1e-7 * (np.max(np.abs(a)) + 1e-30))
+
+
+# ---------------------------------------------------------------------------
+# Gradients over the link in bf16 (MT_BF16_GRADS): each gradient is the
+# oracle's within its own rounding (2^-8 relative at most) on top of the mode's
+# tolerance, with kept gradients (widened on the host) and through the
+# recycled staging ring in the bench's flag set.
+
+@pytest.mark.parametrize("mode,flags", [("fp32", mt.MT_KEEP_GRADS | mt.MT_BF16_GRADS),
+                                        ("bf16", mt.MT_KEEP_GRADS | mt.MT_BF16_GRADS),
+                                        ("bf16", BENCH_FLAGS | mt.MT_BF16_GRADS)])
+def test_bf16_gradient_transfer(mode, flags):
+    cfg = O.Config(6, 128, 2, 1, 64, 200, 300)
+    run_parity(cfg, 2, 32, mode, steps=3, seed=37, std=0.05, flags=flags, ring_slots=2, extra=2.0 ** -8)
+
+
+# ---------------------------------------------------------------------------
+# Schedule robustness: host delays injected into loads, gradient copies and
+# every AdamW, and NaN written over each released layer and gradient buffer,
+# leave every result bit for bit unchanged.
+
+class _env:
+    def __init__(self, **kv):
+        self.kv = {k: str(v) for k, v in kv.items()}
+
+    def __enter__(self):
+        import os
+        self.old = {k: os.environ.get(k) for k in self.kv}
+        os.environ.update(self.kv)
+
+    def __exit__(self, *a):
+        import os
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+@pytest.mark.parametrize("dtype,flags,slots", [(mt.MT_BF16, mt.MT_OVERLAP_OPT, 2),
+                                               (mt.MT_FP32, mt.MT_KEEP_GRADS, 0),
+                                               (mt.MT_BF16, 0, 1)])
+def test_host_delays_and_poisoned_buffers_change_nothing(dtype, flags, slots):
+    cfg = O.Config(6, 128, 2, 1, 64, 200, 300)
+    params = init_params(cfg, 41, 0.05)
+    out = []
+    hooks = (dict(), dict(MT_TEST_DELAY_H2D_US=1500, MT_TEST_DELAY_D2H_US=1500, MT_TEST_DELAY_ADAMW_US=20000,
+                          MT_TEST_POISON=1))
+    for env in hooks:
+        with _env(**env):
+            ctx = make_ctx(cfg, 2, 40, params, dtype=dtype, flags=flags, ring_slots=slots)
+        with ctx:
+            out.append(_run_cached_steps(ctx, 3, 41, 2, 40, cfg.vocab, len(params)))
+    (l0, t0, s0), (l1, t1, s1) = out
+    assert l0 == l1
+    for a, b in zip(t0 + s0, t1 + s1):
+        np.testing.assert_array_equal(a, b)
+    assert all(np.isfinite(x).all() for x in s1)
+
+
+# ---------------------------------------------------------------------------
+# A host wait beyond cfg.wait_timeout_ms: every AdamW held for 1.5 s against
+# a 250 ms limit. The step returns MT_ETIMEOUT naming what it waited for, the
+# context refuses further steps, and its state can still be read and freed.
+
+@pytest.mark.parametrize("flags,slots,steps,expect", [
+    (mt.MT_KEEP_GRADS, 0, 1, "AdamW updates still running"),
+    (0, 1, 1, "no free staging slot"),
+    (mt.MT_OVERLAP_OPT | mt.MT_KEEP_GRADS, 0, 2, "AdamW update"),
+])
+def test_wait_timeout(flags, slots, steps, expect):
+    cfg = O.Config(4, 128, 2, 1, 64, 200, 300)
+    params = init_params(cfg, 43, 0.05)
+    with _env(MT_TEST_DELAY_ADAMW_US=1500000):
+        c = mt.make_config(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn_dim,
+                           cfg.vocab, 2, 40, dtype=mt.MT_BF16, flags=flags, host_threads=4,
+                           grad_ring_slots=slots, wait_timeout_ms=250)
+        ctx = mt.Context(c, params)
+    with ctx:
+        tok, tgt = synth.token_batch(43, 2, 40, cfg.vocab)
+        for _ in range(steps - 1):
+            ctx.train_step(tok, tgt)
+        with pytest.raises(mt.MTError) as e:
+            ctx.train_step(tok, tgt)
+        assert e.value.code == mt.MT_ETIMEOUT
+        assert expect in str(e.value), str(e.value)
+        with pytest.raises(mt.MTError) as e2:
+            ctx.train_step(tok, tgt)
+        assert e2.value.code == mt.MT_ESTATE
+        assert np.all(np.isfinite(ctx.params(1)))
+
+
+def test_trace_dump_is_chrome_json_in_schedule_order(tmp_path):
+    import json
+    cfg = O.Config(4, 128, 2, 1, 64, 200, 300)
+    L = cfg.n_layers
+    with make_ctx(cfg, 2, 40, init_params(cfg, 3, 0.05), flags=mt.MT_KEEP_GRADS | mt.MT_TRACE) as ctx:
+        tok, tgt = synth.token_batch(3, 2, 40, cfg.vocab)
+        ctx.train_step(tok, tgt)
+        path = str(tmp_path / "trace.json")
+        ctx.trace_dump(path)
+        sched = ctx.schedule()
+    with open(path) as f:
+        ev = json.load(f)["traceEvents"]
+    names = {e["tid"]: e["args"]["name"] for e in ev if e["ph"] == "M"}
+    assert names[0] == "copy-in" and names[1] == "compute" and names[2] == "copy-out"
+    spans = [e for e in ev if e["ph"] == "X"]
+    assert len(spans) == len(sched)
+    comp = [e["name"] for e in sorted((e for e in spans if e["tid"] == 1), key=lambda e: e["ts"])]
+    assert comp == [f"fwd layer {l}" for l in range(L)] + ["head head"] + \
+        [f"bwd layer {l}" for l in reversed(range(L))]
+    for e in spans:
+        assert e["dur"] >= 0
+    grads = [e["name"] for e in sorted((e for e in spans if e["tid"] == 2), key=lambda e: e["ts"])]
+    assert grads == ["grad head"] + [f"grad layer {l}" for l in reversed(range(L))]
