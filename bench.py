@@ -34,12 +34,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_context(w, dtype, seed, flags, host_threads=0, chunk_rows=0, ckpt_host=0, buffers=2):
+def build_context(w, dtype, seed, flags, host_threads=0, chunk_rows=0, ckpt_host=0, buffers=2, micro_batches=0):
     from host_memory_streamed_amd import mt, synth
     cfg = mt.make_config(w.n_layers, w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn_dim, w.vocab,
                          w.batch, w.seq, dtype=dtype, n_layer_buffers=buffers,
                          host_threads=host_threads,
-                         flags=flags, chunk_rows=chunk_rows, ckpt_host=ckpt_host)
+                         flags=flags, chunk_rows=chunk_rows, ckpt_host=ckpt_host, micro_batches=micro_batches)
     t0 = time.perf_counter()
     ctx = mt.Context(cfg)
     log(f"context created in {time.perf_counter() - t0:.1f}s; device bytes {ctx.device_bytes() / 1e9:.2f} GB; "
@@ -103,9 +103,13 @@ def link_probe(mib=1024, reps=3):
     return out
 
 
-def fit_layers(w, dtype, flags, share=0.85):
+def fit_layers(w, dtype, flags, share=0.85, device_free=None):
     """The most layers of w (at most its own count) whose host store, as the
-    library sizes it, takes at most `share` of the memory available now."""
+    library sizes it, takes at most `share` of the memory available now.
+    Residual checkpoints that would not fit in device memory are parked in
+    host memory (one pageable slab each, plus two pinned bounce slabs): they
+    count too, estimating that the layer workspace leaves 70% of the free
+    device memory to checkpoint slots."""
     from host_memory_streamed_amd import mt
     avail = None
     with open("/proc/meminfo") as f:
@@ -119,7 +123,19 @@ def fit_layers(w, dtype, flags, share=0.85):
         cfg = mt.make_config(L, w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn_dim, w.vocab,
                              w.batch, w.seq, dtype=dtype, flags=flags)
         hb = mt.host_bytes(cfg)
-        if hb["pinned"] + hb["pageable"] > share * avail:
+        parked = 0
+        if device_free:
+            # the library keeps as many checkpoint slots on the device as fit
+            # next to its fixed part (1 GiB margin) and parks the rest, each
+            # in a host slab, through two pinned bounce slabs
+            plan = mt.device_plan(cfg)
+            slot = plan["ckpt_slot"]
+            fit = (device_free - (1 << 30) - plan["fixed"]) // slot
+            if fit < L + 1:
+                if L < 3 or fit < 2:
+                    break
+                parked = (L - fit + 2) * slot
+        if hb["pinned"] + hb["pageable"] + parked > share * avail:
             break
         best = L
     return max(best, 1)
@@ -233,7 +249,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="14b", help="tiny | 1.3b | 14b | 120b (120b: --layers)")
+    ap.add_argument("--workload", default="14b",
+                    help="tiny | 1.3b | 14b | 7b-512k | 7b-1m | 120b (120b and 7b-1m: cut to fit, or --layers)")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--batch", type=int, default=None,
                     help="override the batch (sequences per step): more tokens per streamed byte")
@@ -255,6 +272,11 @@ def main():
     ap.add_argument("--no-refresh", action="store_true",
                     help="with a device cache, fetch cached units in the next forward instead of refreshing them "
                          "in the backward")
+    ap.add_argument("--bf16-grads", action="store_true",
+                    help="gradients cross the host link as bf16 (a measured variant; the default keeps them fp32)")
+    ap.add_argument("--micro-batches", type=int, default=0,
+                    help="run each streamed unit over the batch in this many micro-batches, summing the weight "
+                         "gradients on the device (one weight stream per step)")
     ap.add_argument("--progress", action="store_true",
                     help="print a line as each layer of a step finishes (for steps that take minutes)")
     ap.add_argument("--no-link-probe", action="store_true",
@@ -278,23 +300,25 @@ def main():
     w = mt.WORKLOADS[args.workload]
     dtype = mt.MT_BF16 if args.dtype == "bf16" else mt.MT_FP32
     flags = mt.MT_KERNEL_TIMING | mt.MT_TRACE | (0 if args.sync_opt else mt.MT_OVERLAP_OPT) | \
-        (mt.MT_PROGRESS if args.progress else 0) | (mt.MT_CACHE_NO_REFRESH if args.no_refresh else 0)
+        (mt.MT_PROGRESS if args.progress else 0) | (mt.MT_CACHE_NO_REFRESH if args.no_refresh else 0) | \
+        (mt.MT_BF16_GRADS if args.bf16_grads else 0)
     layers_note = None
     if args.batch:
         w = mt.Workload(**{**w.__dict__, "batch": args.batch})
     if args.layers:
         w = mt.Workload(**{**w.__dict__, "n_layers": args.layers})
-    elif args.workload == "120b":
-        # the 120B-shaped workload keeps its per-layer shape and is cut to the
-        # layers whose host store fits in this machine's RAM
-        L = fit_layers(w, dtype, flags)
+    elif args.workload in ("120b", "7b-1m"):
+        # the 120B-shaped and the million-token workloads keep their layer
+        # shape and are cut to the layers whose host store (and parked
+        # checkpoints) fit in this machine's RAM
+        L = fit_layers(w, dtype, flags, device_free=torch.cuda.mem_get_info()[0])
         if L < w.n_layers:
-            layers_note = f"cut from {w.n_layers} to {L} layers to fit host RAM"
+            layers_note = f"cut from {w.n_layers} to {L} layers to fit host RAM and device memory"
             log(layers_note)
             w = mt.Workload(**{**w.__dict__, "n_layers": L})
     buffers = w.n_layers + 1 if args.resident else min(max(2, args.layer_buffers), w.n_layers + 1)
     ctx = build_context(w, dtype, args.seed, flags, chunk_rows=args.chunk_rows, ckpt_host=args.ckpt_host,
-                        buffers=buffers)
+                        buffers=buffers, micro_batches=args.micro_batches)
     layout = ctx.layout_info()
     tokens, targets = synth.token_batch(args.seed, w.batch, w.seq, w.vocab)
     M = w.batch * w.seq
@@ -376,6 +400,8 @@ def main():
                    "master": "fp32 p/m/v in host memory", "parallelism": "none (1 GPU)",
                    "optimizer": ("host AdamW, each update landing before its step returns" if args.sync_opt else
                                  "host AdamW, updates finishing during the next step's forward in load order"),
+                   "grad_transfer": "bf16" if args.bf16_grads else "fp32",
+                   **({"micro_batches": args.micro_batches} if args.micro_batches > 1 else {}),
                    **layout},
         "mfu": round(mfu, 4),
         "host_link": {

@@ -212,7 +212,7 @@ static void free_ctx(Ctx* c) {
   for (auto* p : c->ck_host) host_free_plain(p, (size_t)c->M_max * c->D.d * 4);
   for (auto* p : c->bounce)
     if (p) hipHostFree(p);
-  for (void* p : {(void*)c->x0_host, (void*)c->dx0_host, (void*)c->tgt_host, (void*)c->loss_host})
+  for (void* p : {(void*)c->x0_host, (void*)c->tgt_host, (void*)c->loss_host})
     if (p) hipHostFree(p);
   for (void* p : c->dev_allocs) hipFree(p);
   for (auto e : c->kt.ev) hipEventDestroy(e);
@@ -268,18 +268,37 @@ void mt_destroy(mt_ctx* ctx) {
     }                                                                                       \
   } while (0)
 
-int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, const mt_device_env* env,
-              mt_ctx** out) {
-  if (!out) return set_error(nullptr, MT_EINVAL, "out is NULL");
-  *out = nullptr;
-  std::string why;
-  if (validate(cfg, why)) return set_error(nullptr, MT_EINVAL, why);
-  int ndev = 0;
-  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1)
-    return set_error(nullptr, MT_EHIP, "no HIP device available");
 
-  mt_ctx* h = new mt_ctx();
-  Ctx& c = h->c;
+// Device memory of a context: malloc (each piece from hipMalloc), region
+// (carved in order from a caller's block, 256-byte aligned) or count (sizes
+// only, for planning without a device).
+struct DevAlloc {
+  enum Mode { MALLOC, REGION, COUNT } mode = MALLOC;
+  Ctx* c = nullptr;
+  char* base = nullptr;
+  size_t cap = 0, used = 0;
+  bool take(size_t bytes, void** p) {
+    bytes = (std::max<size_t>(bytes, 1) + 255) / 256 * 256;
+    if (mode == COUNT) {
+      *p = nullptr;
+      used += bytes;
+      return true;
+    }
+    if (mode == REGION) {
+      if (used + bytes > cap) return false;
+      *p = base + used;
+    } else {
+      if (hipMalloc(p, bytes) != hipSuccess) return false;
+      c->dev_allocs.push_back(*p);
+    }
+    used += bytes;
+    c->dev_bytes += (int64_t)bytes;
+    return true;
+  }
+};
+
+// Dimensions, buffer assignment, batch and micro-batch rows, unit layouts.
+static void setup_layout(Ctx& c, const mt_model_cfg* cfg) {
   c.cfg = *cfg;
   c.D = make_dims(*cfg);
   c.dtype = cfg->compute_dtype;
@@ -289,91 +308,24 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
     c.nbuf = cfg->n_layer_buffers;
     c.ncache = c.nbuf - 2;
   }
-  c.dev_current.assign(c.D.L + 1, 0);
   c.M_max = (int64_t)cfg->max_batch * cfg->max_seq;
-  {
-    const int k = std::max(1, cfg->micro_batches);
-    c.mb_seqs = (cfg->max_batch + k - 1) / k;
-    c.M_ws = (int64_t)c.mb_seqs * cfg->max_seq;
-  }
-  c.tensors = tensor_table(c.D);
-  c.pool = new Pool(default_threads(cfg->host_threads));
-  c.delay_h2d_us = env_int("MT_TEST_DELAY_H2D_US");
-  c.delay_d2h_us = env_int("MT_TEST_DELAY_D2H_US");
-  c.delay_adamw_us = env_int("MT_TEST_DELAY_ADAMW_US");
-  c.poison = env_int("MT_TEST_POISON") != 0;
+  const int k = std::max(1, cfg->micro_batches);
+  c.mb_seqs = (cfg->max_batch + k - 1) / k;
+  c.M_ws = (int64_t)c.mb_seqs * cfg->max_seq;
+  c.units.resize(c.D.L + 2);
+  for (int l = 0; l < c.D.L; ++l) c.units[l].lay = layer_layout(c.D);
+  c.units[c.D.L].lay = head_layout(c.D);
+  c.units[c.D.L + 1].lay = emb_layout(c.D);
+}
+
+// Layer buffers, gradient buffers and the activation workspace (everything
+// on the device but the residual checkpoints).
+static bool alloc_device(Ctx& c, DevAlloc& A) {
+  const mt_model_cfg* cfg = &c.cfg;
   const Dims& D = c.D;
-  const bool keep = cfg->flags & MT_KEEP_GRADS;
   const int S = c.dtype;
-
-  // ---- host store ----
-  c.units.resize(D.L + 2);
-  for (int l = 0; l < D.L; ++l) c.units[l].lay = layer_layout(D);
-  c.units[D.L].lay = head_layout(D);
-  c.units[D.L + 1].lay = emb_layout(D);
-  for (int i = 0; i < D.L + 2; ++i) {
-    Unit& u = c.units[i];
-    const bool streamed = i <= D.L;
-    const size_t nb = (size_t)u.lay.n * 4;
-    if (streamed && S == 0) {
-      HIP_OR(hipHostMalloc((void**)&u.p, nb, hipHostMallocDefault), MT_EHOSTOOM, "pinned master allocation");
-      u.p_pinned = true;
-    } else {
-      u.p = (float*)host_alloc_plain(nb);
-    }
-    u.m = (float*)host_alloc_plain(nb);
-    u.v = (float*)host_alloc_plain(nb);
-    if (!u.p || !u.m || !u.v) { mt_destroy(h); return set_error(nullptr, MT_EHOSTOOM, "host allocation failed"); }
-    if (streamed && keep) HIP_OR(hipHostMalloc((void**)&u.g, nb, hipHostMallocDefault), MT_EHOSTOOM, "pinned gradient allocation");
-    if (!streamed) {
-      u.g = (float*)host_alloc_plain(nb);
-      if (!u.g) { mt_destroy(h); return set_error(nullptr, MT_EHOSTOOM, "host allocation failed"); }
-    }
-    if (streamed && S == 1)
-      HIP_OR(hipHostMalloc(&u.shadow, u.lay.image_bytes(S), hipHostMallocDefault), MT_EHOSTOOM, "pinned shadow allocation");
-  }
-  int64_t max_unit = std::max(c.units[0].lay.n, c.units[D.L].lay.n);
-  if (staged_grads(*cfg)) {
-    const std::vector<int64_t> sizes = ring_sizes(*cfg, c.units[0].lay.n, c.units[D.L].lay.n);
-    if (cfg->flags & MT_OVERLAP_OPT) c.head_slot = (int)sizes.size() - 1;
-    for (int64_t n : sizes) {
-      float* p = nullptr;
-      HIP_OR(hipHostMalloc((void**)&p, (size_t)n * grad_bytes(*cfg), hipHostMallocDefault), MT_EHOSTOOM,
-             "pinned gradient ring");
-      c.ring_slot.push_back(p);
-      c.ring_elems.push_back(n);
-    }
-  }
-  c.slot_busy.assign(c.ring_slot.size(), 0);
-  c.unit_busy.assign(D.L + 2, 0);
-  c.adam_end.assign(D.L + 2, std::chrono::steady_clock::time_point{});
-  HIP_OR(hipHostMalloc((void**)&c.x0_host, (size_t)c.M_max * D.d * 4, hipHostMallocDefault), MT_EHOSTOOM, "pinned staging");
-  HIP_OR(hipHostMalloc((void**)&c.dx0_host, (size_t)c.M_max * D.d * 4, hipHostMallocDefault), MT_EHOSTOOM, "pinned staging");
-  HIP_OR(hipHostMalloc((void**)&c.tgt_host, (size_t)c.M_max * 4, hipHostMallocDefault), MT_EHOSTOOM, "pinned staging");
-  HIP_OR(hipHostMalloc((void**)&c.loss_host, (size_t)c.M_max * 4, hipHostMallocDefault), MT_EHOSTOOM, "pinned staging");
-  // pinned memory is not guaranteed to be zero: clear p, images and kept gradients
-  for (int i = 0; i <= D.L; ++i) {
-    Unit& u = c.units[i];
-    auto clear = [&](void* p, size_t bytes) {
-      const size_t ch = 64 << 20;
-      c.pool->run((int64_t)((bytes + ch - 1) / ch), [&](int64_t j) {
-        const size_t a = (size_t)j * ch, b = std::min(bytes, a + ch);
-        std::memset(static_cast<char*>(p) + a, 0, b - a);
-      });
-    };
-    if (u.p_pinned) clear(u.p, (size_t)u.lay.n * 4);
-    if (u.shadow) clear(u.shadow, u.lay.image_bytes(S));
-    if (u.g) clear(u.g, (size_t)u.lay.n * 4);
-  }
-
-  // ---- device ----
-  auto dalloc = [&](size_t bytes, void** p) -> bool {
-    if (bytes == 0) bytes = 256;
-    if (hipMalloc(p, bytes) != hipSuccess) return false;
-    c.dev_allocs.push_back(*p);
-    c.dev_bytes += (int64_t)bytes;
-    return true;
-  };
+  const int64_t max_unit = std::max(c.units[0].lay.n, c.units[D.L].lay.n);
+  auto dalloc = [&](size_t bytes, void** p) -> bool { return A.take(bytes, p); };
   bool ok = true;
   // streaming buffers fit any unit that streams through them; a cached
   // unit's buffer fits that unit
@@ -441,17 +393,133 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
   const int half = D.hd / 2;
   ok &= dalloc((size_t)cfg->max_seq * half * 4, (void**)&w.rope_cos);
   ok &= dalloc((size_t)cfg->max_seq * half * 4, (void**)&w.rope_sin);
-  if (!ok) { mt_destroy(h); return set_error(nullptr, MT_EDEVOOM, "device allocation failed"); }
+  return ok;
+}
+
+
+int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, const mt_device_env* env,
+              mt_ctx** out) {
+  if (!out) return set_error(nullptr, MT_EINVAL, "out is NULL");
+  *out = nullptr;
+  std::string why;
+  if (validate(cfg, why)) return set_error(nullptr, MT_EINVAL, why);
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1)
+    return set_error(nullptr, MT_EHIP, "no HIP device available");
+
+  if (env && env->workspace && (((uintptr_t)env->workspace & 255) || env->workspace_bytes <= 0))
+    return set_error(nullptr, MT_EINVAL, "env workspace must be 256-byte aligned with workspace_bytes > 0");
+
+  mt_ctx* h = new mt_ctx();
+  Ctx& c = h->c;
+  setup_layout(c, cfg);
+  c.dev_current.assign(c.D.L + 1, 0);
+  c.tensors = tensor_table(c.D);
+  c.pool = new Pool(default_threads(cfg->host_threads));
+  c.delay_h2d_us = env_int("MT_TEST_DELAY_H2D_US");
+  c.delay_d2h_us = env_int("MT_TEST_DELAY_D2H_US");
+  c.delay_adamw_us = env_int("MT_TEST_DELAY_ADAMW_US");
+  c.poison = env_int("MT_TEST_POISON") != 0;
+  const Dims& D = c.D;
+  const bool keep = cfg->flags & MT_KEEP_GRADS;
+  const int S = c.dtype;
+
+  // ---- host store ----
+  for (int i = 0; i < D.L + 2; ++i) {
+    Unit& u = c.units[i];
+    const bool streamed = i <= D.L;
+    const size_t nb = (size_t)u.lay.n * 4;
+    if (streamed && S == 0) {
+      HIP_OR(hipHostMalloc((void**)&u.p, nb, hipHostMallocDefault), MT_EHOSTOOM, "pinned master allocation");
+      u.p_pinned = true;
+    } else {
+      u.p = (float*)host_alloc_plain(nb);
+    }
+    u.m = (float*)host_alloc_plain(nb);
+    u.v = (float*)host_alloc_plain(nb);
+    if (!u.p || !u.m || !u.v) { mt_destroy(h); return set_error(nullptr, MT_EHOSTOOM, "host allocation failed"); }
+    if (streamed && keep) HIP_OR(hipHostMalloc((void**)&u.g, nb, hipHostMallocDefault), MT_EHOSTOOM, "pinned gradient allocation");
+    if (!streamed) {
+      u.g = (float*)host_alloc_plain(nb);
+      if (!u.g) { mt_destroy(h); return set_error(nullptr, MT_EHOSTOOM, "host allocation failed"); }
+    }
+    if (streamed && S == 1)
+      HIP_OR(hipHostMalloc(&u.shadow, u.lay.image_bytes(S), hipHostMallocDefault), MT_EHOSTOOM, "pinned shadow allocation");
+  }
+  int64_t max_unit = std::max(c.units[0].lay.n, c.units[D.L].lay.n);
+  if (staged_grads(*cfg)) {
+    const std::vector<int64_t> sizes = ring_sizes(*cfg, c.units[0].lay.n, c.units[D.L].lay.n);
+    if (cfg->flags & MT_OVERLAP_OPT) c.head_slot = (int)sizes.size() - 1;
+    for (int64_t n : sizes) {
+      float* p = nullptr;
+      HIP_OR(hipHostMalloc((void**)&p, (size_t)n * grad_bytes(*cfg), hipHostMallocDefault), MT_EHOSTOOM,
+             "pinned gradient ring");
+      c.ring_slot.push_back(p);
+      c.ring_elems.push_back(n);
+    }
+  }
+  c.slot_busy.assign(c.ring_slot.size(), 0);
+  c.unit_busy.assign(D.L + 2, 0);
+  c.adam_end.assign(D.L + 2, std::chrono::steady_clock::time_point{});
+  // x0 (gathered embedding rows, host -> device at the start of the step and,
+  // with parked checkpoints, again before layer 0's backward) and dx0 (layer
+  // 0's input gradient, device -> host after that backward) are never live
+  // together: one pinned slab serves both
+  HIP_OR(hipHostMalloc((void**)&c.x0_host, (size_t)c.M_max * D.d * 4, hipHostMallocDefault), MT_EHOSTOOM, "pinned staging");
+  c.dx0_host = c.x0_host;
+  HIP_OR(hipHostMalloc((void**)&c.tgt_host, (size_t)c.M_max * 4, hipHostMallocDefault), MT_EHOSTOOM, "pinned staging");
+  HIP_OR(hipHostMalloc((void**)&c.loss_host, (size_t)c.M_max * 4, hipHostMallocDefault), MT_EHOSTOOM, "pinned staging");
+  // pinned memory is not guaranteed to be zero: clear p, images and kept gradients
+  for (int i = 0; i <= D.L; ++i) {
+    Unit& u = c.units[i];
+    auto clear = [&](void* p, size_t bytes) {
+      const size_t ch = 64 << 20;
+      c.pool->run((int64_t)((bytes + ch - 1) / ch), [&](int64_t j) {
+        const size_t a = (size_t)j * ch, b = std::min(bytes, a + ch);
+        std::memset(static_cast<char*>(p) + a, 0, b - a);
+      });
+    };
+    if (u.p_pinned) clear(u.p, (size_t)u.lay.n * 4);
+    if (u.shadow) clear(u.shadow, u.lay.image_bytes(S));
+    if (u.g) clear(u.g, (size_t)u.lay.n * 4);
+  }
+
+  // ---- device ----
+  DevAlloc A;
+  A.c = &c;
+  if (env && env->workspace) {
+    A.mode = DevAlloc::REGION;
+    A.base = static_cast<char*>(env->workspace);
+    A.cap = (size_t)env->workspace_bytes;
+  }
+  if (!alloc_device(c, A)) {
+    mt_destroy(h);
+    return set_error(nullptr, MT_EDEVOOM, A.mode == DevAlloc::REGION
+                                              ? "env workspace smaller than the layer buffers and the workspace "
+                                                "(see mt_device_plan)"
+                                              : "device allocation failed");
+  }
+  bool ok = true;
+  Workspace& w = c.ws;
+  const int64_t Mb = c.M_max, d = D.d;
+  const int half = D.hd / 2;
 
   // ---- residual checkpoints: device slots, parking the rest in host memory ----
   {
     const size_t slot = (size_t)Mb * d * 4;
     int k = cfg->ckpt_host;
     if (k == 0) {
-      size_t free_b = 0, total_b = 0;
-      HIP_OR(hipMemGetInfo(&free_b, &total_b), MT_EHIP, "hipMemGetInfo");
-      const size_t margin = (size_t)1 << 30;
-      const int64_t fit = free_b > margin ? (int64_t)((free_b - margin) / slot) : 0;
+      // free device memory (or what the caller's workspace has left), less a
+      // margin for the runtime when allocating
+      size_t free_b = 0, total_b = 0, margin = 0;
+      if (A.mode == DevAlloc::REGION) {
+        free_b = A.cap - A.used;
+      } else {
+        HIP_OR(hipMemGetInfo(&free_b, &total_b), MT_EHIP, "hipMemGetInfo");
+        margin = (size_t)1 << 30;
+      }
+      const size_t slot_a = (slot + 255) / 256 * 256;
+      const int64_t fit = free_b > margin ? (int64_t)((free_b - margin) / slot_a) : 0;
       if (fit < D.L + 1) {
         if (D.L < 3 || fit < 2) {
           mt_destroy(h);
@@ -463,10 +531,10 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
     c.ck_nh = k > 0 ? k + 3 : 0;
     const int dev_slots = D.L + 1 - c.ck_nh;
     if (k > 0) {
-      ok &= dalloc(slot, (void**)&c.stage[0]);
-      ok &= dalloc(slot, (void**)&c.stage[1]);
+      ok &= A.take(slot, (void**)&c.stage[0]);
+      ok &= A.take(slot, (void**)&c.stage[1]);
     }
-    ok &= dalloc(slot * (size_t)dev_slots, (void**)&c.ckpt);
+    ok &= A.take(slot * (size_t)dev_slots, (void**)&c.ckpt);
     if (!ok) { mt_destroy(h); return set_error(nullptr, MT_EDEVOOM, "device allocation of residual checkpoints failed"); }
     for (int i = 0; i < k; ++i) {
       float* p = (float*)host_alloc_plain(slot);
@@ -510,6 +578,20 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs, cons
   return MT_OK;
 }
 
+int mt_device_plan(const mt_model_cfg* cfg, int64_t* fixed_bytes, int64_t* ckpt_slot_bytes) {
+  std::string why;
+  if (validate(cfg, why)) return set_error(nullptr, MT_EINVAL, why);
+  Ctx c;
+  setup_layout(c, cfg);
+  DevAlloc A;
+  A.mode = DevAlloc::COUNT;
+  A.c = &c;
+  alloc_device(c, A);
+  if (fixed_bytes) *fixed_bytes = (int64_t)A.used;
+  if (ckpt_slot_bytes) *ckpt_slot_bytes = ((int64_t)c.M_max * c.D.d * 4 + 255) / 256 * 256;
+  return MT_OK;
+}
+
 int mt_host_bytes(const mt_model_cfg* cfg, int64_t* state_bytes, int64_t* pinned_bytes,
                   int64_t* pageable_bytes, int64_t* parked_ckpt_bytes) {
   std::string why;
@@ -534,7 +616,7 @@ int mt_host_bytes(const mt_model_cfg* cfg, int64_t* state_bytes, int64_t* pinned
   unit(el, false);
   if (staged_grads(*cfg))
     for (int64_t n : ring_sizes(*cfg, ll.n, hl.n)) pinned += n * grad_bytes(*cfg);
-  pinned += 2 * M * D.d * 4 + 2 * M * 4;             // x0 / dx0, targets / losses staging
+  pinned += M * D.d * 4 + 2 * M * 4;                 // x0 and dx0 (one slab), targets / losses staging
   if (state_bytes) *state_bytes = state;
   if (pinned_bytes) *pinned_bytes = pinned;
   if (pageable_bytes) *pageable_bytes = pageable;

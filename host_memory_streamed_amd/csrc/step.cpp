@@ -854,9 +854,12 @@ int train_step_impl(Ctx& c, StepEvents& E, const int32_t* tokens, const int32_t*
   st.h2d_bytes = h2d_bytes;
   st.d2h_bytes = d2h_bytes;
   st.adamw_ms = (double)(c.adam_ns.load() - adam_ns0) * 1e-6;
-  int64_t n_all = 0;
-  for (auto& u : c.units) n_all += u.lay.n;
-  st.adamw_bytes = (double)n_all * (16.0 + 12.0 + (c.dtype ? 2.0 : 0.0));
+  // read p, m, v, g; write p, m, v (+ the bf16 image of streamed units; +
+  // the widened fp32 gradient when bf16 gradients are kept). The embedding's
+  // gradient is formed on the host in fp32 and has no device image.
+  const double n_emb = (double)c.emb().lay.n, n_str = (double)(L + 0) * c.units[0].lay.n + c.head().lay.n;
+  st.adamw_bytes = n_emb * 28.0 +
+                   n_str * (12.0 + (double)gbytes + 12.0 + (c.dtype ? 2.0 : 0.0) + (g16 && keep ? 4.0 : 0.0));
   st.tail_ms = step_ms - last_land_ms;
   st.tokens = M;
   {

@@ -43,7 +43,8 @@ class ModelConfig(ctypes.Structure):
 
 
 class DeviceEnv(ctypes.Structure):
-    _fields_ = [("copy_in", ctypes.c_void_p), ("compute", ctypes.c_void_p), ("copy_out", ctypes.c_void_p)]
+    _fields_ = [("copy_in", ctypes.c_void_p), ("compute", ctypes.c_void_p), ("copy_out", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64)]
 
 
 class StepStats(ctypes.Structure):
@@ -74,6 +75,7 @@ _SIGS = {
                                      ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "mt_tensor_info": (ctypes.c_int, [ctypes.POINTER(ModelConfig), _I32, ctypes.c_char_p, _I32,
                                       ctypes.POINTER(_I64), ctypes.POINTER(_I32)]),
+    "mt_device_plan": (ctypes.c_int, [ctypes.POINTER(ModelConfig), ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "mt_create": (ctypes.c_int, [ctypes.POINTER(ModelConfig), _P, ctypes.POINTER(DeviceEnv), ctypes.POINTER(_P)]),
     "mt_set_param": (ctypes.c_int, [_P, _I32, _P]),
     "mt_train_step": (ctypes.c_int, [_P, _P, _P, _I32, _I32, ctypes.POINTER(_F)]),
@@ -174,6 +176,14 @@ def host_bytes(cfg: ModelConfig) -> dict:
     return {"state": st.value, "pinned": pin.value, "pageable": pag.value, "parked_ckpt": ck.value}
 
 
+def device_plan(cfg: ModelConfig) -> dict:
+    """Device memory a context of cfg takes (no GPU needed): the fixed part
+    and one residual checkpoint slot."""
+    fixed, slot = _I64(), _I64()
+    _check(lib().mt_device_plan(ctypes.byref(cfg), ctypes.byref(fixed), ctypes.byref(slot)))
+    return {"fixed": fixed.value, "ckpt_slot": slot.value}
+
+
 def tensor_table(cfg: ModelConfig):
     """[(name, shape)] in the canonical order, as the library reports it."""
     out = []
@@ -189,7 +199,7 @@ def tensor_table(cfg: ModelConfig):
 class Context:
     """One training context (mt_create ... mt_destroy)."""
 
-    def __init__(self, cfg: ModelConfig, params=None, streams=None):
+    def __init__(self, cfg: ModelConfig, params=None, streams=None, workspace=None):
         self.cfg = cfg
         self.table = tensor_table(cfg)
         h = _P()
@@ -198,8 +208,12 @@ class Context:
             keep = [np.ascontiguousarray(p, dtype=np.float32) for p in params]   # alive during the call
             arr = (_P * len(keep))(*[k.ctypes.data for k in keep])
         env = None
-        if streams is not None:
-            env = DeviceEnv(*streams)
+        if streams is not None or workspace is not None:
+            st = tuple(streams) if streams is not None else (None, None, None)
+            ws_ptr, ws_bytes = (None, 0)
+            if workspace is not None:
+                ws_ptr, ws_bytes = _ptr(workspace[0]), int(workspace[1])
+            env = DeviceEnv(*st, ws_ptr, ws_bytes)
         rc = lib().mt_create(ctypes.byref(cfg), ctypes.cast(arr, _P) if arr is not None else None,
                              ctypes.byref(env) if env is not None else None, ctypes.byref(h))
         _check(rc, None)
@@ -422,5 +436,7 @@ WORKLOADS = {
     "1.3b": Workload("1.3b", 24, 2048, 16, 16, 128, 5632, 32000, 4, 2048),
     "14b": Workload("14b", 48, 5120, 40, 8, 128, 13824, 152064, 1, 4096),
     "7b-512k": Workload("7b-512k", 32, 4096, 32, 32, 128, 11008, 32000, 1, 524288),
+    # the same decoder at twice the context (1048576 tokens), past the pages' 512k
+    "7b-1m": Workload("7b-1m", 32, 4096, 32, 32, 128, 11008, 32000, 1, 1048576),
     "120b": Workload("120b", 88, 10240, 80, 8, 128, 28672, 128000, 1, 4096),
 }

@@ -117,9 +117,11 @@ typedef struct mt_model_cfg {
    * max_batch * max_seq rows would exceed 4 GiB). Weight gradients sum the
    * chunks in order, so a different chunk size changes their rounding. */
   int32_t chunk_rows;
-  /* Residual checkpoints x_1..x_k (layer inputs) parked in pinned host memory
-   * between the forward and the backward instead of device memory; each
-   * parked one crosses the host link once each way. 0 = automatic (none
+  /* Residual checkpoints x_1..x_k (layer inputs) parked in host memory
+   * between the forward and the backward instead of device memory: each in
+   * a pageable slab of its own, crossing the host link once each way through
+   * one of two pinned bounce slabs (the worker pool copies between a bounce
+   * slab and the parked slab). 0 = automatic (none
    * unless the device cannot hold all L + 1 of them next to the workspace);
    * k in [1, n_layers - 2] = exactly k. Parking k of them frees k + 1
    * device slots (x_0 is re-sent from the gathered embedding rows). Results
@@ -155,11 +157,23 @@ typedef struct mt_model_cfg {
 } mt_model_cfg;
 
 /* Optional streams for the three pipeline stages (hipStream_t values passed as
- * void*). NULL env, or a NULL member, makes the library create its own. */
+ * void*) and device memory. NULL env, or a NULL member, makes the library
+ * create its own streams and take its device memory with hipMalloc.
+ * workspace: a caller-owned block of workspace_bytes device bytes (256-byte
+ * aligned; from a framework's allocator, for example) from which the
+ * context carves every device buffer instead (layer and gradient buffers,
+ * the activation workspace, residual checkpoint slots). It must hold at
+ * least mt_device_plan's fixed_bytes plus two checkpoint slots (or all
+ * n_layers + 1 slots when n_layers < 3); checkpoints that do not fit in the
+ * rest are parked in host memory (cfg.ckpt_host = 0). It must stay
+ * allocated, and untouched by the caller, until mt_destroy. The library
+ * takes no device memory during a step either way. */
 typedef struct mt_device_env {
   void* copy_in;
   void* compute;
   void* copy_out;
+  void* workspace;
+  int64_t workspace_bytes;
 } mt_device_env;
 
 typedef struct mt_ctx mt_ctx;
@@ -187,7 +201,18 @@ int mt_tensor_info(const mt_model_cfg* cfg, int32_t id, char* name, int32_t name
 int mt_host_bytes(const mt_model_cfg* cfg, int64_t* state_bytes, int64_t* pinned_bytes,
                   int64_t* pageable_bytes, int64_t* parked_ckpt_bytes);
 
-/* Create a context: validates cfg, allocates the host store (fp32 master p,
+/* Device memory a context of cfg takes, without a device: fixed_bytes for
+ * the layer buffers, gradient buffers and activation workspace, and
+ * ckpt_slot_bytes for each residual checkpoint slot it keeps on the device
+ * (n_layers + 1 slots when none is parked; with k parked, n_layers - k).
+ * Any output may be NULL. MT_EINVAL on a bad cfg. */
+int mt_device_plan(const mt_model_cfg* cfg, int64_t* fixed_bytes, int64_t* ckpt_slot_bytes);
+
+/* Create a context ("MegaTrain: Full Precision Training of 100B+ Parameter
+ * Large Language Models on a Single GPU", abstract: parameters and optimizer
+ * states live in host memory, the GPU is a transient compute engine; the
+ * double-buffered engine needs device buffers for layers in flight).
+ * Validates cfg, allocates the host store (fp32 master p,
  * AdamW m and v zeroed, step count 0, the bf16 device-format shadow in bf16
  * mode, gradient buffers), the device layer buffers, gradient buffers,
  * checkpoints and activation workspace, the three streams and the events.
@@ -199,14 +224,22 @@ int mt_create(const mt_model_cfg* cfg, const float* const* host_param_ptrs,
               const mt_device_env* env, mt_ctx** out);
 
 /* Copy one tensor's fp32 values into the master store and refresh its
- * device-format shadow. Valid between steps. */
+ * device-format shadow (the host store is the parameters' home, abstract
+ * above). Valid between steps; waits for updates still in flight. */
 int mt_set_param(mt_ctx* ctx, int32_t id, const float* src);
 
 /* One training step on tokens / targets, each [B, T] int32 row-major
- * (read during the call; every id must lie in [0, vocab)). Synchronous: it
- * returns after every AdamW update has landed in host memory. *loss_out is
- * the mean cross-entropy over the B*T positions. On MT_ENONFINITE the state is
- * unchanged and the step count is not advanced. */
+ * (read during the call; every id must lie in [0, vocab)): the layer-wise
+ * streamed forward, the head, recompute + backward in reverse layer order,
+ * gradients streamed out and the CPU AdamW (abstract above; "Technical
+ * Brief: MegaTrain's Single-GPU 120B-Parameter Training Breakthrough",
+ * section "Checkpointing, Manual Gradients, and CPU-Side Optimizer Steps").
+ * It returns after every AdamW update has landed in host memory, or, with
+ * MT_OVERLAP_OPT, once every gradient has (the updates then finish during
+ * the next step). *loss_out is the mean cross-entropy over the B*T
+ * positions. On MT_ENONFINITE the state is unchanged and the step count is
+ * not advanced; on MT_ETIMEOUT see cfg.wait_timeout_ms; MT_ESTATE after an
+ * earlier MT_ETIMEOUT. */
 int mt_train_step(mt_ctx* ctx, const int32_t* tokens, const int32_t* targets, int32_t B,
                   int32_t T, float* loss_out);
 
@@ -220,8 +253,11 @@ int mt_token_losses(mt_ctx* ctx, const float** ptr, int64_t* n);
 
 /* Read-only, library-owned views of the fp32 master parameters, the raw
  * gradients dL/dp of the last step (MT_ENOGRADS unless MT_KEEP_GRADS), and
- * the AdamW moments with the step count. Valid until the next
- * mt_train_step / mt_set_param / mt_destroy. */
+ * the AdamW moments with the step count: the host-resident state the
+ * technical brief's CPU-side optimizer keeps in full precision (section
+ * "Checkpointing, Manual Gradients, and CPU-Side Optimizer Steps"). Each
+ * waits for updates still in flight. Valid until the next mt_train_step /
+ * mt_set_param / mt_destroy. */
 int mt_params(mt_ctx* ctx, int32_t id, const float** ptr, int64_t* numel);
 int mt_grads(mt_ctx* ctx, int32_t id, const float** ptr, int64_t* numel);
 int mt_opt_state(mt_ctx* ctx, int32_t id, const float** m, const float** v, int64_t* t);
@@ -241,6 +277,10 @@ typedef struct mt_step_stats {
   int64_t step;            /* AdamW step count after the step */
 } mt_step_stats;
 
+/* Measurement of the last step: link bytes and copy time, compute time, the
+ * host AdamW's time and traffic (the technical brief, "Limitations of Current
+ * Throughput Metrics and Empirical Validation", names link use, host memory
+ * bandwidth and optimizer latency as what to measure). */
 int mt_stats(mt_ctx* ctx, mt_step_stats* out);
 
 /* Per-kernel-class totals of the last step (needs MT_KERNEL_TIMING), measured
@@ -279,7 +319,10 @@ typedef struct mt_sched_entry {
 
 int mt_schedule(mt_ctx* ctx, mt_sched_entry* out, int32_t cap, int32_t* n);
 
-/* Write the schedule log as Chrome trace-event JSON. */
+/* Write the schedule log as Chrome trace-event JSON: one timeline row per
+ * stream (copy-in, compute, copy-out, host AdamW, host submission), showing
+ * the overlap of prefetch, compute and gradient offload that the abstract's
+ * double-buffered engine is built for. */
 int mt_trace_dump(mt_ctx* ctx, const char* path);
 
 /* Device bytes the context holds (buffers, checkpoints, workspace). */

@@ -421,9 +421,12 @@ class StepResult:
     checkpoints: list = field(default_factory=list)   # residual stream x_0..x_L
 
 
-def gradients(params, tokens, targets, cfg: Config, mode: str = "fp32"):
+def gradients(params, tokens, targets, cfg: Config, mode: str = "fp32", progress=None):
     """Loss, per-token loss, gradients of every tensor, and the residual-stream
-    checkpoints x_0..x_L, by the plain forward and analytic backward."""
+    checkpoints x_0..x_L, by the plain forward and analytic backward.
+    progress: optional callable given a short text after each layer's
+    forward and backward and after the head (for runs that take minutes)."""
+    say = progress or (lambda text: None)
     prec = _Prec(mode)
     B, T = tokens.shape
     M = B * T
@@ -437,13 +440,16 @@ def gradients(params, tokens, targets, cfg: Config, mode: str = "fp32"):
         x, c = layer_fwd(x, _layer_weights(P, cfg, l), cfg, prec, rope, B, T)
         caches.append(c)
         ckpts.append(x)
+        say(f"oracle {mode}: layer {l} forward")
     loss, g, d_fn, d_head = head_fwd_bwd(x, P[-2], P[-1], targets.reshape(-1), cfg, prec)
+    say(f"oracle {mode}: head")
     grads = [None] * len(P)
     grads[-2], grads[-1] = d_fn, d_head
     for l in reversed(range(cfg.n_layers)):
         g, dW = layer_bwd(g, caches[l], _layer_weights(P, cfg, l), cfg, prec, rope, B, T)
         for i, n in enumerate(LAYER_TENSORS):
             grads[1 + 9 * l + i] = dW[n]
+        say(f"oracle {mode}: layer {l} backward")
     dE = np.zeros_like(P[0])
     np.add.at(dE, tok, g)
     grads[0] = dE

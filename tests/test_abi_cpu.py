@@ -168,3 +168,23 @@ def test_rmsnorm_bwd_rejects_misaligned_operands():
         a[i] = odd
         assert L.mt_op_rmsnorm_bwd(*a) == mt.MT_EINVAL
     assert mt.rmsnorm_bwd_ws_floats(4096, 5120) == 1024 * 5120
+
+
+def test_device_plan_without_a_device():
+    """The device memory plan of the 14B-shaped workload, computed on the
+    host: the fixed part (layer and gradient buffers, activation workspace)
+    and one checkpoint slot of 4096 x 5120 fp32; micro-batches shrink the
+    fixed part and leave the slot (the whole batch's residuals) alone."""
+    w = mt.WORKLOADS["14b"]
+    def plan(batch, mb):
+        c = mt.make_config(w.n_layers, w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn_dim, w.vocab,
+                           batch, w.seq, dtype=mt.MT_BF16, micro_batches=mb)
+        return mt.device_plan(c)
+    p1, p4, p4m = plan(1, 0), plan(4, 0), plan(4, 4)
+    assert p1["ckpt_slot"] == 4096 * 5120 * 4
+    assert p4["ckpt_slot"] == 4 * p1["ckpt_slot"] == p4m["ckpt_slot"]
+    # two bf16 layer buffers (the head, 1.56 GB, is the largest unit) and two
+    # fp32 gradient buffers (3.1 GB) at least
+    assert p1["fixed"] > 2 * 1.5e9 + 2 * 3.1e9
+    assert p4m["fixed"] < p4["fixed"]
+    assert p4m["fixed"] - p1["fixed"] < 0.1 * p1["fixed"]   # only the residual gradient and the losses grow

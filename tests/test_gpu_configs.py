@@ -23,44 +23,13 @@ are the workload's):
 import numpy as np
 import pytest
 
-import oracle as O
 from oracle.configs import shape
-from test_gpu_step import check_losses, compare_step, init_params, make_ctx, release_on_failure
+from test_gpu_step import init_params, make_ctx, run_parity_sampled
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 from host_memory_streamed_amd import mt, synth  # noqa: E402
-
-SAMPLE = 1 << 16
-
-
-@release_on_failure
-def run_parity_sampled(cfg, B, T, mode, steps=1, seed=0, std=0.02, **ctx_kw):
-    params = init_params(cfg, seed, std)
-    n = len(params)
-    dtype = mt.MT_BF16 if mode == "bf16" else mt.MT_FP32
-    with make_ctx(cfg, B, T, params, dtype=dtype, flags=mt.MT_KEEP_GRADS, **ctx_kw) as ctx:
-        P, M0, V0, t = params, [np.zeros(0)] * n, [np.zeros(0)] * n, 0
-        for s in range(steps):
-            tokens, targets = synth.token_batch(seed + 10 * s, B, T, cfg.vocab)
-            print(f"step {s + 1}/{steps}: gpu", flush=True)
-            loss = ctx.train_step(tokens, targets)
-            print(f"step {s + 1}/{steps}: oracle", flush=True)
-            ref_loss, ref_tl, grads, _ = O.gradients(P, tokens, targets, cfg, mode)
-            res = O.StepResult(ref_loss, ref_tl, grads, None, None, None, t + 1)
-            print(f"step {s + 1}/{steps}: compare", flush=True)
-            check_losses(mode, loss, ctx.token_losses().reshape(B, T), res)
-            if t == 0:
-                M0 = V0 = [np.zeros_like(p) for p in P]
-            compare_step(ctx, res, cfg, mode, (P, M0, V0, t), tokens, sample=SAMPLE)
-            del res, grads
-            t += 1
-            if s + 1 < steps:
-                P = [ctx.params(i) for i in range(n)]
-                M0 = [ctx.opt_state(i)[0] for i in range(n)]
-                V0 = [ctx.opt_state(i)[1] for i in range(n)]
-
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("mode", ["fp32", "bf16"])
@@ -99,7 +68,7 @@ def test_1p3b_full_depth_streamed_equals_resident(dtype):
 @pytest.mark.timeout(600)
 def test_14b_two_layers_4096_full_vocab_bf16():
     cfg, B, T = shape("14b", n_layers=2)
-    run_parity_sampled(cfg, B, T, "bf16", seed=13)
+    run_parity_sampled(cfg, B, T, "bf16", seed=13, depth="wide")
 
 
 @pytest.mark.timeout(600)
@@ -107,10 +76,10 @@ def test_7b_three_layers_8192_chunked_parked_bf16():
     cfg, _, _ = shape("7b-512k", n_layers=3)
     # three layers so that one residual checkpoint can be parked (x_1); the
     # QKV projection and the MLP run in chunks of 3000 rows (3000, 3000, 2192)
-    run_parity_sampled(cfg, 1, 8192, "bf16", seed=43, chunk_rows=3000, ckpt_host=1)
+    run_parity_sampled(cfg, 1, 8192, "bf16", seed=43, depth="wide", chunk_rows=3000, ckpt_host=1)
 
 
 @pytest.mark.timeout(600)
 def test_120b_layer_shape_two_layers_bf16():
     cfg, _, _ = shape("120b", n_layers=2)
-    run_parity_sampled(cfg, 1, 512, "bf16", seed=17)
+    run_parity_sampled(cfg, 1, 512, "bf16", seed=17, depth="wide")
