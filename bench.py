@@ -244,7 +244,52 @@ def cpu_baseline(w, vocab_share=8):
     }
 
 
+def summarize_kernel_trace(path, steps, skip, kernel_substr, flops_per_launch=None):
+    """Per-dispatch durations of one kernel from a rocprofv3 kernel trace
+    (its kernel_trace.csv): the dispatches of the last steps - skip steps
+    (the kernel's launches split evenly over the traced steps, in start
+    order), all of them and those that overlap no runtime copy kernel
+    (under kernel tracing the runtime runs each device-to-host copy as a
+    blit kernel, and a dispatch that overlaps one waits for compute units).
+    Prints a markdown summary."""
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    for r in rows:
+        r["t0"], r["t1"] = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+    copies = sorted((r["t0"], r["t1"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+    mine = sorted((r for r in rows if kernel_substr in r["Kernel_Name"]), key=lambda r: r["t0"])
+    per = len(mine) // steps
+    kept = mine[skip * per:]
+    starts = [c[0] for c in copies]
+
+    import bisect
+
+    def overlaps(r):
+        i = bisect.bisect_left(starts, r["t1"])
+        return any(copies[j][1] > r["t0"] for j in range(max(0, i - 64), i))
+    clean = [r for r in kept if not overlaps(r)]
+    avg = lambda rs: sum(r["t1"] - r["t0"] for r in rs) / max(1, len(rs)) / 1e3
+    print(f"| dispatches | count | average us |\n|---|---:|---:|")
+    print(f"| `{kernel_substr}`, {steps - skip} of {steps} traced steps | {len(kept)} | {avg(kept):.1f} |")
+    print(f"| the same, overlapping no copy kernel | {len(clean)} | {avg(clean):.1f} |")
+    if flops_per_launch:
+        for name, rs in (("all", kept), ("no copy overlap", clean)):
+            t = avg(rs) * 1e-6
+            print(f"\n{name}: {flops_per_launch / t / 1e12:.1f} TFLOP/s, frac {flops_per_launch / t / PEAK_BF16:.4f} "
+                  f"of {PEAK_BF16 / 1e12:.0f}")
+
+
 def main():
+    if "--summarize-trace" in sys.argv:
+        sp = argparse.ArgumentParser()
+        sp.add_argument("--summarize-trace", required=True, help="rocprofv3 kernel_trace.csv")
+        sp.add_argument("--trace-steps", type=int, required=True, help="steps in the traced run (warmup included)")
+        sp.add_argument("--trace-skip", type=int, default=1, help="leading steps to leave out")
+        sp.add_argument("--kernel", default="gemm_big_kernelIDF16bLi0EE", help="substring of the kernel symbol")
+        sp.add_argument("--flops-per-launch", type=float, default=None)
+        a = sp.parse_args()
+        summarize_kernel_trace(a.summarize_trace, a.trace_steps, a.trace_skip, a.kernel, a.flops_per_launch)
+        return
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
