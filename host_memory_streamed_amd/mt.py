@@ -109,6 +109,8 @@ _SIGS = {
     "mt_op_attn_bwd": (ctypes.c_int, [_I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
     "mt_op_attn_bwd_rope": (ctypes.c_int, [_I32, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                            _P]),
+    "mt_op_attn_bwd_rope_noalloc": (ctypes.c_int, [_I32, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                                   _P]),
     "mt_op_swiglu_fwd": (ctypes.c_int, [_I32, _P, _P, _I64, _I32, _P]),
     "mt_op_swiglu_bwd": (ctypes.c_int, [_I32, _P, _P, _P, _I64, _I32, _P]),
     "mt_op_xent": (ctypes.c_int, [_I32, _P, _P, _P, _P, _I64, _I32, _F, _P]),
@@ -380,6 +382,12 @@ def attn_bwd(dtype, qkv, o, dout, lse, dqkv, ws, B, T, H, Hkv, hd, stream=None):
 def attn_bwd_rope(dtype, qkv, o, dout, lse, cos, sin, dqkv, ws, B, T, H, Hkv, hd, stream=None):
     _check(lib().mt_op_attn_bwd_rope(dtype, _ptr(qkv), _ptr(o), _ptr(dout), _ptr(lse), _ptr(cos), _ptr(sin),
                                      _ptr(dqkv), _ptr(ws), B, T, H, Hkv, hd, _stream(stream)))
+
+
+def attn_bwd_rope_noalloc(dtype, qkv, o, dout, lse, cos, sin, dqkv, B, T, H, Hkv, hd, stream=None):
+    """mt_op_attn_bwd_rope with the library's static scratch (no workspace)."""
+    _check(lib().mt_op_attn_bwd_rope_noalloc(dtype, _ptr(qkv), _ptr(o), _ptr(dout), _ptr(lse), _ptr(cos),
+                                             _ptr(sin), _ptr(dqkv), B, T, H, Hkv, hd, _stream(stream)))
 
 
 def swiglu_fwd(out_dtype, gu, act, M, F, stream=None):

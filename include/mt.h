@@ -332,8 +332,8 @@ int mt_device_bytes(mt_ctx* ctx, int64_t* bytes);
  * parked in host memory, and checkpoint slots held in device memory. */
 int mt_layout_info(mt_ctx* ctx, int64_t* chunk_rows, int32_t* ckpt_host, int32_t* ckpt_device_slots);
 
-/* Text of the last error on ctx (or of the last failed mt_create on this
- * thread when ctx is NULL). Never NULL. */
+/* Text of the last error on ctx (or, when ctx is NULL, of the last failed
+ * mt_create or mt_op_* call on this thread that reports one). Never NULL. */
 const char* mt_last_error(const mt_ctx* ctx);
 
 void mt_destroy(mt_ctx* ctx);

@@ -113,6 +113,23 @@ int mt_op_attn_bwd_rope(int32_t dtype, const void* qkv, const float* o, const fl
                         void* ws, int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
                         void* stream);
 
+/* mt_op_attn_bwd_rope without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Its scratch is a static device array of
+ * MT_NOALLOC_SCRATCH_BYTES per GPU, held from library load until the process
+ * ends; nothing is allocated or freed by the call. Same kernels, arguments
+ * (less ws) and results as mt_op_attn_bwd_rope. MT_EINVAL, with
+ * mt_last_error(NULL) stating the need, when mt_op_attn_bwd_ws_bytes(dtype,
+ * B, T, H, hd) exceeds MT_NOALLOC_SCRATCH_BYTES (64 MiB: for example B*T*H*hd
+ * up to 32M elements in bf16 mode, the 14B-shaped layer at 4096 tokens).
+ * Every call on one GPU shares that GPU's scratch and overwrites it: calls
+ * that overlap on one GPU (other streams or threads) race; order them on one
+ * stream. */
+#define MT_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int mt_op_attn_bwd_rope_noalloc(int32_t dtype, const void* qkv, const float* o, const float* dout,
+                                const float* lse, const float* cos, const float* sin, void* dqkv, int32_t B,
+                                int32_t T, int32_t H, int32_t Hkv, int32_t hd, void* stream);
+
 /* SwiGLU on gu [M, 2F] fp32 (gate = columns [0, F), up = [F, 2F)):
  * act = silu(gate) up as out_dtype [M, F]. Backward: from dact [M, F] fp32,
  * dgu [M, 2F] as out_dtype with dgate = dact up s (1 + gate (1 - s)),
