@@ -146,7 +146,9 @@ static int validate(const mt_model_cfg* c, std::string& why) {
     return bad("head_dim must be 16/32/64/128 (fp32) or 64/128 (bf16)");
   if (c->ffn_dim < 1 || c->vocab < 2) return bad("ffn_dim and vocab must be positive");
   if (c->max_batch < 1 || c->max_seq < 1) return bad("max_batch and max_seq must be >= 1");
-  if ((int64_t)c->max_batch * c->max_seq > (1LL << 31) - 1) return bad("max_batch * max_seq too large");
+  if ((int64_t)c->max_batch * c->max_seq >= MAX_BLOCK_ROWS) return bad("max_batch * max_seq must be < 2^24 tokens");
+  if ((int64_t)(c->n_heads + 2 * c->n_kv_heads) * c->head_dim >= MAX_ATTN_LD)
+    return bad("(n_heads + 2 n_kv_heads) * head_dim must be < 2^24");
   if (c->n_layer_buffers < 2) return bad("n_layer_buffers must be >= 2");
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f) || !(c->lr >= 0.0) || !(c->beta1 >= 0.0 && c->beta1 < 1.0) ||
       !(c->beta2 >= 0.0 && c->beta2 < 1.0) || !(c->adam_eps >= 0.0))

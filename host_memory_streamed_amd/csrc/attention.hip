@@ -369,22 +369,23 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const float* __restri
                                                            const float* __restrict__ dout,
                                                            T* __restrict__ dcast, float* __restrict__ D,
                                                            int64_t rows, int Tn, int H) {
-  const int64_t rid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (m, h) pair
-  if (rid >= rows) return;
   const int lane = threadIdx.x & 63;
-  const int64_t m = rid / H;
-  const int h = (int)(rid % H);
-  const int64_t off = m * (int64_t)H * HD + h * HD;
-  float acc = 0.f;
-  for (int i = lane; i < HD; i += 64) {
-    const float d = dout[off + i];
-    acc += d * o[off + i];
-    dcast[off + i] = from_f32<T>(d);
-  }
-  acc = wave_sum(acc);
-  if (lane == 0) {
-    const int64_t b = m / Tn, t = m % Tn;
-    D[(b * H + h) * Tn + t] = acc;
+  // one wave per (m, h) pair, striding over the grid
+  for (int64_t rid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); rid < rows; rid += (int64_t)gridDim.x * 4) {
+    const int64_t m = rid / H;
+    const int h = (int)(rid % H);
+    const int64_t off = m * (int64_t)H * HD + h * HD;
+    float acc = 0.f;
+    for (int i = lane; i < HD; i += 64) {
+      const float d = dout[off + i];
+      acc += d * o[off + i];
+      dcast[off + i] = from_f32<T>(d);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      const int64_t b = m / Tn, t = m % Tn;
+      D[(b * H + h) * Tn + t] = acc;
+    }
   }
 }
 
@@ -582,7 +583,7 @@ hipError_t bwd_launch(const void* qkv, const float* o, const float* dout, const 
   float* D = reinterpret_cast<float*>(ws);
   T* dcast = reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + attn_ws_d_bytes(B, Tn, H));
   const int64_t rows = M * H;
-  hipLaunchKernelGGL((attn_bwd_pre_kernel<T, HD>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+  hipLaunchKernelGGL((attn_bwd_pre_kernel<T, HD>), dim3((unsigned)std::min<int64_t>((rows + 3) / 4, 1 << 22)), dim3(256), 0, s,
                      o, dout, dcast, D, rows, Tn, H);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

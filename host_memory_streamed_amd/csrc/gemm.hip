@@ -785,7 +785,10 @@ hipError_t launch_big(const void* A, int64_t lda, const void* B, int64_t ldb, fl
 
 bool big_ok(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N) {
   const int64_t es = dtype ? 2 : 4;
-  auto al = [&](const void* p, int64_t ld) { return ((uintptr_t)p % 16 == 0) && ((ld * es) % 16 == 0); };
+  // 16-byte rows, and byte offsets inside a 256-row tile within the copies' 32-bit range
+  auto al = [&](const void* p, int64_t ld) {
+    return ((uintptr_t)p % 16 == 0) && ((ld * es) % 16 == 0) && (int64_t)BIG * ld * es < MAX_COPY_OFFSET;
+  };
   return al(A, lda) && al(B, ldb) && M >= 1 && N >= 1;
 }
 

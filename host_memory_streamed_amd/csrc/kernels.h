@@ -26,6 +26,19 @@ hipError_t gemm_ws(int dtype, int layout, const void* A, int64_t lda, const void
                    int64_t ldc, const float* R, int64_t ldr, int64_t M, int64_t N, int64_t K, void* ws,
                    int64_t ws_bytes, hipStream_t s);
 
+// Limits set by the kernels' 32-bit quantities. Work-items per grid dimension
+// stay below 2^32: the kernels that give each row a 256-thread block (RoPE,
+// cross-entropy) take fewer than MAX_BLOCK_ROWS rows. Every element index that
+// involves the token count is 64-bit. The direct global->LDS copies address
+// their bytes as a 32-bit offset from a 64-bit tile base: attention tiles span
+// 64 rows of the packed projection, (H + 2 Hkv) hd elements each, so that row
+// length stays below MAX_ATTN_LD; GEMM tiles span 256 rows of an operand, and
+// operands with longer rows take the 128x128 kernel, which loads through
+// 64-bit pointers.
+constexpr int64_t MAX_BLOCK_ROWS = 1ll << 24;
+constexpr int64_t MAX_ATTN_LD = 1ll << 24;
+constexpr int64_t MAX_COPY_OFFSET = 1ll << 31;
+
 bool attn_supported(int dtype, int hd);
 // bf16 forward on 32x32 matrix-core tiles (hd 64 or 128), attn_fwd_bf16.hip
 hipError_t attn_fwd_bf16(const void* qkv, float* o, void* o_cast, float* lse, int B, int T, int H,

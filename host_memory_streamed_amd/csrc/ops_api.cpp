@@ -77,6 +77,7 @@ int mt_op_rmsnorm_bwd(const float* x, const float* w, const float* rstd, const f
 static int rope_check(int32_t out_dtype, const void* in, void* out, const float* c, const float* s, int32_t B,
                       int32_t T, int32_t H, int32_t Hkv, int32_t hd) {
   if (!dtype_ok(out_dtype) || B < 0 || T < 0 || H < 1 || Hkv < 1 || hd < 2 || hd % 2) return MT_EINVAL;
+  if ((int64_t)B * T >= MAX_BLOCK_ROWS) return MT_EINVAL;   // one block per token row
   if ((int64_t)B * T > 0 && (!in || !out || !c || !s)) return MT_EINVAL;
   return MT_OK;
 }
@@ -99,6 +100,10 @@ static int attn_check(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t Hk
   if (!dtype_ok(dtype) || !attn_supported(dtype, hd)) return MT_EINVAL;
   if (B < 0 || T < 0 || H < 1 || Hkv < 1 || H % Hkv) return MT_EINVAL;
   if (B > 65535 || H > 65535) return MT_EINVAL;
+  // tile byte offsets of the direct copies, and work-items per grid dimension
+  // (one 256-thread workgroup per 64 queries or keys and head, at most)
+  if ((int64_t)(H + 2 * Hkv) * hd >= MAX_ATTN_LD) return MT_EINVAL;
+  if (((int64_t)T + 63) / 64 * H * 256 >= (1ll << 32)) return MT_EINVAL;
   return MT_OK;
 }
 
@@ -153,7 +158,7 @@ int mt_op_swiglu_bwd(int32_t out_dtype, const float* gu, const float* dact, void
 
 int mt_op_xent(int32_t out_dtype, const float* logits, const int32_t* targets, float* loss, void* dlogits,
                int64_t rows, int32_t V, float scale, void* stream) {
-  if (!dtype_ok(out_dtype) || rows < 0 || rows > INT32_MAX || V < 1) return MT_EINVAL;
+  if (!dtype_ok(out_dtype) || rows < 0 || rows >= MAX_BLOCK_ROWS || V < 1) return MT_EINVAL;
   if (rows == 0) return MT_OK;
   if (!logits || !targets || !loss || !dlogits) return MT_EINVAL;
   return hip_rc(xent(out_dtype, logits, targets, loss, dlogits, rows, V, scale, st(stream)));

@@ -154,6 +154,31 @@ def test_gemm_ws_rejects_bad_workspace():
     assert mt.gemm_ws_bytes() >= 16 * 15 * 256 * 256 * 4
 
 
+def test_launch_limits_refused_on_the_host():
+    """Shapes past the kernels' 32-bit limits are refused before any device
+    call: 2^24 token rows for the one-block-per-row kernels, 2^24 elements
+    for a row of the packed projection (the attention tiles' copy offsets),
+    2^32 work-items per grid dimension for attention."""
+    L = mt.lib()
+    p = ctypes.c_void_p(4096)
+    # one past the largest token count
+    c = mt.make_config(2, 64, 4, 4, 16, 172, 256, 1, 1 << 24)
+    h = ctypes.c_void_p()
+    assert L.mt_create(ctypes.byref(c), None, None, ctypes.byref(h)) == mt.MT_EINVAL and not h.value
+    assert b"2^24" in L.mt_last_error(None)
+    c = mt.make_config(2, 64, 131072, 1, 128, 172, 256, 1, 32)
+    assert L.mt_create(ctypes.byref(c), None, None, ctypes.byref(h)) == mt.MT_EINVAL and not h.value
+    assert L.mt_op_xent(mt.MT_BF16, p, p, p, p, 1 << 24, 1000, 1.0, None) == mt.MT_EINVAL
+    assert L.mt_op_rope_fwd(mt.MT_BF16, p, p, p, p, 1, 1 << 24, 4, 4, 128, None) == mt.MT_EINVAL
+    assert L.mt_op_rope_fwd(mt.MT_BF16, p, p, p, p, 2, 1 << 23, 4, 4, 128, None) == mt.MT_EINVAL
+    # packed projection rows of (H + 2 Hkv) hd >= 2^24 elements
+    assert L.mt_op_attn_fwd(mt.MT_BF16, p, p, p, p, 1, 64, 65535, 65535, 128, None) == mt.MT_EINVAL
+    # (T / 64) * H workgroups of 256 threads past 2^32
+    assert L.mt_op_attn_fwd(mt.MT_BF16, p, p, p, p, 1, (1 << 31) - 1, 64, 8, 128, None) == mt.MT_EINVAL
+    assert L.mt_op_attn_bwd_rope(mt.MT_BF16, p, p, p, p, p, p, p, p, 1, 64, 65535, 65535, 128, None) \
+        == mt.MT_EINVAL
+
+
 def test_rmsnorm_bwd_rejects_misaligned_operands():
     # host-side argument checks run before any device call (addresses only)
     L = mt.lib()
