@@ -51,6 +51,12 @@ struct F32Cfg {
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
+// max(m, x) for the running maximum of raw scores: the median of (m, x, +inf).
+// The median instruction takes the matrix-core results as they are, where a
+// maximum with IEEE semantics first quiets each operand (one more VALU
+// instruction per score); chains of it fuse into three-operand maxima.
+__device__ __forceinline__ float max_score(float m, float x) { return __builtin_amdgcn_fmed3f(m, x, INFINITY); }
+
 // Direct global -> LDS copy (buffer form) of a 64-row K or V tile: wave w fills 1 KB pieces
 // w*WP .. w*WP+WP-1, lane i landing 16 bytes at piece + 16 i; each lane
 // fetches the chunk that the permuted layout puts there. Rows at or past the
@@ -194,9 +200,9 @@ __global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __rest
       }
       float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s0[r], s0[r + 1]));
+      for (int r = 0; r < 16; ++r) mx = max_score(mx, s0[r]);
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s1[r], s1[r + 1]));
+      for (int r = 0; r < 16; ++r) mx = max_score(mx, s1[r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
       const float m_new = fmaxf(m, mx * sl2);
       const float alpha = exp2f(m - m_new);
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(FT, 2) void attn_fwd_bf16_kernel(const bf16* __rest
           }
         }
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[st][r], s[st][r + 1]));
+        for (int r = 0; r < 16; ++r) mx = max_score(mx, s[st][r]);
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
