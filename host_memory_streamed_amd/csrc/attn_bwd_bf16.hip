@@ -10,7 +10,12 @@
 //    S = Q K^T and dP = dO V^T (its keys are the columns); 64-query Q and dO
 //    tiles of every query head of the group stream through double-buffered
 //    LDS (copied in pieces spread over the previous tile's work); dV^T += dO^T P and dK^T += Q^T dS take P and dS from the
-//    accumulators and dO^T, Q^T through the LDS transpose read.
+//    accumulators and dO^T, Q^T through the LDS transpose read. On short
+//    sequences with grouped kv heads a workgroup takes one query head of the
+//    group instead: the causal key blocks differ in length by up to the
+//    sequence's block count, and as many times more, shorter work items
+//    spread over the CUs longest first. Those write fp32 partials, and a
+//    third pass sums them over the group's heads in head order.
 //  dQ pass: a workgroup owns 128 queries of one head (4 waves x 32); the
 //    wave's Q and dO stay in registers as the B operands of S^T = K Q^T and
 //    dP^T = V dO^T; 64-key K and V tiles stream through double-buffered LDS;
@@ -31,6 +36,10 @@ constexpr float B_LOG2E = 1.4426950408889634f;
 constexpr int BT = 256;   // threads
 constexpr int BW = 128;   // keys (dK/dV) or queries (dQ) per workgroup
 constexpr int BS = 64;    // rows per streamed tile
+// dK/dV work items are split over the query heads of a kv group up to this
+// many tokens per sequence (the partials take B * min(T, DKV_SPLIT_T) * H *
+// 2 hd fp32 of workspace)
+constexpr int DKV_SPLIT_T = 8192;
 #ifndef FENCE2
 #define FENCE2 2          // steps per scheduling region in the pipelined phases
 #endif
@@ -241,7 +250,8 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
                                                              OutT* __restrict__ dqkv,
                                                              const float* __restrict__ rcos,
                                                              const float* __restrict__ rsin, int Tn,
-                                                             int H, int Hkv, int nkb, int xcd_groups) {
+                                                             int H, int Hkv, int nkb, int xcd_groups, int hsplit,
+                                                             float* __restrict__ part) {
   typedef Swz<HD> C;
   // one array per buffer: the compiler then sees that a copy in flight into
   // one buffer does not alias reads of the other and does not wait for it
@@ -250,19 +260,25 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
   __shared__ __attribute__((aligned(16))) float Ls[2][BS];
   __shared__ __attribute__((aligned(16))) float Dsh[2][BS];
 
+  // work item: (kv head, key block, head subset hs of hsplit), low key
+  // blocks (the most queries) first
   const int id = blockIdx.x;
-  int kvh, kb;
+  int kvh, kb, hs;
   if (xcd_groups) {
-    const int per = (nkb * Hkv) >> 3;
+    const int per = (nkb * Hkv * hsplit) >> 3;
     const int item = (id & 7) * per + (id >> 3);
-    kvh = item / nkb;
-    kb = item % nkb;   // low key blocks see the most queries: first
+    kvh = item / (nkb * hsplit);
+    const int rem = item % (nkb * hsplit);
+    kb = rem / hsplit;
+    hs = rem % hsplit;
   } else {
     kvh = id % Hkv;
-    kb = id / Hkv;
+    const int rem = id / Hkv;
+    kb = rem / hsplit;
+    hs = rem % hsplit;
   }
   const int b = blockIdx.z;
-  const int grp = H / Hkv;
+  const int grp = H / Hkv / hsplit;   // query heads of this item
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = tid >> 6;
   const int c = lane & 31, G = lane >> 5;
@@ -305,12 +321,12 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
   const int nqt = (Tn + BS - 1) / BS - qt0;
   const int n_it = grp * nqt;
 
-  // tiles run over heads kvh*grp .. kvh*grp+grp-1, each over query tiles
+  // tiles run over the item's grp heads from (kvh * hsplit + hs) * grp on, each over query tiles
   // qt0 .. qt0+nqt-1; (nx_h, nx_qt) is the next tile to stage, cu_qt the
   // current tile's query tile. (sh, sq0) is what the current tile stages:
   // the next tile, or itself again when there is none (into the free buffer,
   // never read).
-  int nx_h = kvh * grp, nx_qt = qt0, cu_qt = qt0;
+  int nx_h = (kvh * hsplit + hs) * grp, nx_qt = qt0, cu_qt = qt0;
   int sh = nx_h, sq0 = nx_qt * BS;
   float lv = 0.f;
   auto pick_next = [&](bool more) __attribute__((always_inline)) {
@@ -532,12 +548,59 @@ __global__ __launch_bounds__(BT, 1) void attn_dkv_bf16_kernel(const bf16* __rest
     if (it + 1 < n_it) tile(it + 2 < n_it, Q1, O1, Q0, O0, 1);
   }
 
-  if (key < Tn) {
+  if (key < Tn && hsplit > 1) {
+    // partial row [dK | dV] of this head subset: part[b][kvh][hs][key][2 HD]
+    float* prow = part + ((((int64_t)b * Hkv + kvh) * hsplit + hs) * Tn + key) * (2 * HD);
+    store_acc_row<float, HD>(prow, dk, 1.f / sqrtf((float)HD), nullptr, nullptr, G);
+    store_acc_row<float, HD>(prow + HD, dv, 1.f, nullptr, nullptr, G);
+  } else if (key < Tn) {
     OutT* row = dqkv + ((int64_t)b * Tn + key) * ld;   // dqkv has the qkv layout
     const float* cs = rcos ? rcos + (int64_t)key * (HD / 2) : nullptr;
     const float* sn = rsin ? rsin + (int64_t)key * (HD / 2) : nullptr;
     store_acc_row<OutT, HD>(row + (H + kvh) * HD, dk, 1.f / sqrtf((float)HD), cs, sn, G);
     store_acc_row<OutT, HD>(row + (H + Hkv + kvh) * HD, dv, 1.f, nullptr, nullptr, G);
+  }
+}
+
+// dK and dV rows from the partials of the dK/dV pass: the sum over the
+// hsplit head subsets in order, then the dK rotation back (as store_acc_row)
+// and the cast. One wave per (token, kv head); lane i holds hd columns i and
+// i + HD/2, which the rotation pairs.
+template <int HD, typename OutT>
+__global__ __launch_bounds__(256) void attn_dkv_sum_kernel(const float* __restrict__ part, OutT* __restrict__ dqkv,
+                                                           const float* __restrict__ rcos,
+                                                           const float* __restrict__ rsin, int64_t rows, int Tn,
+                                                           int H, int Hkv, int hsplit) {
+  const int lane = threadIdx.x & 63;
+  const int64_t ld = (int64_t)(H + 2 * Hkv) * HD;
+  for (int64_t rid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); rid < rows; rid += (int64_t)gridDim.x * 4) {
+    const int64_t m = rid / Hkv;   // token row b * Tn + t
+    const int kvh = (int)(rid % Hkv);
+    const int64_t b = m / Tn, t = m % Tn;
+    const float* p0 = part + (((b * Hkv + kvh) * hsplit) * Tn + t) * (2 * HD);
+    const int64_t pstride = (int64_t)Tn * 2 * HD;
+    OutT* krow = dqkv + m * ld + (H + kvh) * HD;
+    OutT* vrow = dqkv + m * ld + (H + Hkv + kvh) * HD;
+    for (int i = lane; i < HD / 2; i += 64) {
+      float k1 = 0.f, k2 = 0.f, v1 = 0.f, v2 = 0.f;
+      for (int j = 0; j < hsplit; ++j) {
+        const float* p = p0 + j * pstride;
+        k1 += p[i];
+        k2 += p[i + HD / 2];
+        v1 += p[HD + i];
+        v2 += p[HD + i + HD / 2];
+      }
+      if (rcos) {
+        const float c = rcos[t * (HD / 2) + i], s = rsin[t * (HD / 2) + i];
+        const float o1 = k1 * c + k2 * s, o2 = k2 * c - k1 * s;
+        k1 = o1;
+        k2 = o2;
+      }
+      krow[i] = from_f32<OutT>(k1);
+      krow[i + HD / 2] = from_f32<OutT>(k2);
+      vrow[i] = from_f32<OutT>(v1);
+      vrow[i + HD / 2] = from_f32<OutT>(v2);
+    }
   }
 }
 
@@ -734,12 +797,21 @@ hipError_t launch_bwd(const void* qkv, const float* o, const float* dout, const 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nb = (Tn + BW - 1) / BW;
-  const int64_t kv_items = (int64_t)nb * Hkv, q_items = (int64_t)nb * H;
+  const int hsplit = attn_dkv_hsplit(Tn, H, Hkv);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(dcast) + (int64_t)B * Tn * H * HD * 2);
+  const int64_t kv_items = (int64_t)nb * Hkv * hsplit, q_items = (int64_t)nb * H;
   hipLaunchKernelGGL((attn_dkv_bf16_kernel<HD, OutT>), dim3((unsigned)kv_items, 1, B), dim3(BT), 0, s,
                      (const bf16*)qkv, (const bf16*)dcast, lse, (const float*)D, (OutT*)dqkv, rcos, rsin,
-                     Tn, H, Hkv, nb, (int)((kv_items % 8 == 0) && (Hkv % 8 == 0)));
+                     Tn, H, Hkv, nb, (int)((kv_items % 8 == 0) && (Hkv % 8 == 0)), hsplit, part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (hsplit > 1) {
+    const int64_t sum_rows = M * Hkv;
+    hipLaunchKernelGGL((attn_dkv_sum_kernel<HD, OutT>), dim3((unsigned)std::min<int64_t>((sum_rows + 3) / 4, 1 << 22)),
+                       dim3(256), 0, s, (const float*)part, (OutT*)dqkv, rcos, rsin, sum_rows, Tn, H, Hkv, hsplit);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((attn_dq_bf16_kernel<HD, OutT>), dim3((unsigned)q_items, 1, B), dim3(BT), 0, s,
                      (const bf16*)qkv, (const bf16*)dcast, lse, (const float*)D, (OutT*)dqkv, rcos, rsin,
                      Tn, H, Hkv, nb, (int)((q_items % 8 == 0) && (H % 8 == 0)));
@@ -747,6 +819,14 @@ hipError_t launch_bwd(const void* qkv, const float* o, const float* dout, const 
 }
 
 }  // namespace
+
+// Head subsets per dK/dV work item: every query head of a kv group on its own
+// for short sequences with grouped kv heads, else one subset.
+int attn_dkv_hsplit(int Tn, int H, int Hkv) { return (H > Hkv && Tn <= DKV_SPLIT_T) ? H / Hkv : 1; }
+
+int64_t attn_dkv_part_bytes(int B, int Tn, int H, int hd) {
+  return (int64_t)B * std::min(Tn, DKV_SPLIT_T) * H * 2 * hd * 4;
+}
 
 hipError_t attn_bwd_bf16(const void* qkv, const float* o, const float* dout, const float* lse, void* dqkv,
                          int out_dtype, const float* rcos, const float* rsin, void* ws, int B, int Tn,

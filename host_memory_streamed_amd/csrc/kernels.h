@@ -49,6 +49,10 @@ hipError_t attn_bwd_bf16(const void* qkv, const float* o, const float* dout, con
                          int out_dtype, const float* rcos, const float* rsin, void* ws, int B, int T, int H,
                          int Hkv, int hd, hipStream_t s);
 int64_t attn_ws_d_bytes(int B, int T, int H);
+// bf16 attention backward: head subsets per dK/dV work item (attn_bwd_bf16.hip)
+// and the workspace its fp32 partials take
+int attn_dkv_hsplit(int Tn, int H, int Hkv);
+int64_t attn_dkv_part_bytes(int B, int Tn, int H, int hd);
 hipError_t attn_fwd(int dtype, const void* qkv, float* o, void* o_cast, float* lse, int B, int T,
                     int H, int Hkv, int hd, hipStream_t s);
 // dqkv of out_dtype (fp32, or bf16 when dtype is bf16); with rcos/rsin (the

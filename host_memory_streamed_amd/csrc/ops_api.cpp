@@ -117,7 +117,8 @@ int mt_op_attn_fwd(int32_t dtype, const void* qkv, float* o, void* o_cast, float
 }
 
 int64_t mt_op_attn_bwd_ws_bytes(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t hd) {
-  return attn_ws_d_bytes(B, T, H) + (int64_t)B * T * H * hd * (dtype == MT_BF16 ? 2 : 4);
+  return attn_ws_d_bytes(B, T, H) + (int64_t)B * T * H * hd * (dtype == MT_BF16 ? 2 : 4) +
+         (dtype == MT_BF16 ? attn_dkv_part_bytes(B, T, H, hd) : 0);
 }
 
 int mt_op_attn_bwd(int32_t dtype, const void* qkv, const float* o, const float* dout, const float* lse,

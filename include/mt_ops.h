@@ -95,8 +95,10 @@ int mt_op_attn_fwd(int32_t dtype, const void* qkv, float* o, void* o_cast, float
 /* Causal flash attention backward: given qkv (as in forward), o and dout
  * [M, H hd] fp32 and lse, writes dqkv [M, (H+2Hkv) hd] fp32 (dq, then dk and
  * dv summed over each kv group). P is recomputed from lse; D = rowsum(dout o)
- * in fp32; dq and dk/dv come from separate, deterministic passes.
- * ws: mt_op_attn_bwd_ws_bytes(...) bytes of device scratch. */
+ * in fp32; dq and dk/dv come from separate, deterministic passes (in bf16
+ * mode with H > Hkv and T <= 8192, dk/dv per query head, then summed over
+ * the group in head order). ws: mt_op_attn_bwd_ws_bytes(...) bytes of device
+ * scratch. */
 int64_t mt_op_attn_bwd_ws_bytes(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t hd);
 int mt_op_attn_bwd(int32_t dtype, const void* qkv, const float* o, const float* dout,
                    const float* lse, float* dqkv, void* ws, int32_t B, int32_t T, int32_t H,
@@ -120,8 +122,8 @@ int mt_op_attn_bwd_rope(int32_t dtype, const void* qkv, const float* o, const fl
  * ends; nothing is allocated or freed by the call. Same kernels, arguments
  * (less ws) and results as mt_op_attn_bwd_rope. MT_EINVAL, with
  * mt_last_error(NULL) stating the need, when mt_op_attn_bwd_ws_bytes(dtype,
- * B, T, H, hd) exceeds MT_NOALLOC_SCRATCH_BYTES (64 MiB: for example B*T*H*hd
- * up to 32M elements in bf16 mode, the 14B-shaped layer at 4096 tokens).
+ * B, T, H, hd) exceeds MT_NOALLOC_SCRATCH_BYTES (64 MiB: for example the
+ * 14B-shaped layer's 40 heads of 128 over 1024 tokens in bf16 mode).
  * Every call on one GPU shares that GPU's scratch and overwrites it: calls
  * that overlap on one GPU (other streams or threads) race; order them on one
  * stream. */
