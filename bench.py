@@ -299,6 +299,8 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--batch", type=int, default=None,
                     help="override the batch (sequences per step): more tokens per streamed byte")
+    ap.add_argument("--seq-len", type=int, default=None,
+                    help="override the tokens per sequence (the workload's layer shape kept)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp32"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -350,6 +352,8 @@ def main():
     layers_note = None
     if args.batch:
         w = mt.Workload(**{**w.__dict__, "batch": args.batch})
+    if args.seq_len:
+        w = mt.Workload(**{**w.__dict__, "seq": args.seq_len})
     if args.layers:
         w = mt.Workload(**{**w.__dict__, "n_layers": args.layers})
     elif args.workload in ("120b", "7b-1m"):
