@@ -414,15 +414,17 @@ def test_attention_bwd_14b_shape_sampled():
         bf16_close(g[k0:k0 + 64, H + Hkv + kv], dv, floor=1e-2 * np.sqrt(np.mean(dv ** 2)))
 
 
-@pytest.mark.parametrize("T", [524288, 1048576])
-def test_attention_long_sequence_sampled(T):
+@pytest.mark.parametrize("T,H,Hkv", [(524288, 2, 2), (1048576, 2, 2), (8192, 4, 2), (8320, 4, 2)])
+def test_attention_long_sequence_sampled(T, H, Hkv):
     """Causal attention over one sequence of 524288 tokens (the long-context
     workload's length) and of 1048576 (twice it); 2 heads of dim 128 keep
     the check to seconds: forward rows and the dq rows of sampled queries,
     and dk/dv of the last 64-key tile, against float64 computed row by row;
     plus, over the whole length, sum_t dv[t] = sum_q dO[q] (each probability
-    row sums to one)."""
-    H, Hkv, hd, dtype = 2, 2, 128, mt.MT_BF16
+    row sums to one). With grouped kv heads, on both sides of the length up
+    to which the dK/dV pass takes one query head per work item (8192 tokens:
+    per-head partials and their sum; 8320: the whole group per item)."""
+    hd, dtype = 128, mt.MT_BF16
     rng = np.random.default_rng(T)
     W = (H + 2 * Hkv) * hd
     qkv = O.bf16(rng.standard_normal((T, W), dtype=np.float32)).astype(np.float32)
