@@ -229,9 +229,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int6
 // 2 (M) x 4 (N), each wave owning 128x64 (4x2 MFMA 32x32 tiles); two waves per
 // SIMD hide each other's latencies. The K loop moves 128 bytes per row per
 // step (64 bf16 / 32 fp32) through two 64 KB LDS stages (one workgroup per
-// CU). Global loads for the next step go to registers before the current
-// step's products; interior tiles take a branch-free load path, edge tiles a
-// guarded one. LDS rows are 128 bytes with the 16-byte chunks permuted by
+// CU). Full tiles copy each stage straight from global memory into LDS, one
+// stage ahead, and read each k-step's fragments one k-step ahead of its
+// products; edge tiles and K tails load through registers on a guarded path.
+// LDS rows are 128 bytes with the 16-byte chunks permuted by
 // S(row, c) = c ^ (row & 7) ^ ((row >> 3) & 7): fragment reads (8 consecutive
 // rows, one chunk), row stores (one row, 8 chunks) and the transposed 4-byte
 // stores of M/N-contiguous operands all spread over the banks.
@@ -579,6 +580,64 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
     }
   };
   auto no_hook = [](int) {};
+  // The same stage with each k-step's fragments read one k-step ahead of its
+  // products (two fragment sets), so only the first k-step of a stage waits
+  // on LDS latency. Scheduling fences pin the order: k-step 0's reads, then
+  // for each k-step s the hook's copies, the reads of k-step s + 1 and the
+  // products of k-step s.
+  struct Frags {
+    Vec16 a[4], b[2];
+  };
+  auto read_frags = [&](const char* cur, int s, Frags& f) __attribute__((always_inline)) {
+    const int c = 2 * s + g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (A_NAT) {
+        const bf16x8 t = BigNat::frag(cur, wm * 128 + i * 32, s, lane);
+        __builtin_memcpy(&f.a[i], &t, 16);
+      } else {
+        f.a[i] = *reinterpret_cast<const Vec16*>(cur + a_base[i] + ((c ^ a_x[i]) << 4));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if constexpr (B_NAT) {
+        const bf16x8 t = BigNat::frag(cur + BIG_TILE_BYTES, wn * 64 + j * 32, s, lane);
+        __builtin_memcpy(&f.b[j], &t, 16);
+      } else {
+        f.b[j] = *reinterpret_cast<const Vec16*>(cur + b_base[j] + ((c ^ b_x[j]) << 4));
+      }
+    }
+  };
+  auto mma_frags = [&](const Frags& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < NSUB; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        typename MF::frag fa;
+        __builtin_memcpy(&fa, reinterpret_cast<const char*>(&f.a[i]) + q * sizeof(fa), sizeof(fa));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          typename MF::frag fb;
+          __builtin_memcpy(&fb, reinterpret_cast<const char*>(&f.b[j]) + q * sizeof(fb), sizeof(fb));
+          acc[i][j] = MF::mma(fa, fb, acc[i][j]);
+        }
+      }
+  };
+  auto mma_stage_ahead = [&](const char* cur, auto hook) __attribute__((always_inline)) {
+    Frags f0, f1;
+    read_frags(cur, 0, f0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      hook(s);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < 4) read_frags(cur, s + 1, (s & 1) ? f0 : f1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_frags((s & 1) ? f1 : f0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   // guarded stage through registers (edge tiles, the K tail)
   auto reg_stage = [&](int k0, char* dst) {
     la.template load<true>(A, lda, m0, M, k0, K, tid);
@@ -609,27 +668,13 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void gemm_big_kernel(const T* __res
         // first two k-steps, or all in the first where only one k-step's
         // fragments fit in registers (both operands K-contiguous)
         constexpr int CSTEPS = (A_NAT || B_NAT) ? 2 : 1;
-        mma_stage(cur, [&](int s) {
+        mma_stage_ahead(cur, [&](int s) {
           if (s < CSTEPS) {
 #pragma unroll
             for (int j = 4 * s / CSTEPS; j < 4 * (s + 1) / CSTEPS; ++j) {
               la.direct_piece(j, A, lda, m0, kn, nxt, tid);
               lb.direct_piece(j, B, ldb, n0, kn, nxt + BIG_TILE_BYTES, tid);
             }
-          }
-          if (s == 3) {
-            // order for the stage: each k-step's LDS reads one step ahead of
-            // its products, the copies after the first reads
-            constexpr int NDS = (A_NAT ? 8 : 4) + (B_NAT ? 4 : 2);   // LDS reads per k-step
-            __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 8 / CSTEPS, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-            if constexpr (CSTEPS == 2) __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
           }
         });
         __builtin_amdgcn_s_waitcnt(0x0F70);
