@@ -251,7 +251,10 @@ def summarize_kernel_trace(path, steps, skip, kernel_substr, flops_per_launch=No
     order), all of them and those that overlap no runtime copy kernel
     (under kernel tracing the runtime runs each device-to-host copy as a
     blit kernel, and a dispatch that overlaps one waits for compute units).
-    Prints a markdown summary."""
+    Copies overlap some shapes more often than others, so the clean subset
+    has another mix of shapes than the step: the per-launch estimate weights
+    each grid size's clean mean by that grid size's share of all kept
+    dispatches. Prints a markdown summary."""
     import csv
     rows = list(csv.DictReader(open(path)))
     for r in rows:
@@ -269,12 +272,20 @@ def summarize_kernel_trace(path, steps, skip, kernel_substr, flops_per_launch=No
         return any(copies[j][1] > r["t0"] for j in range(max(0, i - 64), i))
     clean = [r for r in kept if not overlaps(r)]
     avg = lambda rs: sum(r["t1"] - r["t0"] for r in rs) / max(1, len(rs)) / 1e3
+    grid = lambda r: int(r.get("Grid_Size") or r.get("Grid_Size_X"))
+    shapes = sorted({grid(r) for r in kept})
+    by = {g: ([r for r in kept if grid(r) == g], [r for r in clean if grid(r) == g]) for g in shapes}
+    weighted = sum(len(a) / len(kept) * avg(c) for a, c in by.values() if c)
     print(f"| dispatches | count | average us |\n|---|---:|---:|")
     print(f"| `{kernel_substr}`, {steps - skip} of {steps} traced steps | {len(kept)} | {avg(kept):.1f} |")
     print(f"| the same, overlapping no copy kernel | {len(clean)} | {avg(clean):.1f} |")
+    print(f"| clean mean per grid size, weighted by the step's mix | {len(kept)} | {weighted:.1f} |")
+    print(f"\n| grid size (threads) | dispatches | clean | average us, all | average us, clean |\n|---:|---:|---:|---:|---:|")
+    for g, (a, c) in by.items():
+        print(f"| {g} | {len(a)} | {len(c)} | {avg(a):.1f} | {avg(c):.1f} |")
     if flops_per_launch:
-        for name, rs in (("all", kept), ("no copy overlap", clean)):
-            t = avg(rs) * 1e-6
+        for name, t in (("all", avg(kept)), ("no copy overlap", avg(clean)), ("shape-weighted, no copy overlap", weighted)):
+            t *= 1e-6
             print(f"\n{name}: {flops_per_launch / t / 1e12:.1f} TFLOP/s, frac {flops_per_launch / t / PEAK_BF16:.4f} "
                   f"of {PEAK_BF16 / 1e12:.0f}")
 
