@@ -312,6 +312,8 @@ def main():
                     help="override the batch (sequences per step): more tokens per streamed byte")
     ap.add_argument("--seq-len", type=int, default=None,
                     help="override the tokens per sequence (the workload's layer shape kept)")
+    ap.add_argument("--host-threads", type=int, default=0,
+                    help="host AdamW / gather worker threads (0 = online CPUs)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp32"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -377,7 +379,8 @@ def main():
             log(layers_note)
             w = mt.Workload(**{**w.__dict__, "n_layers": L})
     buffers = w.n_layers + 1 if args.resident else min(max(2, args.layer_buffers), w.n_layers + 1)
-    ctx = build_context(w, dtype, args.seed, flags, chunk_rows=args.chunk_rows, ckpt_host=args.ckpt_host,
+    ctx = build_context(w, dtype, args.seed, flags, host_threads=args.host_threads, chunk_rows=args.chunk_rows,
+                        ckpt_host=args.ckpt_host,
                         buffers=buffers, micro_batches=args.micro_batches)
     layout = ctx.layout_info()
     tokens, targets = synth.token_batch(args.seed, w.batch, w.seq, w.vocab)
@@ -462,6 +465,7 @@ def main():
                                  "host AdamW, updates finishing during the next step's forward in load order"),
                    "grad_transfer": "bf16" if args.bf16_grads else "fp32",
                    **({"micro_batches": args.micro_batches} if args.micro_batches > 1 else {}),
+                   **({"host_threads": args.host_threads} if args.host_threads > 0 else {}),
                    **layout},
         "mfu": round(mfu, 4),
         "host_link": {
