@@ -364,17 +364,19 @@ struct BigLoader {
 
 // bf16 operand whose rows run along M or N (A of TN, B of NN and TN): it stays
 // in its natural layout, one 512-byte LDS row per k (256 elements, 32 chunks
-// of 16 bytes), chunk c of row r stored at c ^ ((r & 3) << 1). A fragment for
+// of 16 bytes), chunk c of row r stored at c ^ ((r & 3) << 2). A fragment for
 // 32 consecutive m (or n) and 8 consecutive k per lane group comes from two
 // LDS transpose reads of 4 k each, in the k-slot order of a K-contiguous
-// fragment; with the permutation each 16-lane transpose read (4 rows x 2
-// chunks) covers 32 distinct banks.
+// fragment. LDS serves the 8-byte transpose read 32 lanes (256 bytes) per
+// cycle: 4 rows x 4 chunks, which the permutation puts in four different
+// 64-byte bank groups, so the 32 lanes cover all 64 banks. The rows' copies
+// write whole rows contiguously, conflict-free under any permutation.
 struct BigNat {
   static constexpr int VE = 8;
   static constexpr int ROWB = 512;
   static constexpr int NV = 64 * 32 / BIG_THREADS;   // chunks per thread per stage
   Vec16 v[NV];
-  static __device__ __forceinline__ int pchunk(int row, int c) { return c ^ ((row & 3) << 1); }
+  static __device__ __forceinline__ int pchunk(int row, int c) { return c ^ ((row & 3) << 2); }
 
   template <bool CHECK>
   __device__ __forceinline__ void load(const bf16* __restrict__ base, int64_t ld, int r0, int rows, int k0,
